@@ -1,0 +1,213 @@
+"""CPU oracle for the W8A8 INT8 linear layer -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It shares no code with the HIP library
+(``w8a8_int8_gemm_token_amd``) and never imports it.
+
+The arithmetic lives in ``q8_oracle.c`` (plain C loops, IEEE fp32, no fused
+multiply-add except where ``fmaf`` is written).  This module only compiles it
+with gcc, loads it with ctypes and marshals numpy arrays.  Each function names
+the definition it follows; the C file carries the full citations and the
+readings taken where the pages are silent.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
+against exact rational arithmetic, library routines, closed forms and
+invariants (none of them re-uses this module's arithmetic).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q8_oracle.c")
+_LIB = os.path.join(_HERE, "libq8_oracle.so")
+_CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC"]
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile q8_oracle.c into libq8_oracle.so with gcc (no GPU involved)."""
+    if force or not os.path.exists(_LIB) or \
+            os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        F = ctypes.c_float
+        sig = {
+            "q8o_env_ok": ([], ctypes.c_int),
+            "q8o_f32_to_bf16": ([F], ctypes.c_uint16),
+            "q8o_bf16_to_f32": ([ctypes.c_uint16], F),
+            "q8o_quant_per_token": ([P, I, I, P, P], None),
+            "q8o_quant_weight": ([P, I, I, I, P, P], ctypes.c_int),
+            "q8o_mm_i32": ([P, P, I, I, I, P], ctypes.c_int),
+            "q8o_epilogue_channel": ([P, P, P, I, I, P], None),
+            "q8o_scaled_mm": ([P, P, P, P, I, I, I, P], ctypes.c_int),
+            "q8o_scaled_mm_group128": ([P, P, P, P, I, I, I, P], ctypes.c_int),
+            "q8o_w8a16_ref": ([P, P, P, I, I, I, P, P], None),
+            "q8o_smooth_scales": ([P, I, I, F, P], ctypes.c_int),
+            "q8o_smooth_fold_x": ([P, P, I, I, P], None),
+            "q8o_smooth_fold_w": ([P, P, I, I, P], None),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        if not lib.q8o_env_ok():
+            raise RuntimeError("oracle: FPU not in round-to-nearest-even mode")
+        _lib = lib
+    return _lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.dtype(dtype):
+        raise TypeError(f"oracle: expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def f32_to_bf16(v: float) -> int:
+    """bf16 bits of fp32 value v, round to nearest even."""
+    return int(_load().q8o_f32_to_bf16(ctypes.c_float(v)))
+
+
+def bf16_to_f32(bits: int) -> float:
+    return float(_load().q8o_bf16_to_f32(ctypes.c_uint16(bits)))
+
+
+def quant_per_token(x_bf16: np.ndarray):
+    """a1-a3.  x_bf16: uint16 [M,K] (bf16 bits) -> (xq int8 [M,K], s fp32 [M])."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    xq = np.empty((M, K), np.int8)
+    s = np.empty((M,), np.float32)
+    _load().q8o_quant_per_token(_p(x), M, K, _p(xq), _p(s))
+    return xq, s
+
+
+def quant_weight(w_f32: np.ndarray, group: int | None = None):
+    """a0.  w: fp32 [N,K] -> (wq int8 [N,K], s fp32 [N] or [N,K/group])."""
+    w = _c(w_f32, np.float32)
+    N, K = w.shape
+    g = K if group is None else group
+    wq = np.empty((N, K), np.int8)
+    s = np.empty((N, K // g), np.float32)
+    if _load().q8o_quant_weight(_p(w), N, K, g, _p(wq), _p(s)) != 0:
+        raise ValueError("oracle: group must divide K")
+    return wq, (s[:, 0].copy() if group is None else s)
+
+
+def mm_i32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """a4.  a int8 [M,K], b int8 [N,K] -> exact int32 [M,N]."""
+    a = _c(a, np.int8)
+    b = _c(b, np.int8)
+    M, K = a.shape
+    N, K2 = b.shape
+    assert K == K2
+    out = np.empty((M, N), np.int32)
+    if _load().q8o_mm_i32(_p(a), _p(b), M, N, K, _p(out)) != 0:
+        raise OverflowError("oracle: int32 accumulator overflow")
+    return out
+
+
+def epilogue_channel(acc: np.ndarray, s_tok: np.ndarray, s_ch: np.ndarray):
+    """a5.  int32 [M,N] -> bf16 bits uint16 [M,N]."""
+    acc = _c(acc, np.int32)
+    s_tok = _c(s_tok, np.float32)
+    s_ch = _c(s_ch, np.float32)
+    M, N = acc.shape
+    y = np.empty((M, N), np.uint16)
+    _load().q8o_epilogue_channel(_p(acc), _p(s_tok), _p(s_ch), M, N, _p(y))
+    return y
+
+
+def scaled_mm(a, b, s_tok, s_ch) -> np.ndarray:
+    """a4+a5.  -> bf16 bits uint16 [M,N]."""
+    a = _c(a, np.int8)
+    b = _c(b, np.int8)
+    s_tok = _c(s_tok, np.float32)
+    s_ch = _c(s_ch, np.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    y = np.empty((M, N), np.uint16)
+    if _load().q8o_scaled_mm(_p(a), _p(b), _p(s_tok), _p(s_ch), M, N, K,
+                             _p(y)) != 0:
+        raise OverflowError("oracle: int32 accumulator overflow")
+    return y
+
+
+def scaled_mm_group128(a, b, s_tok, s_grp) -> np.ndarray:
+    """a4+a5g.  s_grp fp32 [N, K/128] -> bf16 bits uint16 [M,N]."""
+    a = _c(a, np.int8)
+    b = _c(b, np.int8)
+    s_tok = _c(s_tok, np.float32)
+    s_grp = _c(s_grp, np.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    assert s_grp.shape == (N, K // 128)
+    y = np.empty((M, N), np.uint16)
+    if _load().q8o_scaled_mm_group128(_p(a), _p(b), _p(s_tok), _p(s_grp),
+                                      M, N, K, _p(y)) != 0:
+        raise ValueError("oracle: K must be a multiple of 128")
+    return y
+
+
+def w8a16_ref(x_bf16, wq, s_ch, with_mag: bool = False):
+    """a6 reference.  -> fp64 y_ref [M,N] (and fp64 magnitude sums)."""
+    x = _c(x_bf16, np.uint16)
+    wq = _c(wq, np.int8)
+    s_ch = _c(s_ch, np.float32)
+    M, K = x.shape
+    N = wq.shape[0]
+    y = np.empty((M, N), np.float64)
+    mag = np.empty((M, N), np.float64) if with_mag else None
+    _load().q8o_w8a16_ref(_p(x), _p(wq), _p(s_ch), M, N, K, _p(y),
+                          _p(mag) if with_mag else None)
+    return (y, mag) if with_mag else y
+
+
+def smooth_scales(x_bf16, cap: float = 16.0) -> np.ndarray:
+    """s_j = min(cap, sqrtf(max_m |x[m,j]|)) -> fp32 [K]."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    s = np.empty((K,), np.float32)
+    if _load().q8o_smooth_scales(_p(x), M, K, cap, _p(s)) != 0:
+        raise ValueError("oracle: a smoothing scale is 0 (all-zero column)")
+    return s
+
+
+def smooth_fold_x(x_bf16, s) -> np.ndarray:
+    x = _c(x_bf16, np.uint16)
+    s = _c(s, np.float32)
+    M, K = x.shape
+    out = np.empty((M, K), np.uint16)
+    _load().q8o_smooth_fold_x(_p(x), _p(s), M, K, _p(out))
+    return out
+
+
+def smooth_fold_w(w_f32, s) -> np.ndarray:
+    w = _c(w_f32, np.float32)
+    s = _c(s, np.float32)
+    N, K = w.shape
+    out = np.empty((N, K), np.float32)
+    _load().q8o_smooth_fold_w(_p(w), _p(s), N, K, _p(out))
+    return out

@@ -1,0 +1,335 @@
+/*
+ * q8_oracle.c -- the CPU oracle for the W8A8 INT8 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library and includes nothing from it.
+ *
+ * Every routine is a plain, slow, obviously correct loop nest written from the
+ * definitions on the pages (IEEE fp32 arithmetic, round-to-nearest-even, no
+ * reordering beyond what the definition states).  Build with
+ *     gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
+ * so that no multiply-add is fused unless fmaf() is written, and so that the
+ * rounding mode is the default round-to-nearest-even (checked at run time by
+ * q8o_env_ok()).  OpenMP splits only independent outer loops (rows), which
+ * cannot change any result.
+ *
+ * Sources (page title, then section):
+ *  [P1] "Qwen3.8-27B -- SmoothQuant + activation-aware GPTQ, W8A8 INT8 (v3)",
+ *       section "Recipe": SmoothQuant folds with scales capped at 16; INT8
+ *       per-channel symmetric weights and INT8 per-token dynamic activations
+ *       for the W8A8 group; INT8 per-channel weights with BF16 activations for
+ *       the W8A16 group.  Section "Serving": --dtype bfloat16.
+ *  [P2] "lued/Qwen3.8-27B-INT8-W8A16-MTP", section "Why W8A16 on Ampere":
+ *       weight-only kernels rebuild the weights for a 16-bit GEMM.
+ *  [P3] "Qwen3.8-27B -- FP8 block + AWQ", section "Recipe": the smoothing fold
+ *       preserves the function; the new weight over the old one is a
+ *       separable row-times-column scale.
+ *  [P4] "Qwen3.8-27B-INT8-W8A8", section "Quantization": symmetric INT8
+ *       weights per output channel, INT8 dynamic per-token activations.
+ *  [P5] "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", section "Quantization details":
+ *       8 bits, group size 128, symmetric, desc_act false (groups are the
+ *       natural contiguous K blocks); true int8 x int8 compute with one weight
+ *       scale per 128-wide K block.
+ *
+ * Readings where the pages are silent (each one is also listed in the design
+ * notes):
+ *  - the activation scale is absmax/127 computed as ONE correctly rounded
+ *    fp32 division; a row whose absmax is 0 gets scale 0 and all-zero codes;
+ *  - a code is round-half-to-even of the correctly rounded fp32 quotient
+ *    x/s (a division, not a multiply by a reciprocal), clamped to [-127,127];
+ *  - (float)acc is the round-to-nearest-even int32 -> fp32 conversion;
+ *  - the per-channel epilogue is bf16_rne( (((float)acc) * s_tok) * s_ch ),
+ *    fp32 products in that order; there is no bias;
+ *  - the group-128 epilogue accumulates in fp32 with one fmaf per group in
+ *    ascending group order, starting from 0, then multiplies by s_tok once;
+ *  - W8A16 converts the int8 weight exactly and applies the channel scale in
+ *    the epilogue; the oracle returns the fp64 value of that sum;
+ *  - the smoothing scale is s_j = min(cap, sqrtf(max_m |X[m,j]|)) with cap 16
+ *    (exponent 0.5 on the plain column maximum), X' = bf16_rne(X / s_j) and
+ *    W' = fl32(W * s_j).
+ */
+#include <fenv.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- bf16 -- */
+
+/* bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits. */
+static float bf16_bits_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* fp32 -> bf16 with round-to-nearest, ties to even, on the bit pattern.
+ * NaN is kept a (quiet) NaN; infinities and overflow follow IEEE. */
+uint16_t q8o_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+float q8o_bf16_to_f32(uint16_t b) { return bf16_bits_to_f32(b); }
+
+/* 1 if the FPU is in round-to-nearest-even mode (every routine relies on it). */
+int q8o_env_ok(void) { return fegetround() == FE_TONEAREST; }
+
+/* ------------------------------------------------- symmetric INT8 codes -- */
+
+/* Absmax scale of n fp32 values: s = fl32(absmax / 127); 0 for a zero span.
+ * [P1 "Recipe"; P4 "Quantization"; P5 "Quantization details": symmetric] */
+static float absmax_scale(const float *v, int64_t n)
+{
+    float a = 0.0f;
+    for (int64_t k = 0; k < n; ++k) {
+        float m = fabsf(v[k]);
+        if (m > a)
+            a = m;
+    }
+    return a / 127.0f; /* one IEEE division; a == 0 gives 0 */
+}
+
+/* q = clamp(rne(fl32(x / s)), -127, 127); s == 0 gives 0. */
+static int8_t code_of(float x, float s)
+{
+    if (s == 0.0f)
+        return 0;
+    float t = x / s;          /* correctly rounded fp32 quotient */
+    float r = nearbyintf(t);  /* round half to even (default mode) */
+    if (r > 127.0f)
+        r = 127.0f;
+    if (r < -127.0f)
+        r = -127.0f;
+    return (int8_t)r;
+}
+
+/* a1-a3: per-token dynamic quantization of a bf16 activation matrix.
+ * x: [M][K] bf16 bits, row-major.  xq: [M][K] int8.  s_tok: [M] fp32.
+ * [P1 "Recipe": INT8 per-token dynamic activations; P4 "Quantization"] */
+void q8o_quant_per_token(const uint16_t *x, int64_t M, int64_t K,
+                         int8_t *xq, float *s_tok)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+        for (int64_t k = 0; k < K; ++k)
+            row[k] = bf16_bits_to_f32(x[m * K + k]);
+        float s = absmax_scale(row, K);
+        s_tok[m] = s;
+        for (int64_t k = 0; k < K; ++k)
+            xq[m * K + k] = code_of(row[k], s);
+        free(row);
+    }
+}
+
+/* a0: offline symmetric weight quantization of an fp32 weight W [N][K].
+ * group == K: one scale per output channel (s: [N]).
+ * group == 128: one scale per (channel, contiguous 128-wide K block),
+ * s: [N][K/128] row-major.
+ * [P1 "Recipe" and P4 "Quantization": per-channel symmetric;
+ *  P5 "Quantization details": group size 128, symmetric, desc_act false]
+ * Returns 0, or -1 if group does not divide K. */
+int q8o_quant_weight(const float *w, int64_t N, int64_t K, int64_t group,
+                     int8_t *wq, float *s)
+{
+    if (group <= 0 || K % group != 0)
+        return -1;
+    const int64_t G = K / group;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < G; ++g) {
+            const float *span = w + n * K + g * group;
+            float sg = absmax_scale(span, group);
+            s[n * G + g] = sg;
+            for (int64_t k = 0; k < group; ++k)
+                wq[n * K + g * group + k] = code_of(span[k], sg);
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------- INT8 GEMM -- */
+
+/* a4: acc[m][n] = sum_k a[m][k] * b[n][k], exact (int64 loop).
+ * a: [M][K] int8, b: [N][K] int8 (PyTorch Linear layout), acc: [M][N] int32.
+ * [P1 "Serving": INT8 x INT8 on tensor cores; P5: true int8 x int8 compute]
+ * Returns 0, or -1 if some sum does not fit in int32 (then acc is clamped). */
+int q8o_mm_i32(const int8_t *a, const int8_t *b, int64_t M, int64_t N,
+               int64_t K, int32_t *acc)
+{
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t t = 0;
+            for (int64_t k = 0; k < K; ++k)
+                t += (int64_t)a[m * K + k] * (int64_t)b[n * K + k];
+            if (t > INT32_MAX) {
+                t = INT32_MAX;
+                bad = 1;
+            }
+            if (t < INT32_MIN) {
+                t = INT32_MIN;
+                bad = 1;
+            }
+            acc[m * N + n] = (int32_t)t;
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* a5: y[m][n] = bf16_rne( fl32( fl32((float)acc * s_tok[m]) * s_ch[n] ) ).
+ * [P1 "Recipe": per-token x per-channel scales; "Serving": bf16 dtype] */
+void q8o_epilogue_channel(const int32_t *acc, const float *s_tok,
+                          const float *s_ch, int64_t M, int64_t N,
+                          uint16_t *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float v = (float)acc[m * N + n]; /* RNE int32 -> fp32 */
+            v = v * s_tok[m];
+            v = v * s_ch[n];
+            y[m * N + n] = q8o_f32_to_bf16(v);
+        }
+    }
+}
+
+/* a4+a5 in one call, without storing the int32 matrix. */
+int q8o_scaled_mm(const int8_t *a, const int8_t *b, const float *s_tok,
+                  const float *s_ch, int64_t M, int64_t N, int64_t K,
+                  uint16_t *y)
+{
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t t = 0;
+            for (int64_t k = 0; k < K; ++k)
+                t += (int64_t)a[m * K + k] * (int64_t)b[n * K + k];
+            if (t > INT32_MAX || t < INT32_MIN)
+                bad = 1;
+            float v = (float)(int32_t)t;
+            v = v * s_tok[m];
+            v = v * s_ch[n];
+            y[m * N + n] = q8o_f32_to_bf16(v);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* a4+a5g: group-128 weights.  For g = 0 .. K/128-1 in order:
+ *   p_g = sum_{k in [128g, 128g+128)} a[m][k]*b[n][k]   (int32, exact;
+ *         |p_g| <= 128*128*128 < 2^24 so (float)p_g is exact)
+ *   acc = fmaf((float)p_g, s_grp[n][g], acc)           (acc starts at 0)
+ * then y = bf16_rne( fl32(acc * s_tok[m]) ).
+ * [P5 "Quantization details": one weight scale per 128-wide K block]
+ * Returns 0, or -1 if K is not a multiple of 128. */
+int q8o_scaled_mm_group128(const int8_t *a, const int8_t *b,
+                           const float *s_tok, const float *s_grp,
+                           int64_t M, int64_t N, int64_t K, uint16_t *y)
+{
+    if (K % 128 != 0)
+        return -1;
+    const int64_t G = K / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float acc = 0.0f;
+            for (int64_t g = 0; g < G; ++g) {
+                int32_t p = 0;
+                for (int64_t k = g * 128; k < g * 128 + 128; ++k)
+                    p += (int32_t)a[m * K + k] * (int32_t)b[n * K + k];
+                acc = fmaf((float)p, s_grp[n * G + g], acc);
+            }
+            float v = acc * s_tok[m];
+            y[m * N + n] = q8o_f32_to_bf16(v);
+        }
+    }
+    return 0;
+}
+
+/* a6 reference: W8A16.  y_ref[m][n] = s_ch[n] * sum_k x[m][k] * q[n][k] in
+ * fp64 (each product is exact in fp64), plus the magnitude sum
+ * mag[m][n] = s_ch[n] * sum_k |x[m][k]| * |q[n][k]| that sizes the
+ * floating-point error bound of any summation order.
+ * [P1 "Recipe": W8A16 group, INT8 per-channel weights with BF16 activations;
+ *  P2 "Why W8A16 on Ampere": weights are rebuilt for a 16-bit GEMM] */
+void q8o_w8a16_ref(const uint16_t *x, const int8_t *q, const float *s_ch,
+                   int64_t M, int64_t N, int64_t K, double *y_ref,
+                   double *mag)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double t = 0.0, u = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double xv = (double)bf16_bits_to_f32(x[m * K + k]);
+                double qv = (double)q[n * K + k];
+                t += xv * qv;
+                u += fabs(xv) * fabs(qv);
+            }
+            y_ref[m * N + n] = (double)s_ch[n] * t;
+            if (mag)
+                mag[m * N + n] = (double)s_ch[n] * u;
+        }
+    }
+}
+
+/* ------------------------------------------------ smoothing fold (a0) -- */
+
+/* s_j = min(cap, sqrtf(max_m |x[m][j]|)), j < K.  [P1 "Recipe": SmoothQuant
+ * folds, scales capped at 16; the plain column maximum with exponent 0.5
+ * stands in for the per-hook alpha and windowed statistic.]
+ * Returns 0, or -1 if some s_j is 0 (an all-zero column cannot be folded). */
+int q8o_smooth_scales(const uint16_t *x, int64_t M, int64_t K, float cap,
+                      float *s)
+{
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t j = 0; j < K; ++j) {
+        float a = 0.0f;
+        for (int64_t m = 0; m < M; ++m) {
+            float v = fabsf(bf16_bits_to_f32(x[m * K + j]));
+            if (v > a)
+                a = v;
+        }
+        float r = sqrtf(a);
+        if (r > cap)
+            r = cap;
+        s[j] = r;
+        if (!(r > 0.0f))
+            bad = 1;
+    }
+    return bad ? -1 : 0;
+}
+
+/* X' = bf16_rne(fl32(x / s_j)).  [P3 "Recipe": 1/s folded into the input] */
+void q8o_smooth_fold_x(const uint16_t *x, const float *s, int64_t M,
+                       int64_t K, uint16_t *xo)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < K; ++j)
+            xo[m * K + j] = q8o_f32_to_bf16(bf16_bits_to_f32(x[m * K + j]) / s[j]);
+}
+
+/* W' = fl32(w * s_j).  [P3 "Recipe": s folded into the next linear's input
+ * dimension] */
+void q8o_smooth_fold_w(const float *w, const float *s, int64_t N, int64_t K,
+                       float *wo)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < K; ++j)
+            wo[n * K + j] = w[n * K + j] * s[j];
+}
