@@ -1,0 +1,244 @@
+"""Benchmark of the W8A8 INT8 linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one pass of the W8A8 hot path over the prefill workload
+(X bf16 [8192, 5120] after the smoothing fold, W int8 [15360, 5120] with
+per-channel scales): per-token quantization of X (row absmax -> scale ->
+codes) followed by the INT8 x INT8 -> INT32 GEMM with the per-token x
+per-channel epilogue to bf16, both through the library's one-call entry
+point.  Inputs (synthetic, seeded) are resident in HBM before timing; the
+weight quantization and the fold are offline preparation, outside the timed
+region.  Prints one JSON line:
+  value    = 2*M*N*K*steps / elapsed  (TOPS, whole quant+GEMM step)
+  roofline = the GEMM kernel alone, timed with events on the launch stream,
+             against the INT8 dense MFMA peak (5.0 POP/s)
+  cpu_baseline = the CPU oracle on a bounded sample of the same workload
+  secondary    = decode (M=8) GB/s of the fused kernel with the weight copies
+             rotated past the 256 MB last-level cache, and the other workloads
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+import w8a8_int8_gemm_token_amd as q8  # noqa: E402
+
+METRIC = "W8A8 quant+GEMM TOPS at M=8192,K=5120,N=15360; % INT8 MFMA peak; M=8 GB/s"
+PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, published
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA, published
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def events_time(fn, iters: int) -> float:
+    """Average ms per call of fn() over iters calls, HIP events on the
+    current stream (the stream the library launches on)."""
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def prefill_setup(dev):
+    wl = synth.WORKLOADS["prefill"]
+    x = synth.activations(wl, 0).to(dev)
+    w = synth.weights(wl, 0).to(dev)
+    xo, wo, _ = q8.q8_smooth_fold(x, w)
+    del x, w
+    wq, sc = q8.q8_quant_weight(wo)
+    del wo
+    torch.cuda.synchronize()
+    return wl, xo, wq, sc
+
+
+def cpu_baseline(target_s: float = 12.0):
+    """The oracle (as it stands) on a bounded sample of the prefill workload:
+    quantize a block of token rows and run the scaled INT8 GEMM for them
+    against all 15360 channels.  Scaled to TOPS like the GPU figure."""
+    import oracle
+    wl = synth.WORKLOADS["prefill"]
+    x = synth.bf16_bits(synth.activations(wl, 0))
+    w = synth.weights(wl, 0).numpy()
+    s = oracle.smooth_scales(x)
+    xo = oracle.smooth_fold_x(x, s)
+    wq, sc = oracle.quant_weight(oracle.smooth_fold_w(w, s))
+    del w
+
+    def run(rows):
+        t0 = time.perf_counter()
+        xq, st = oracle.quant_per_token(np.ascontiguousarray(xo[:rows]))
+        oracle.scaled_mm(xq, wq, st, sc)
+        return time.perf_counter() - t0
+
+    rows = 4
+    t = run(rows)
+    rows = int(max(4, min(wl.M, rows * target_s / max(t, 1e-3))))
+    t = run(rows)
+    ops = 2.0 * rows * wl.N * wl.K
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {wl.M} token rows x all {wl.N} channels, K={wl.K} "
+                      f"(quant + INT32 GEMM + epilogue), {t:.1f} s"}
+
+
+def decode_gbs(dev, iters=200):
+    """Fused quant+GEMM at M in {1,8}: algorithmic bytes / kernel time, with
+    enough weight copies rotated that one cycle exceeds 2x the 256 MB MALL."""
+    wl = synth.WORKLOADS["decode"]
+    w = synth.weights(wl, 0).to(dev)
+    wq, sc = q8.q8_quant_weight(w)
+    del w
+    ncopy = 24  # 24 x 26.2 MB = 629 MB
+    wqs = [wq.clone() for _ in range(ncopy)]
+    out = {}
+    for M in (1, 8):
+        x = synth.activations(wl, 0, M=M).to(dev)
+        y = torch.empty((M, wl.N), dtype=torch.bfloat16, device=dev)
+        xq = torch.empty((M, wl.K), dtype=torch.int8, device=dev)
+        st = torch.empty((M,), dtype=torch.float32, device=dev)
+        state = {"i": 0}
+
+        def step():
+            i = state["i"]
+            q8.q8_quant_scaled_mm(x, wqs[i % ncopy], sc, out=y, xq_out=xq, scale_tok_out=st)
+            state["i"] = i + 1
+
+        for _ in range(3 * ncopy):
+            step()
+        torch.cuda.synchronize()
+        ms = events_time(step, iters)
+        nbytes = wl.N * wl.K + 4 * wl.N + 2 * M * wl.K + 2 * M * wl.N + 4 * M + M * wl.K
+        out[f"M{M}"] = {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                        "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "bytes": nbytes}
+    return out
+
+
+def group_tops(dev, iters=20):
+    wl = synth.WORKLOADS["group128"]
+    x = synth.activations(wl, 0).to(dev)
+    w = synth.weights(wl, 0).to(dev)
+    wq, sg = q8.q8_quant_weight(w, group=128)
+    xq, st = q8.q8_quant_per_token(x)
+    y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
+    f = lambda: q8.q8_scaled_mm_group128(xq, wq, st, sg, out=y)  # noqa: E731
+    for _ in range(3):
+        f()
+    ms = events_time(f, iters)
+    t = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
+    return {"us": ms * 1e3, "TOPS": t, "frac_int8_peak": t / PEAK_INT8_TOPS}
+
+
+def w8a16_tflops(dev, iters=10):
+    wl = synth.WORKLOADS["w8a16"]
+    x = synth.activations(wl, 0).to(dev)
+    w = synth.weights(wl, 0).to(dev)
+    wq, sc = q8.q8_quant_weight(w)
+    del w
+    y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
+    f = lambda: q8.w8a16_mm(x, wq, sc, out=y)  # noqa: E731
+    for _ in range(2):
+        f()
+    ms = events_time(f, iters)
+    t = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
+    return {"us": ms * 1e3, "TFLOPS": t, "frac_bf16_peak": t / PEAK_BF16_TFLOPS}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    q8.load()
+
+    log("setup: prefill workload")
+    wl, xo, wq, sc = prefill_setup(dev)
+    M, N, K = wl.M, wl.N, wl.K
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    st = torch.empty((M,), dtype=torch.float32, device=dev)
+
+    def step():
+        q8.q8_quant_scaled_mm(xo, wq, sc, out=y, xq_out=xq, scale_tok_out=st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ops = 2.0 * M * N * K
+    value = ops * args.steps / elapsed / 1e12
+
+    # dominant kernel (the INT8 GEMM) alone, events on the launch stream
+    gemm = lambda: q8.q8_scaled_mm(xq, wq, st, sc, out=y)  # noqa: E731
+    gemm_ms = events_time(gemm, args.steps)
+    quant = lambda: q8.q8_quant_per_token(xo, out=xq, scale_out=st)  # noqa: E731
+    quant_ms = events_time(quant, args.steps)
+    achieved = ops / (gemm_ms * 1e-3) / 1e12
+    quant_bytes = M * K * 2 + M * K + 4 * M
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_INT8_TOPS, "traffic": None,
+                "kernel": "gemm_i8_kernel (per-channel epilogue)",
+                "kernel_us": gemm_ms * 1e3}
+    secondary = {"quant_kernel": {"us": quant_ms * 1e3,
+                                  "GB/s": quant_bytes / (quant_ms * 1e-3) / 1e9}}
+    if not args.no_secondary:
+        log("secondary: decode")
+        secondary["decode"] = decode_gbs(dev)
+        log("secondary: group128")
+        secondary["group128"] = group_tops(dev)
+        log("secondary: w8a16")
+        secondary["w8a16"] = w8a16_tflops(dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline()
+    rec = {
+        "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": "prefill W8A8 linear: per-token quant + INT8 GEMM, "
+                               "M=8192 K=5120 N=15360, bf16 out", "M": M, "K": K, "N": N},
+        "frac_int8_peak": value / PEAK_INT8_TOPS,
+        "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,216 @@
+/*
+ * q8.h -- C ABI of libq8: the W8A8 INT8 linear layer (per-token dynamic
+ * activations, per-channel or group-128 symmetric INT8 weights) and its
+ * W8A16 companion, as hand-written HIP kernels for AMD MI355X (gfx950).
+ *
+ * The operation, as the pages state it (page title, section):
+ *  - "Qwen3.8-27B -- SmoothQuant + activation-aware GPTQ, W8A8 INT8 (v3)",
+ *    "Recipe": the W8A8 group uses INT8 per-channel symmetric weights and
+ *    INT8 per-token dynamic activations; the W8A16 group keeps BF16
+ *    activations with INT8 per-channel weights.  "Serving": W8A8 modules run
+ *    a scaled INT8 GEMM, W8A16 modules a weight-only GEMM; the activation
+ *    dtype is bfloat16.
+ *  - "Qwen3.8-27B-INT8-W8A8", "Quantization": symmetric INT8 weights per
+ *    output channel; INT8 dynamic per-token activations.
+ *  - "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", "Quantization details": group size
+ *    128, symmetric, desc_act false; true int8 x int8 compute needs one
+ *    weight scale per 128-wide K block.  "Serving (vLLM, gfx908 fork)": the
+ *    GEMM inputs are quantized to INT8 at run time.
+ *  - "Qwen3.8-27B -- FP8 block + AWQ", "Recipe": every quantized dimension is
+ *    divisible by 128; the smoothing fold (1/s into the input, s into the
+ *    weight's input dimension) preserves the function.
+ *
+ * Conventions (all entry points):
+ *  - Matrices are row-major with an explicit leading dimension in ELEMENTS.
+ *    X is [M,K] (tokens x input features), W is [N,K] (output channels x
+ *    input features, the PyTorch Linear layout, K contiguous), Y is [M,N].
+ *  - Every pointer is a DEVICE pointer owned by the caller.  The library
+ *    never allocates, frees or synchronizes; a call validates its arguments,
+ *    enqueues its kernels on `stream` (0 = the null stream) and returns.
+ *    Faults inside a kernel surface at the caller's next synchronization.
+ *  - Errors are return codes; nothing is printed and nothing throws.
+ *    Validation happens before any HIP call, so an invalid call enqueues
+ *    nothing and leaves the outputs untouched.
+ *  - M == 0 is a valid empty call (returns Q8_OK, enqueues nothing).
+ *  - bf16 values are passed as raw 16-bit patterns (q8_bf16).
+ *  - NaN or infinite inputs are outside the contract (results undefined,
+ *    no fault).
+ *  - Calls on one stream are ordered; calls that write the same output on
+ *    different streams race.
+ */
+#ifndef Q8_H
+#define Q8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    Q8_OK = 0,
+    Q8_EINVAL = 1,       /* null pointer, negative or zero size, ld < row */
+    Q8_EUNSUPPORTED = 2, /* a shape or alignment rule below is broken     */
+    Q8_EHIP = 3          /* the HIP runtime refused a launch              */
+} q8_status;
+
+typedef uint16_t q8_bf16; /* raw bfloat16 bits */
+typedef void *q8_stream;  /* hipStream_t; 0 selects the null stream */
+
+/* Largest K of any GEMM entry point: 128*128*K stays below 2^31, so the
+ * int32 accumulator cannot overflow even for the code -128. */
+#define Q8_MAX_K 130944
+
+/* Text for a status code (static storage; never NULL). */
+const char *q8_status_str(q8_status s);
+
+/* ------------------------------------------------------------------------
+ * q8_quant_per_token -- per-token dynamic symmetric INT8 quantization.
+ * For every row m of X:
+ *   a = max_k |x[m,k]|                    (exact, bf16 widened to fp32)
+ *   scale_tok[m] = a / 127                (one correctly rounded fp32 division;
+ *                                           0 when a == 0)
+ *   xq[m,k] = clamp(rne(x[m,k] / scale_tok[m]), -127, 127)
+ *             (correctly rounded fp32 quotient, round half to even; a zero
+ *              row gives all-zero codes)
+ * Cited: "...W8A8 INT8 (v3)", "Recipe" (INT8 per-token dynamic
+ * activations); "Qwen3.8-27B-INT8-W8A8", "Quantization".
+ *   x        [M, ldx]  bf16, read
+ *   xq       [M, ldxq] int8, written (columns 0..K-1)
+ *   scale_tok[M]       fp32, written
+ * Rules: M >= 0, K >= 1, ldx >= K, ldxq >= K.  Any K and alignment is
+ * accepted (a vector path is taken when rows are 16-byte aligned).
+ * ---------------------------------------------------------------------- */
+q8_status q8_quant_per_token(const q8_bf16 *x, int64_t ldx, int8_t *xq,
+                             int64_t ldxq, float *scale_tok, int64_t M,
+                             int64_t K, q8_stream stream);
+
+/* ------------------------------------------------------------------------
+ * q8_scaled_mm -- INT8 x INT8 -> INT32 GEMM with the per-token x
+ * per-channel scale epilogue, bf16 out:
+ *   acc[m,n] = sum_k a[m,k] * b[n,k]                     (exact int32)
+ *   c[m,n]   = bf16_rne( ((float)acc * scale_tok[m]) * scale_ch[n] )
+ *              (fp32 products in this order; no bias)
+ * Cited: "...W8A8 INT8 (v3)", "Recipe" and "Serving" (INT8 x INT8 on
+ * tensor cores, bfloat16 dtype); "Qwen3.8-27B-INT8-W8A8", "Quantization".
+ *   a         [M, lda] int8 activations codes (full int8 range accepted)
+ *   b         [N, ldb] int8 weight codes
+ *   scale_tok [M] fp32, scale_ch [N] fp32
+ *   c         [M, ldc] bf16, written (columns 0..N-1)
+ * Rules: M >= 0; N >= 16 and N % 16 == 0; K >= 128, K % 128 == 0,
+ * K <= Q8_MAX_K; lda, ldb >= K and multiples of 16; ldc >= N and a
+ * multiple of 8; a, b 16-byte aligned; c 16-byte aligned; scales 4-byte
+ * aligned.  Else Q8_EUNSUPPORTED (or Q8_EINVAL for null/negative).
+ * ---------------------------------------------------------------------- */
+q8_status q8_scaled_mm(const int8_t *a, int64_t lda, const int8_t *b,
+                       int64_t ldb, const float *scale_tok,
+                       const float *scale_ch, q8_bf16 *c, int64_t ldc,
+                       int64_t M, int64_t N, int64_t K, q8_stream stream);
+
+/* ------------------------------------------------------------------------
+ * q8_scaled_mm_group128 -- INT8 GEMM with one weight scale per (output
+ * channel, contiguous 128-wide K block), bf16 out.  For g = 0..K/128-1 in
+ * ascending order:
+ *   p_g = sum_{k in [128g, 128g+128)} a[m,k] * b[n,k]     (exact int32)
+ *   acc = fmaf((float)p_g, scale_grp[n*(K/128) + g], acc) (acc starts at 0)
+ * then c[m,n] = bf16_rne(acc * scale_tok[m]).
+ * Cited: "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", "Quantization details" (group
+ * size 128, symmetric, desc_act false; one weight scale per 128-wide K
+ * block for true int8 x int8 compute).
+ *   scale_grp [N, K/128] fp32 row-major (contiguous).
+ * Rules: as q8_scaled_mm.
+ * ---------------------------------------------------------------------- */
+q8_status q8_scaled_mm_group128(const int8_t *a, int64_t lda,
+                                const int8_t *b, int64_t ldb,
+                                const float *scale_tok,
+                                const float *scale_grp, q8_bf16 *c,
+                                int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                q8_stream stream);
+
+/* ------------------------------------------------------------------------
+ * w8a16_mm -- weight-only INT8 GEMM with bf16 activations, bf16 out:
+ *   c[m,n] = bf16_rne( scale_ch[n] * sum_k x[m,k] * (bf16)w[n,k] )
+ * The int8 -> bf16 weight conversion is exact; products and sums run on
+ * bf16 matrix cores with fp32 accumulation (summation order is the
+ * hardware's); the channel scale is applied once in the fp32 epilogue.
+ * Cited: "...W8A8 INT8 (v3)", "Recipe" (W8A16 group: INT8 per-channel
+ * weights, BF16 activations); "lued/Qwen3.8-27B-INT8-W8A16-MTP", "Why W8A16
+ * on Ampere" (weight-only kernels rebuild weights for a 16-bit GEMM).
+ *   x [M, ldx] bf16, w [N, ldw] int8, scale_ch [N] fp32, c [M, ldc] bf16.
+ * Rules: as q8_scaled_mm, with ldx >= K a multiple of 8 and x 16-byte
+ * aligned.
+ * ---------------------------------------------------------------------- */
+q8_status w8a16_mm(const q8_bf16 *x, int64_t ldx, const int8_t *w,
+                   int64_t ldw, const float *scale_ch, q8_bf16 *c,
+                   int64_t ldc, int64_t M, int64_t N, int64_t K,
+                   q8_stream stream);
+
+/* ------------------------------------------------------------------------
+ * q8_quant_scaled_mm -- the whole W8A8 layer in one call: per-token
+ * quantization of x (as q8_quant_per_token) followed by q8_scaled_mm.
+ * The quantized activations and their scales are written to the caller's
+ * xq / scale_tok buffers (they are outputs, and the GEMM's inputs).  For
+ * M <= 16 a single fused kernel quantizes and multiplies; otherwise two
+ * kernels run back to back on `stream`.
+ *   x [M, ldx] bf16; b [N, ldb] int8; scale_ch [N]; c [M, ldc] bf16;
+ *   xq [M, K] int8 (dense, ld = K), scale_tok [M] fp32.
+ * Rules: as q8_scaled_mm, plus ldx >= K a multiple of 8, x 16-byte aligned.
+ * ---------------------------------------------------------------------- */
+q8_status q8_quant_scaled_mm(const q8_bf16 *x, int64_t ldx, const int8_t *b,
+                             int64_t ldb, const float *scale_ch, q8_bf16 *c,
+                             int64_t ldc, int8_t *xq, float *scale_tok,
+                             int64_t M, int64_t N, int64_t K,
+                             q8_stream stream);
+
+/* ------------------------------------------------------------------------
+ * q8_mm_i32 -- the raw INT32 product acc[m,n] = sum_k a[m,k]*b[n,k]
+ * (exact), written as int32 [M, ldc].  A test hook for the INT8 mainloop.
+ * Rules: as q8_scaled_mm, with ldc >= N a multiple of 4.
+ * ---------------------------------------------------------------------- */
+q8_status q8_mm_i32(const int8_t *a, int64_t lda, const int8_t *b,
+                    int64_t ldb, int32_t *c, int64_t ldc, int64_t M,
+                    int64_t N, int64_t K, q8_stream stream);
+
+/* ------------------------------------------------------------------------
+ * q8_quant_weight -- offline symmetric INT8 weight quantization of an fp32
+ * weight W [N,K]: one scale per (row, contiguous span of `group` columns),
+ *   scale[n*(K/group) + g] = absmax(span) / 127   (correctly rounded)
+ *   wq[n,k] = clamp(rne(w[n,k] / scale), -127, 127)   (0 for a zero span)
+ * group == K gives per-output-channel scales; group == 128 the group-128
+ * layout [N, K/128].
+ * Cited: "...W8A8 INT8 (v3)", "Recipe" and "Qwen3.8-27B-INT8-W8A8",
+ * "Quantization" (per-channel symmetric); "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128",
+ * "Quantization details" (group 128, symmetric, natural K order).
+ *   w [N, ldw] fp32; wq [N, ldwq] int8; scale [N * K/group] fp32.
+ * Rules: N >= 0, K >= 1, group >= 1 dividing K, ldw, ldwq >= K.
+ * ---------------------------------------------------------------------- */
+q8_status q8_quant_weight(const float *w, int64_t ldw, int8_t *wq,
+                          int64_t ldwq, float *scale, int64_t N, int64_t K,
+                          int64_t group, q8_stream stream);
+
+/* ------------------------------------------------------------------------
+ * q8_smooth_fold -- offline smoothing fold of an activation sample X [M,K]
+ * and a weight W [N,K]:
+ *   s[j]   = min(cap, sqrtf(max_m |x[m,j]|))     (0 for an all-zero column,
+ *                                                  which must not be folded)
+ *   xo[m,j] = bf16_rne(x[m,j] / s[j])            (correctly rounded quotient)
+ *   wo[n,j] = w[n,j] * s[j]                      (fp32 product)
+ * Cited: "...W8A8 INT8 (v3)", "Recipe" (SmoothQuant folds, scales capped at
+ * 16); "Qwen3.8-27B -- FP8 block + AWQ", "Recipe" (1/s into the input side,
+ * s into the weight's input dimension; function-preserving).  The exponent
+ * 0.5 on the plain column maximum stands in for the pages' per-hook alpha
+ * and windowed statistic.
+ *   x [M, ldx] bf16; w [N, ldw] fp32; s [K] fp32 out; xo [M, ldxo] bf16 out;
+ *   wo [N, ldwo] fp32 out.  xo may equal x and wo may equal w (in place).
+ * Rules: M, N >= 1, K >= 1, lds >= K, cap > 0.
+ * ---------------------------------------------------------------------- */
+q8_status q8_smooth_fold(const q8_bf16 *x, int64_t ldx, const float *w,
+                         int64_t ldw, float *s, q8_bf16 *xo, int64_t ldxo,
+                         float *wo, int64_t ldwo, int64_t M, int64_t N,
+                         int64_t K, float cap, q8_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8_H */

@@ -1,0 +1,96 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every entry point that include/q8.h declares,
+and reject invalid arguments with the documented status code before any HIP
+call (so these calls are safe on a machine without a GPU).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import w8a8_int8_gemm_token_amd as q8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, EINVAL, EUNSUP = 0, 1, 2
+A = 0x10000  # fake, 16-byte aligned "device" addresses: never dereferenced
+B = 0x20000
+C = 0x30000
+S = 0x40000
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "q8.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q8_\w+|w8a16_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(q8.lib_path()):
+        pytest.skip("libq8.so not built")
+    return q8.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(q8.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(4):
+        assert lib.q8_status_str(code)
+    assert b"unknown" in lib.q8_status_str(99)
+
+
+def _mm(lib, a=A, lda=256, b=B, ldb=256, st=S, sc=S, c=C, ldc=128, M=16, N=128, K=256):
+    return lib.q8_scaled_mm(a, lda, b, ldb, st, sc, c, ldc, M, N, K, None)
+
+
+def test_scaled_mm_validation(lib):
+    assert _mm(lib, M=0) == OK                      # empty: nothing enqueued
+    assert _mm(lib, M=-1) == EINVAL
+    assert _mm(lib, a=None) == EINVAL
+    assert _mm(lib, st=None) == EINVAL
+    assert _mm(lib, K=0) == EINVAL
+    assert _mm(lib, lda=128) == EINVAL               # ld < K
+    assert _mm(lib, ldc=64) == EINVAL                # ld < N
+    assert _mm(lib, N=120, ldc=128) == EUNSUP        # N % 16
+    assert _mm(lib, K=200, lda=256, ldb=256) == EUNSUP  # K % 128
+    assert _mm(lib, K=q8.MAX_K + 128, lda=10**6, ldb=10**6) == EUNSUP
+    assert _mm(lib, a=A + 8) == EUNSUP               # misaligned
+    assert _mm(lib, lda=264) == EUNSUP               # ld not a multiple of 16
+    assert _mm(lib, ldc=132) == EUNSUP               # ldc not a multiple of 8
+    assert _mm(lib, sc=S + 2) == EUNSUP              # misaligned scale
+
+
+def test_other_entry_points_validation(lib):
+    assert lib.q8_quant_per_token(A, 256, B, 256, S, 0, 256, None) == OK
+    assert lib.q8_quant_per_token(None, 256, B, 256, S, 4, 256, None) == EINVAL
+    assert lib.q8_quant_per_token(A, 100, B, 256, S, 4, 256, None) == EINVAL
+    assert lib.q8_quant_per_token(A, 256, B, 256, S, 4, 0, None) == EINVAL
+    assert lib.q8_scaled_mm_group128(A, 256, B, 256, S, None, C, 128, 16, 128, 256, None) == EINVAL
+    assert lib.q8_scaled_mm_group128(A, 256, B, 256, S, S, C, 128, 16, 128, 192, None) == EUNSUP
+    assert lib.w8a16_mm(A, 260, B, 256, S, C, 128, 16, 128, 256, None) == EUNSUP
+    assert lib.w8a16_mm(A, 256, B, 256, None, C, 128, 16, 128, 256, None) == EINVAL
+    assert lib.q8_mm_i32(A, 256, B, 256, C, 130, 16, 128, 256, None) == EUNSUP
+    assert lib.q8_quant_scaled_mm(A, 256, B, 256, S, C, 128, None, S, 8, 128, 256, None) == EINVAL
+    assert lib.q8_quant_scaled_mm(A, 256, B, 256, S, C, 128, A + 4, S, 8, 128, 256, None) == EUNSUP
+    assert lib.q8_quant_weight(A, 256, B, 256, S, 16, 256, 100, None) == EUNSUP
+    assert lib.q8_quant_weight(A, 256, B, 256, S, 0, 256, 128, None) == OK
+    assert lib.q8_quant_weight(A, 256, B, 256, S, 16, 256, 0, None) == EINVAL
+    f = ctypes.c_float
+    assert lib.q8_smooth_fold(A, 256, B, 256, S, C, 256, C, 256, 0, 8, 256, f(16.0), None) == EINVAL
+    assert lib.q8_smooth_fold(A, 256, B, 256, S, C, 256, C, 256, 4, 8, 256, f(0.0), None) == EINVAL
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        q8.q8_quant_per_token(x)

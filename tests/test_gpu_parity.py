@@ -1,0 +1,368 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Integer and byte results (codes, scales, int32 sums, weight codes, folded
+inputs) must be bit-exact.  bf16 outputs of the W8A8 GEMMs must be within 1
+bf16 ulp of the oracle (distance on the ordered-integer map, +0 == -0).
+W8A16 outputs are checked against the oracle's fp64 sum with the
+floating-point error bound of any summation order (per-row relative norm
+<= 2e-2 and elementwise |y - ref| <= 2e-2*|ref| + K*2^-22*mag + bf16
+rounding).  Inputs are the seeded synthetic workloads (synth/); at the full
+sizes the oracle computes sampled rows.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w8a8_int8_gemm_token_amd as q8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def dev(t):
+    if isinstance(t, np.ndarray):
+        t = torch.from_numpy(np.ascontiguousarray(t))
+    return t.to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu()
+
+
+def bits(t_bf16_cpu):
+    return synth.bf16_bits(t_bf16_cpu)
+
+
+def ulp_dist(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    def ordered(u):
+        u = u.astype(np.int32)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def assert_ulp1(got_bits, ref_bits, what):
+    d = ulp_dist(got_bits, ref_bits)
+    n_off = int((d > 0).sum())
+    say(f"{what}: max ulp {int(d.max()) if d.size else 0}, {n_off}/{d.size} not bit-equal")
+    assert d.size == 0 or d.max() <= 1, what
+
+
+# ---------------------------------------------------------------- quant --
+
+@pytest.mark.parametrize("name,seed", [("tiny", 0), ("tiny", 1), ("decode", 0),
+                                       ("decode", 1), ("decode", 2),
+                                       ("group128", 0), ("w8a16", 0)])
+def test_quant_per_token_workloads(name, seed):
+    say("quant", name, seed)
+    x = synth.activations(synth.WORKLOADS[name], seed)
+    xq_ref, s_ref = oracle.quant_per_token(bits(x))
+    xq, s = q8.q8_quant_per_token(dev(x))
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+
+
+@pytest.mark.parametrize("M,K,pad", [(1, 1, 0), (3, 7, 0), (5, 100, 3), (17, 136, 0),
+                                     (4, 512, 0), (9, 520, 8), (6, 2048, 0), (2, 8192, 0),
+                                     (3, 8200, 0), (2, 13824, 0), (1, 40000, 8)])
+def test_quant_per_token_ragged(M, K, pad):
+    say("quant ragged", M, K, pad)
+    xfull, _ = synth.custom(M, K + pad, 16, seed=M * 1000 + K, outlier_cols=3)
+    x = xfull[:, :K]
+    xq_ref, s_ref = oracle.quant_per_token(bits(x.contiguous()))
+    xd = dev(xfull)[:, :K]
+    xq, s = q8.q8_quant_per_token(xd)
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+
+
+def test_quant_zero_rows_and_ties():
+    rows = [
+        [127, 2.5, 3.5, -2.5, 0.5, 1.5, -0.5, -1.5],
+        [0] * 8,
+        [63.5, 1.25, 1.75, -1.25, 0.25, 0.75, -0.75, 62.75],
+        [-254, 5, 7, -5, 1, 3, -3, 253],
+    ]
+    x = torch.tensor(rows, dtype=torch.float32).to(torch.bfloat16)
+    x = torch.cat([x] * 64, dim=1)  # K = 512 (vector path)
+    xq_ref, s_ref = oracle.quant_per_token(bits(x))
+    xq, s = q8.q8_quant_per_token(dev(x))
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    assert s_ref[1] == 0 and not xq_ref[1].any()
+
+
+def test_quant_empty():
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    xq, s = q8.q8_quant_per_token(x)
+    assert xq.shape == (0, 256) and s.shape == (0,)
+
+
+# --------------------------------------------------------- weight quant --
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "group128", "w8a16"])
+def test_quant_weight(name):
+    wl = synth.WORKLOADS[name]
+    say("weight quant", name)
+    w = synth.weights(wl, 0)
+    wd = dev(w)
+    wq_ref, s_ref = oracle.quant_weight(w.numpy())
+    wq, s = q8.q8_quant_weight(wd)
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(host(wq).numpy(), wq_ref)
+    wq_ref, s_ref = oracle.quant_weight(w.numpy(), group=128)
+    wq, s = q8.q8_quant_weight(wd, group=128)
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(host(wq).numpy(), wq_ref)
+
+
+# ---------------------------------------------------------- smooth fold --
+
+def test_smooth_fold_prefill_full():
+    wl = synth.WORKLOADS["prefill"]
+    say("smooth fold prefill full size")
+    x = synth.activations(wl, 0)
+    w = synth.weights(wl, 0)
+    s_ref = oracle.smooth_scales(bits(x))
+    xo_ref = oracle.smooth_fold_x(bits(x), s_ref)
+    wo_ref = oracle.smooth_fold_w(w.numpy(), s_ref)
+    xo, wo, s = q8.q8_smooth_fold(dev(x), dev(w))
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(bits(host(xo)), xo_ref)
+    np.testing.assert_array_equal(host(wo).numpy(), wo_ref)
+
+
+def test_smooth_fold_cap_and_in_place():
+    x = torch.tensor([[1024.0, 4.0, -2.25, 0.5], [3.0, -1.0, 1.0, 0.25]]).to(torch.bfloat16)
+    w = torch.ones((16, 4), dtype=torch.float32)
+    s_ref = oracle.smooth_scales(bits(x))
+    xd, wd = dev(x), dev(w)
+    _, _, s = q8.q8_smooth_fold(xd, wd, x_out=xd, w_out=wd)
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(bits(host(xd)), oracle.smooth_fold_x(bits(x), s_ref))
+    np.testing.assert_array_equal(host(wd).numpy(), oracle.smooth_fold_w(w.numpy(), s_ref))
+
+
+# ------------------------------------------------------------ INT32 GEMM -
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (16, 128, 256), (31, 144, 384),
+                                   (64, 256, 128), (65, 128, 256), (130, 272, 640),
+                                   (257, 400, 1024), (300, 512, 512)])
+def test_mm_i32(M, N, K):
+    say("mm_i32", M, N, K)
+    a = synth.int8_uniform((M, K), seed=M + K)
+    b = synth.int8_uniform((N, K), seed=N + 7 * K)
+    ref = oracle.mm_i32(a, b)
+    got = host(q8.q8_mm_i32(dev(a), dev(b))).numpy()
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_mm_i32_extremes_max_k():
+    K = q8.MAX_K
+    say("mm_i32 max K", K)
+    a = np.full((16, K), -128, np.int8)
+    b = np.full((16, K), -128, np.int8)
+    b[1] = 127
+    b[2, ::2] = 127
+    ref = oracle.mm_i32(a, b)
+    got = host(q8.q8_mm_i32(dev(a), dev(b))).numpy()
+    np.testing.assert_array_equal(got, ref)
+    assert ref[0, 0] == 128 * 128 * K
+
+
+def test_mm_i32_strided_operands():
+    M, N, K = 70, 160, 256
+    a = synth.int8_uniform((M, K + 64), seed=3)
+    b = synth.int8_uniform((N, K + 32), seed=4)
+    ref = oracle.mm_i32(np.ascontiguousarray(a[:, :K]), np.ascontiguousarray(b[:, :K]))
+    outbuf = torch.zeros((M, N + 12), dtype=torch.int32, device=DEV)
+    q8.q8_mm_i32(dev(a)[:, :K], dev(b)[:, :K], out=outbuf[:, :N])
+    got = host(outbuf).numpy()
+    np.testing.assert_array_equal(got[:, :N], ref)
+    assert not got[:, N:].any(), "wrote outside the output view"
+
+
+# ------------------------------------------------------------ W8A8 layer -
+
+def _layer_inputs(name, seed, M=None):
+    wl = synth.WORKLOADS[name]
+    x = synth.activations(wl, seed, M=M)
+    w = synth.weights(wl, seed)
+    return wl, x, w
+
+
+@pytest.mark.parametrize("name,seed", [("tiny", 0), ("tiny", 1), ("tiny", 2),
+                                       ("decode", 0), ("decode", 1), ("decode", 2)])
+def test_scaled_mm_small_workloads(name, seed):
+    say("scaled_mm", name, seed)
+    wl, x, w = _layer_inputs(name, seed)
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y_ref = oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref)
+    wq, sc = q8.q8_quant_weight(dev(w))
+    # two-step path
+    xq, st = q8.q8_quant_per_token(dev(x))
+    y = q8.q8_scaled_mm(xq, wq, st, sc)
+    assert_ulp1(bits(host(y)), y_ref, f"{name}/{seed} two-step")
+    # one-call path (fused kernel for M <= 16)
+    y2, xq2, st2 = q8.q8_quant_scaled_mm(dev(x), wq, sc)
+    np.testing.assert_array_equal(host(xq2).numpy(), xq_ref)
+    np.testing.assert_array_equal(host(st2).numpy(), st_ref)
+    assert_ulp1(bits(host(y2)), y_ref, f"{name}/{seed} fused")
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 15, 16, 17, 33, 64, 65, 200])
+def test_quant_scaled_mm_token_counts(M):
+    say("quant_scaled_mm M", M)
+    K, N = 5120, 1024
+    x, w = synth.custom(M, K, N, seed=M, outlier_cols=52)
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y_ref = oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref)
+    wq, sc = q8.q8_quant_weight(dev(w))
+    y, xq, st = q8.q8_quant_scaled_mm(dev(x), wq, sc)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    np.testing.assert_array_equal(host(st).numpy(), st_ref)
+    assert_ulp1(bits(host(y)), y_ref, f"M={M}")
+    y3 = q8.q8_scaled_mm(xq, wq, st, sc)
+    assert_ulp1(bits(host(y3)), y_ref, f"M={M} scaled_mm")
+
+
+def test_scaled_mm_ragged_and_zero_rows():
+    M, N, K = 131, 208, 384
+    x, w = synth.custom(M, K, N, seed=5, outlier_cols=4)
+    x[7] = 0
+    x[130] = 0
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y_ref = oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref)
+    wq, sc = q8.q8_quant_weight(dev(w))
+    y, xq, st = q8.q8_quant_scaled_mm(dev(x), wq, sc)
+    yb = bits(host(y))
+    assert_ulp1(yb, y_ref, "ragged")
+    assert not (yb[7] & 0x7FFF).any() and not (yb[130] & 0x7FFF).any()
+
+
+def test_prefill_full_size_sampled_rows():
+    """The prefill workload at full size, in the benchmark's launch
+    configuration (fold, weight quant, then the one-call layer), compared on
+    sampled rows (first, last, tile edges, random)."""
+    wl = synth.WORKLOADS["prefill"]
+    say("prefill full size")
+    x = synth.activations(wl, 0)
+    w = synth.weights(wl, 0)
+    s_ref = oracle.smooth_scales(bits(x))
+    xo_ref = oracle.smooth_fold_x(bits(x), s_ref)
+    wo_ref = oracle.smooth_fold_w(w.numpy(), s_ref)
+    wq_ref, sc_ref = oracle.quant_weight(wo_ref)
+    xq_ref, st_ref = oracle.quant_per_token(xo_ref)
+    xo, wo, s = q8.q8_smooth_fold(dev(x), dev(w))
+    del w
+    wq, sc = q8.q8_quant_weight(wo)
+    y, xq, st = q8.q8_quant_scaled_mm(xo, wq, sc)
+    np.testing.assert_array_equal(host(st).numpy(), st_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    np.testing.assert_array_equal(host(sc).numpy(), sc_ref)
+    np.testing.assert_array_equal(host(wq).numpy(), wq_ref)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 4095, 8190, 8191],
+                                     rng.integers(0, wl.M, 23)]))
+    y_ref = oracle.scaled_mm(xq_ref[rows], wq_ref, st_ref[rows], sc_ref)
+    yh = bits(host(y))
+    assert_ulp1(yh[rows], y_ref, "prefill sampled rows")
+
+
+# ------------------------------------------------------------ group 128 --
+
+@pytest.mark.parametrize("M,N,K", [(16, 128, 256), (33, 144, 384), (130, 256, 1024),
+                                   (257, 128, 128)])
+def test_group128_shapes(M, N, K):
+    say("group128", M, N, K)
+    x, w = synth.custom(M, K, N, seed=M + N, outlier_cols=3)
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sg_ref = oracle.quant_weight(w.numpy(), group=128)
+    y_ref = oracle.scaled_mm_group128(xq_ref, wq_ref, st_ref, sg_ref)
+    xq, st = q8.q8_quant_per_token(dev(x))
+    wq, sg = q8.q8_quant_weight(dev(w), group=128)
+    y = q8.q8_scaled_mm_group128(xq, wq, st, sg)
+    assert_ulp1(bits(host(y)), y_ref, f"group128 {M}x{N}x{K}")
+
+
+def test_group128_full_size_sampled_rows():
+    wl = synth.WORKLOADS["group128"]
+    say("group128 full size")
+    x = synth.activations(wl, 0)
+    w = synth.weights(wl, 0)
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sg_ref = oracle.quant_weight(w.numpy(), group=128)
+    xq, st = q8.q8_quant_per_token(dev(x))
+    wq, sg = q8.q8_quant_weight(dev(w), group=128)
+    np.testing.assert_array_equal(host(sg).numpy(), sg_ref)
+    y = q8.q8_scaled_mm_group128(xq, wq, st, sg)
+    rows = np.array([0, 1, 63, 64, 127, 128, 2047, 4094, 4095, 1234, 3000])
+    y_ref = oracle.scaled_mm_group128(xq_ref[rows], wq_ref, st_ref[rows], sg_ref)
+    assert_ulp1(bits(host(y))[rows], y_ref, "group128 sampled rows")
+
+
+# --------------------------------------------------------------- W8A16 --
+
+def _check_w8a16(y_bits, x_bits, wq, s_ch, what):
+    K = x_bits.shape[1]
+    y_ref, mag = oracle.w8a16_ref(x_bits, wq, s_ch, with_mag=True)
+    y = (y_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    err = np.abs(y - y_ref)
+    bound = 2e-2 * np.abs(y_ref) + K * 2.0 ** -22 * mag + 2.0 ** -8 * np.abs(y_ref)
+    rel = np.linalg.norm(y - y_ref, axis=1) / np.maximum(np.linalg.norm(y_ref, axis=1), 1e-30)
+    say(f"{what}: max row rel {rel.max():.2e}, max err/bound {(err / np.maximum(bound, 1e-300)).max():.3f}")
+    assert rel.max() <= 2e-2, what
+    assert np.all(err <= bound), what
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 128, 256), (33, 144, 384), (130, 256, 1024),
+                                   (64, 512, 2048), (300, 128, 13824)])
+def test_w8a16_shapes(M, N, K):
+    say("w8a16", M, N, K)
+    wl = synth.WORKLOADS["w8a16"]
+    x = synth.activations(wl, 0, M=M, K=K)
+    w = synth.weights(wl, 0, N=N, K=K)
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    wq, sc = q8.q8_quant_weight(dev(w))
+    y = q8.w8a16_mm(dev(x), wq, sc)
+    _check_w8a16(bits(host(y)), bits(x), wq_ref, sc_ref, f"w8a16 {M}x{N}x{K}")
+
+
+def test_w8a16_full_size_sampled_rows():
+    wl = synth.WORKLOADS["w8a16"]
+    say("w8a16 full size")
+    x = synth.activations(wl, 0)
+    w = synth.weights(wl, 0)
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    wq, sc = q8.q8_quant_weight(dev(w))
+    y = q8.w8a16_mm(dev(x), wq, sc)
+    rows = np.array([0, 1, 40, 81, 82, 83, 127, 128, 4096, 8190, 8191])
+    xb = bits(x)
+    _check_w8a16(bits(host(y))[rows], np.ascontiguousarray(xb[rows]), wq_ref, sc_ref,
+                 "w8a16 sampled rows")
+
+
+# ------------------------------------------------------- determinism ----
+
+def test_repeat_calls_bitwise_identical():
+    M, N, K = 300, 512, 1024
+    x, w = synth.custom(M, K, N, seed=9, outlier_cols=10)
+    wq, sc = q8.q8_quant_weight(dev(w))
+    xd = dev(x)
+    y1, _, _ = q8.q8_quant_scaled_mm(xd, wq, sc)
+    y2, _, _ = q8.q8_quant_scaled_mm(xd, wq, sc)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))

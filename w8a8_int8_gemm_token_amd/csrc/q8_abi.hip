@@ -1,0 +1,197 @@
+// q8_abi.hip -- the C ABI of libq8 (declared in include/q8.h): argument
+// validation and kernel dispatch.  Validation runs on the host before any
+// HIP call, so an invalid call returns an error code and enqueues nothing.
+#include "q8.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "decode.hpp"
+#include "gemm_i8.hpp"
+#include "quant.hpp"
+#include "w8a16.hpp"
+
+namespace {
+
+using namespace q8;
+
+inline bool al(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline q8_status hip_status(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_EHIP; }
+
+inline hipStream_t st(q8_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Shape rules shared by the GEMM entry points (see q8.h).  `lda_mult` is the
+// multiple the activation leading dimension must be (16 int8 codes or 8 bf16
+// values: 16 bytes), `ldc_mult` that of the output (8 bf16 or 4 int32).
+q8_status check_gemm(const void* a, int64_t lda, int64_t lda_mult, const void* b, int64_t ldb,
+                     const void* c, int64_t ldc, int64_t ldc_mult, int64_t M, int64_t N,
+                     int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return Q8_EINVAL;
+    if (M == 0) return Q8_OK;
+    if (!a || !b || !c || N == 0 || K == 0) return Q8_EINVAL;
+    if (lda < K || ldb < K || ldc < N) return Q8_EINVAL;
+    if (N % 16 != 0 || K % 128 != 0 || K > Q8_MAX_K) return Q8_EUNSUPPORTED;
+    if (M > INT32_MAX / 2 || N > INT32_MAX / 2) return Q8_EUNSUPPORTED;
+    if (lda % lda_mult != 0 || ldb % 16 != 0 || ldc % ldc_mult != 0) return Q8_EUNSUPPORTED;
+    if (!al(a, 16) || !al(b, 16) || !al(c, 16)) return Q8_EUNSUPPORTED;
+    return Q8_OK;
+}
+
+// Scale vectors: non-null (Q8_EINVAL) and 4-byte aligned (Q8_EUNSUPPORTED).
+inline q8_status check_scale(const float* s) {
+    if (s == nullptr) return Q8_EINVAL;
+    return al(s, 4) ? Q8_OK : Q8_EUNSUPPORTED;
+}
+
+// Tile configurations of the INT8 GEMM, chosen by the token count M.
+template <int EPI>
+hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
+    if (p.M <= 64) return launch_gemm_i8<32, 128, 128, 1, 4, EPI, 8>(p, s);
+    return launch_gemm_i8<128, 128, 64, 2, 2, EPI, 8>(p, s);
+}
+
+hipError_t run_gemm_group(const GemmArgs& p, hipStream_t s) {
+    if (p.M <= 64) return launch_gemm_i8<32, 128, 128, 1, 4, EPI_GROUP, 8>(p, s);
+    return launch_gemm_i8<128, 128, 128, 2, 2, EPI_GROUP, 8>(p, s);
+}
+
+hipError_t run_quant(const uint16_t* x, int64_t ldx, int8_t* xq, int64_t ldxq, float* s, int M,
+                     int K, hipStream_t stream) {
+    const dim3 grid((M + 3) / 4), block(256);
+    const bool vec = K % 8 == 0 && ldx % 8 == 0 && ldxq % 8 == 0 && al(x, 16) && al(xq, 8);
+    if (vec && K <= 512)
+        hipLaunchKernelGGL(quant_per_token_reg<1>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
+    else if (vec && K <= 2048)
+        hipLaunchKernelGGL(quant_per_token_reg<4>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
+    else if (vec && K <= 8192)
+        hipLaunchKernelGGL(quant_per_token_reg<16>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
+    else
+        hipLaunchKernelGGL(quant_per_token_any, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* q8_status_str(q8_status s) {
+    switch (s) {
+        case Q8_OK: return "ok";
+        case Q8_EINVAL: return "invalid argument (null pointer, negative/zero size, ld < row)";
+        case Q8_EUNSUPPORTED: return "unsupported shape or alignment";
+        case Q8_EHIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+q8_status q8_quant_per_token(const q8_bf16* x, int64_t ldx, int8_t* xq, int64_t ldxq,
+                             float* scale_tok, int64_t M, int64_t K, q8_stream stream) {
+    if (M < 0 || K < 0) return Q8_EINVAL;
+    if (M == 0) return Q8_OK;
+    if (!x || !xq || !scale_tok || K == 0 || ldx < K || ldxq < K) return Q8_EINVAL;
+    if (!al(x, 2) || !al(scale_tok, 4)) return Q8_EUNSUPPORTED;
+    if (M > INT32_MAX / 2 || K > INT32_MAX / 2) return Q8_EUNSUPPORTED;
+    return hip_status(run_quant(x, ldx, xq, ldxq, scale_tok, (int)M, (int)K, st(stream)));
+}
+
+q8_status q8_scaled_mm(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
+                       const float* scale_tok, const float* scale_ch, q8_bf16* c, int64_t ldc,
+                       int64_t M, int64_t N, int64_t K, q8_stream stream) {
+    q8_status r = check_gemm(a, lda, 16, b, ldb, c, ldc, 8, M, N, K);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_tok);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_ch);
+    if (r != Q8_OK || M == 0) return r;
+    GemmArgs p{a, lda, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};
+    return hip_status(run_gemm_i8<EPI_CHANNEL>(p, st(stream)));
+}
+
+q8_status q8_scaled_mm_group128(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
+                                const float* scale_tok, const float* scale_grp, q8_bf16* c,
+                                int64_t ldc, int64_t M, int64_t N, int64_t K, q8_stream stream) {
+    q8_status r = check_gemm(a, lda, 16, b, ldb, c, ldc, 8, M, N, K);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_tok);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_grp);
+    if (r != Q8_OK || M == 0) return r;
+    GemmArgs p{a, lda, b, ldb, scale_tok, scale_grp, c, ldc, (int)M, (int)N, (int)K};
+    return hip_status(run_gemm_group(p, st(stream)));
+}
+
+q8_status q8_mm_i32(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb, int32_t* c,
+                    int64_t ldc, int64_t M, int64_t N, int64_t K, q8_stream stream) {
+    q8_status r = check_gemm(a, lda, 16, b, ldb, c, ldc, 4, M, N, K);
+    if (r != Q8_OK || M == 0) return r;
+    GemmArgs p{a, lda, b, ldb, nullptr, nullptr, c, ldc, (int)M, (int)N, (int)K};
+    return hip_status(run_gemm_i8<EPI_I32>(p, st(stream)));
+}
+
+q8_status w8a16_mm(const q8_bf16* x, int64_t ldx, const int8_t* w, int64_t ldw,
+                   const float* scale_ch, q8_bf16* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                   q8_stream stream) {
+    q8_status r = check_gemm(x, ldx, 8, w, ldw, c, ldc, 8, M, N, K);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_ch);
+    if (r != Q8_OK || M == 0) return r;
+    W8A16Args p{x, ldx, w, ldw, scale_ch, c, ldc, (int)M, (int)N, (int)K};
+    if (M <= 64) return hip_status(launch_w8a16<32, 128, 64, 1, 4, 8>(p, st(stream)));
+    return hip_status(launch_w8a16<128, 128, 64, 2, 2, 8>(p, st(stream)));
+}
+
+q8_status q8_quant_scaled_mm(const q8_bf16* x, int64_t ldx, const int8_t* b, int64_t ldb,
+                             const float* scale_ch, q8_bf16* c, int64_t ldc, int8_t* xq,
+                             float* scale_tok, int64_t M, int64_t N, int64_t K,
+                             q8_stream stream) {
+    q8_status r = check_gemm(x, ldx, 8, b, ldb, c, ldc, 8, M, N, K);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_ch);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_tok);
+    if (r == Q8_OK && M > 0 && !xq) r = Q8_EINVAL;
+    if (r == Q8_OK && M > 0 && !al(xq, 16)) r = Q8_EUNSUPPORTED;
+    if (r != Q8_OK || M == 0) return r;
+    hipStream_t s = st(stream);
+    if (M <= DECODE_MAX_M && K <= DECODE_MAX_K) {
+        DecodeArgs p{x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok, (int)M, (int)N, (int)K};
+        return hip_status(launch_decode<1>(p, s));
+    }
+    hipError_t e = run_quant(x, ldx, xq, K, scale_tok, (int)M, (int)K, s);
+    if (e != hipSuccess) return Q8_EHIP;
+    GemmArgs p{xq, K, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};
+    return hip_status(run_gemm_i8<EPI_CHANNEL>(p, s));
+}
+
+q8_status q8_quant_weight(const float* w, int64_t ldw, int8_t* wq, int64_t ldwq, float* scale,
+                          int64_t N, int64_t K, int64_t group, q8_stream stream) {
+    if (N < 0 || K < 0 || group < 0) return Q8_EINVAL;
+    if (N == 0) return Q8_OK;
+    if (!w || !wq || !scale || K == 0 || group == 0 || ldw < K || ldwq < K) return Q8_EINVAL;
+    if (K % group != 0) return Q8_EUNSUPPORTED;
+    if (!al(w, 4) || !al(scale, 4)) return Q8_EUNSUPPORTED;
+    const int64_t spans = K / group;
+    if (N * spans > INT32_MAX || group > INT32_MAX) return Q8_EUNSUPPORTED;
+    hipLaunchKernelGGL(quant_weight_span, dim3((unsigned)(N * spans)), dim3(256), 0, st(stream),
+                       w, ldw, wq, ldwq, scale, (int)group, (int)spans);
+    return hip_status(hipGetLastError());
+}
+
+q8_status q8_smooth_fold(const q8_bf16* x, int64_t ldx, const float* w, int64_t ldw, float* s,
+                         q8_bf16* xo, int64_t ldxo, float* wo, int64_t ldwo, int64_t M,
+                         int64_t N, int64_t K, float cap, q8_stream stream) {
+    if (M <= 0 || N <= 0 || K <= 0) return Q8_EINVAL;
+    if (!x || !w || !s || !xo || !wo) return Q8_EINVAL;
+    if (ldx < K || ldw < K || ldxo < K || ldwo < K || !(cap > 0.0f)) return Q8_EINVAL;
+    if (!al(x, 2) || !al(xo, 2) || !al(w, 4) || !al(wo, 4) || !al(s, 4)) return Q8_EUNSUPPORTED;
+    if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return Q8_EUNSUPPORTED;
+    hipStream_t h = st(stream);
+    const int iK = (int)K, iM = (int)M, iN = (int)N;
+    const unsigned kb = (unsigned)((K + 255) / 256);
+    hipLaunchKernelGGL(fill_u32, dim3(kb), dim3(256), 0, h, reinterpret_cast<u32*>(s), 0u, iK);
+    const int rows = 64;
+    hipLaunchKernelGGL(colmax_bf16, dim3(kb, (unsigned)((M + rows - 1) / rows)), dim3(256), 0, h, x,
+                       ldx, reinterpret_cast<u32*>(s), iM, iK, rows);
+    hipLaunchKernelGGL(smooth_finalize, dim3(kb), dim3(256), 0, h, s, cap, iK);
+    hipLaunchKernelGGL(fold_x_bf16, dim3(kb, (unsigned)(M < 65535 ? M : 65535)), dim3(256), 0, h, x,
+                       ldx, s, xo, ldxo, iM, iK);
+    hipLaunchKernelGGL(fold_w_f32, dim3(kb, (unsigned)(N < 65535 ? N : 65535)), dim3(256), 0, h, w,
+                       ldw, s, wo, ldwo, iN, iK);
+    return hip_status(hipGetLastError());
+}
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+// quant.hpp -- per-token activation quantization, offline weight quantization
+// and the smoothing fold, for gfx950.
+//
+// Per-token dynamic symmetric INT8 ("Qwen3.8-27B -- SmoothQuant +
+// activation-aware GPTQ, W8A8 INT8 (v3)", section "Recipe";
+// "Qwen3.8-27B-INT8-W8A8", section "Quantization"): per row, scale =
+// absmax/127 (one correctly rounded division), code = clamp(rne(x/scale),
+// -127, 127).  HBM-bound: one read of the bf16 row, one write of the codes.
+#pragma once
+
+#include "q8_device.hpp"
+
+namespace q8 {
+
+// Max |x| over the 8 bf16 values packed in a uint4 (exact).
+__device__ __forceinline__ float absmax8(uint4 v) {
+    float a = __builtin_fmaxf(__builtin_fabsf(bf16_lo(v.x)), __builtin_fabsf(bf16_hi(v.x)));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v.y)), __builtin_fabsf(bf16_hi(v.y))));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v.z)), __builtin_fabsf(bf16_hi(v.z))));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v.w)), __builtin_fabsf(bf16_hi(v.w))));
+    return a;
+}
+
+// The 8 codes of the 8 bf16 values in v, packed little-endian in a uint2.
+__device__ __forceinline__ uint2 codes8(uint4 v, float s) {
+    uint2 r;
+    r.x = pack_i8x4(code_of(bf16_lo(v.x), s), code_of(bf16_hi(v.x), s),
+                    code_of(bf16_lo(v.y), s), code_of(bf16_hi(v.y), s));
+    r.y = pack_i8x4(code_of(bf16_lo(v.z), s), code_of(bf16_hi(v.z), s),
+                    code_of(bf16_lo(v.w), s), code_of(bf16_hi(v.w), s));
+    return r;
+}
+
+// One wave per row; the row stays in registers (NC 16-byte chunks per lane,
+// K <= NC * 512).  Needs K % 8 == 0, 16-byte aligned x rows and 8-byte
+// aligned xq rows.  4 rows per 256-thread workgroup.
+template <int NC>
+__global__ __launch_bounds__(256) void quant_per_token_reg(
+    const uint16_t* __restrict__ x, int64_t ldx, int8_t* __restrict__ xq, int64_t ldxq,
+    float* __restrict__ s_tok, int M, int K) {
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (int64_t)m * ldx);
+    const int nch = K >> 3;
+    uint4 v[NC];
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nch) {
+            v[i] = xr[c];
+            a = __builtin_fmaxf(a, absmax8(v[i]));
+        }
+    }
+    a = wave_max(a);
+    const float s = a / 127.0f;
+    if (lane == 0) s_tok[m] = s;
+    uint2* qr = reinterpret_cast<uint2*>(xq + (int64_t)m * ldxq);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nch) qr[c] = codes8(v[i], s);
+    }
+}
+
+// Any K, any alignment: one wave per row, two passes over the row.
+__global__ __launch_bounds__(256) void quant_per_token_any(
+    const uint16_t* __restrict__ x, int64_t ldx, int8_t* __restrict__ xq, int64_t ldxq,
+    float* __restrict__ s_tok, int M, int K) {
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const uint16_t* xr = x + (int64_t)m * ldx;
+    float a = 0.0f;
+    for (int k = lane; k < K; k += 64) a = __builtin_fmaxf(a, __builtin_fabsf(bf16_to_f32(xr[k])));
+    a = wave_max(a);
+    const float s = a / 127.0f;
+    if (lane == 0) s_tok[m] = s;
+    int8_t* qr = xq + (int64_t)m * ldxq;
+    for (int k = lane; k < K; k += 64) qr[k] = (int8_t)code_of(bf16_to_f32(xr[k]), s);
+}
+
+// Offline weight quantization: one workgroup per (row, span of G columns).
+__global__ __launch_bounds__(256) void quant_weight_span(
+    const float* __restrict__ w, int64_t ldw, int8_t* __restrict__ wq, int64_t ldwq,
+    float* __restrict__ scale, int G, int spans_per_row) {
+    __shared__ float red[4];
+    const int row = blockIdx.x / spans_per_row;
+    const int g = blockIdx.x % spans_per_row;
+    const float* src = w + (int64_t)row * ldw + (int64_t)g * G;
+    int8_t* dst = wq + (int64_t)row * ldwq + (int64_t)g * G;
+    float a = 0.0f;
+    for (int k = threadIdx.x; k < G; k += 256) a = __builtin_fmaxf(a, __builtin_fabsf(src[k]));
+    a = wave_max(a);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    a = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    const float s = a / 127.0f;
+    if (threadIdx.x == 0) scale[blockIdx.x] = s;
+    for (int k = threadIdx.x; k < G; k += 256) dst[k] = (int8_t)code_of(src[k], s);
+}
+
+// ---- smoothing fold ("...W8A8 INT8 (v3)", "Recipe": SmoothQuant folds with
+// scales capped at 16; "Qwen3.8-27B -- FP8 block + AWQ", "Recipe": the fold
+// is function-preserving) ------------------------------------------------
+
+__global__ void fill_u32(u32* __restrict__ p, u32 v, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// Column maximum of |x| over ROWS rows per workgroup, merged with an integer
+// atomic max on the fp32 bit pattern (order-free for non-negative floats, so
+// the result is exact and deterministic).
+__global__ __launch_bounds__(256) void colmax_bf16(const uint16_t* __restrict__ x, int64_t ldx,
+                                                   u32* __restrict__ cmax, int M, int K,
+                                                   int rows) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= K) return;
+    const int m0 = blockIdx.y * rows;
+    const int m1 = min(M, m0 + rows);
+    float a = 0.0f;
+    for (int m = m0; m < m1; ++m) a = __builtin_fmaxf(a, __builtin_fabsf(bf16_to_f32(x[(int64_t)m * ldx + j])));
+    atomicMax(cmax + j, __float_as_uint(a));
+}
+
+__global__ void smooth_finalize(float* __restrict__ s, float cap, int K) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= K) return;
+    const float r = __builtin_sqrtf(s[j]);  // correctly rounded (no fast-math)
+    s[j] = r > cap ? cap : r;
+}
+
+// x and xo may alias (in-place fold): each element is read, then written, by
+// the same thread.
+__global__ __launch_bounds__(256) void fold_x_bf16(const uint16_t* x, int64_t ldx,
+                                                   const float* __restrict__ s,
+                                                   uint16_t* xo, int64_t ldxo, int M,
+                                                   int K) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= K) return;
+    const float sj = s[j];
+    for (int m = blockIdx.y; m < M; m += gridDim.y)
+        xo[(int64_t)m * ldxo + j] = f32_to_bf16(bf16_to_f32(x[(int64_t)m * ldx + j]) / sj);
+}
+
+__global__ __launch_bounds__(256) void fold_w_f32(const float* w, int64_t ldw,
+                                                  const float* __restrict__ s,
+                                                  float* wo, int64_t ldwo, int N,
+                                                  int K) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= K) return;
+    const float sj = s[j];
+    for (int n = blockIdx.y; n < N; n += gridDim.y)
+        wo[(int64_t)n * ldwo + j] = w[(int64_t)n * ldw + j] * sj;
+}
+
+}  // namespace q8
