@@ -61,6 +61,11 @@ typedef void *q8_stream;  /* hipStream_t; 0 selects the null stream */
  * int32 accumulator cannot overflow even for the code -128. */
 #define Q8_MAX_K 130944
 
+/* GEMM operands are addressed with 32-bit offsets: (rows + 256) * ld * elem
+ * bytes of every matrix operand must stay below this bound (2 GiB minus
+ * one 128-byte stage of slack); larger operands give Q8_EUNSUPPORTED. */
+#define Q8_MAX_OPERAND_BYTES (((int64_t)1 << 31) - 256)
+
 /* Text for a status code (static storage; never NULL). */
 const char *q8_status_str(q8_status s);
 
@@ -100,7 +105,8 @@ q8_status q8_quant_per_token(const q8_bf16 *x, int64_t ldx, int8_t *xq,
  * Rules: M >= 0; N >= 16 and N % 16 == 0; K >= 128, K % 128 == 0,
  * K <= Q8_MAX_K; lda, ldb >= K and multiples of 16; ldc >= N and a
  * multiple of 8; a, b 16-byte aligned; c 16-byte aligned; scales 4-byte
- * aligned.  Else Q8_EUNSUPPORTED (or Q8_EINVAL for null/negative).
+ * aligned; (M + 256) * lda and (N + 256) * ldb below Q8_MAX_OPERAND_BYTES.
+ * Else Q8_EUNSUPPORTED (or Q8_EINVAL for null/negative).
  * ---------------------------------------------------------------------- */
 q8_status q8_scaled_mm(const int8_t *a, int64_t lda, const int8_t *b,
                        int64_t ldb, const float *scale_tok,

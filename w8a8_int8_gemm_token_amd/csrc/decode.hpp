@@ -63,8 +63,8 @@ __global__ __launch_bounds__((4 * CG + 4) * 64) void decode_fused_kernel(DecodeA
         const int xw = wid - NWW;
         const int nch = K >> 3;
         for (int m = xw; m < M; m += 4) {
-            const uint4* xr = reinterpret_cast<const uint4*>(p.x + (int64_t)m * p.ldx);
-            uint4 v[DECODE_MAX_K / 512];
+            const v4u* xr = reinterpret_cast<const v4u*>(p.x + (int64_t)m * p.ldx);
+            v4u v[DECODE_MAX_K / 512];
             float a = 0.0f;
 #pragma unroll
             for (int i = 0; i < DECODE_MAX_K / 512; ++i) {
@@ -84,10 +84,10 @@ __global__ __launch_bounds__((4 * CG + 4) * 64) void decode_fused_kernel(DecodeA
             for (int i = 0; i < DECODE_MAX_K / 512; ++i) {
                 const int c = lane + 64 * i;
                 if (c < nch) {
-                    const uint2 q = codes8(v[i], s);
-                    *reinterpret_cast<uint2*>(lq + m * LQ + c * 8) = q;
+                    const v2u q = codes8(v[i], s);
+                    *reinterpret_cast<v2u*>(lq + m * LQ + c * 8) = q;
                     if (blockIdx.x == 0)
-                        *reinterpret_cast<uint2*>(p.xq + (int64_t)m * K + c * 8) = q;
+                        *reinterpret_cast<v2u*>(p.xq + (int64_t)m * K + c * 8) = q;
                 }
             }
         }
@@ -141,10 +141,10 @@ __global__ __launch_bounds__((4 * CG + 4) * 64) void decode_fused_kernel(DecodeA
         const float u = (float)t[e] * st;
         v[e] = u * p.s_ch[ch + e];
     }
-    uint2 o;
-    o.x = pack_bf16x2(v[0], v[1]);
-    o.y = pack_bf16x2(v[2], v[3]);
-    *reinterpret_cast<uint2*>(p.c + (int64_t)tok * p.ldc + ch) = o;
+    v2u o;
+    o[0] = pack_bf16x2(v[0], v[1]);
+    o[1] = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<v2u*>(p.c + (int64_t)tok * p.ldc + ch) = o;
 }
 
 template <int CG>

@@ -1,31 +1,54 @@
-// gemm_i8.hpp -- tiled INT8 x INT8 -> INT32 GEMM on CDNA4 int8 MFMA
-// (v_mfma_i32_32x32x32_i8), with the scale epilogues of the W8A8 layer.
+// gemm_i8.hpp -- INT8 x INT8 -> INT32 GEMM on CDNA4 int8 MFMA
+// (v_mfma_i32_32x32x32_i8) with the scale epilogues of the W8A8 layer.
 //
-//   acc[m,n] = sum_k x[m,k] * w[n,k]          exact int32
+//   acc[m,n] = sum_k x[m,k] * w[n,k]                       exact int32
 //   EPI_CHANNEL: y = bf16_rne(((float)acc * s_tok[m]) * s_ch[n])
-//   EPI_GROUP:   per 128-wide K block g (ascending), acc_g exact int32 and
-//                f = fmaf((float)acc_g, s_grp[n,g], f); y = bf16_rne(f*s_tok[m])
-//   EPI_I32:     raw int32 acc
+//   EPI_GROUP:   for each 128-wide K block g in ascending order, the exact
+//                int32 block sum p_g is folded as f = fmaf((float)p_g,
+//                s_grp[n,g], f); y = bf16_rne(f * s_tok[m])
+//   EPI_I32:     the raw int32 acc
 // "Qwen3.8-27B -- SmoothQuant + activation-aware GPTQ, W8A8 INT8 (v3)",
 // sections "Recipe" and "Serving" (INT8 x INT8 with per-token x per-channel
 // scales, bf16 out); "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", "Quantization
 // details" (one weight scale per 128-wide K block).
 //
-// Design (gfx950): a workgroup owns a BM (tokens) x BN (channels) output
-// tile; WM x WN waves each own a (BM/WM) x (BN/WN) register tile of 32x32
-// MFMA blocks.  The weight tile feeds the MFMA A operand (32 channels) and
-// the activation tile the B operand (32 tokens), so a lane's accumulators
-// hold four consecutive channels of one token: the epilogue stores 8-byte
-// bf16 quads along N.  K advances BK bytes per stage through a double-
-// buffered LDS tile (rows padded by 16 bytes so the 16-byte fragment reads of
-// 32 rows hit distinct banks); the next stage's global loads are in flight
-// in registers while the current stage's MFMAs run.  Because an integer sum
-// is order-free, the K order inside one MFMA only has to agree between the
-// two operands: lane l of both fragments carries the 16 bytes at
-// k = 32*kk + 16*(l/32) of its row.
+// Tiling: a workgroup owns a BM (tokens) x BN (channels) output tile; WM x WN
+// waves each own a (BM/WM) x (BN/WN) register tile of 32x32 MFMA blocks.  The
+// weight tile feeds the MFMA A operand (32 channels) and the activation tile
+// the B operand (32 tokens), so a lane's accumulators hold four consecutive
+// channels of one token and the epilogue stores 8-byte bf16 quads along N.
+// Because an integer sum is order-free, the K order inside one MFMA only has
+// to agree between the two operands: lane l of both fragments carries the 16
+// bytes at k = 32*kk + 16*(l/32) of its row.
+//
+// Data movement (BK = 128 bytes of K per stage):
+//  * global -> LDS with buffer_load_dwordx4 ... lds (direct to LDS, no VGPR
+//    staging).  Every wave instruction moves 8 rows x 128 contiguous bytes
+//    (whole 128-byte lines).  One buffer resource per operand; a row past
+//    the matrix edge falls outside the resource's range and reads as zero
+//    (its products are never stored).  The row/stage part of the address is
+//    a scalar offset, so a lane keeps only two vector offsets per operand.
+//  * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at slot
+//    c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).  The MFMA fragment reads
+//    (one 16-byte chunk per lane, 32 consecutive rows) are then free of bank
+//    conflicts for 32- and 64-bank LDS, and since f ignores row bits >= 4 the
+//    fragment of each further 32-row block is an immediate offset away.
+//  * two LDS stages, held in distinct LDS objects so that the compiler can
+//    tell the stage being filled from the one being read (it would otherwise
+//    drain every in-flight direct load before each LDS read).
+// Schedule of one stage (four 32-deep sub-steps, two fragment register
+// sets): the fragments of sub-step s+1 are read while the MFMAs of sub-step
+// s run (sched_group_barrier puts the LDS reads, and in sub-step 0 the next
+// stage's direct loads, between the MFMAs); halfway through sub-step 3 the
+// wave waits for its own direct loads of the next stage and all its LDS
+// reads of this one, one barrier publishes the next stage and frees this
+// one, and the first fragments of the next stage are read while the last
+// MFMAs of this stage drain.  One barrier per stage.
 #pragma once
 
 #include "q8_device.hpp"
+
+#define Q8_LDS __attribute__((address_space(3)))
 
 namespace q8 {
 
@@ -43,23 +66,68 @@ struct GemmArgs {
     int M, N, K;
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int EPI, int GM>
+// s_waitcnt with vmcnt = N and lgkmcnt = 0 (expcnt untouched).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without the implicit release fence of __syncthreads
+// (which would drain every in-flight global load); the empty asm statements
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// sched_group_barrier masks
+constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100;
+
+// Schedule of one region: N_MFMA MFMAs, with N_DS LDS reads and N_VM direct
+// loads spread evenly behind them.
+template <int N_MFMA, int N_DS, int N_VM, int I = 0>
+__device__ __forceinline__ void interleave() {
+    if constexpr (I < N_MFMA) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        constexpr int v = N_VM * (I + 1) / N_MFMA - N_VM * I / N_MFMA;
+        constexpr int d = N_DS * (I + 1) / N_MFMA - N_DS * I / N_MFMA;
+        if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, v, 0);
+        if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, d, 0);
+        interleave<N_MFMA, N_DS, N_VM, I + 1>();
+    }
+}
+
+__device__ __forceinline__ int lds_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Buffer resource over `bytes` bytes at p (raw buffer, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int GM>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
-    constexpr int NT = WM * WN * 64;
+    constexpr int BK = 128;
+    constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int LDSW = BK + 16;  // padded row stride (bytes)
-    constexpr int CPR = BK / 16;   // 16-byte chunks per row and stage
-    constexpr int XCH = BM * CPR / NT;
-    constexpr int WCH = BN * CPR / NT;
-    constexpr int KK = BK / 32;
+    constexpr int XIW = BM / 8 / NW, WIW = BN / 8 / NW;  // 8-row loads per wave and stage
+    constexpr int SGI = (EPI == EPI_GROUP) ? BN / 64 : 0;  // 64-scale loads per stage
+    constexpr int LPS = XIW + WIW + (SGI + NW - 1) / NW;
+    constexpr int NR = TM + TN;  // fragment reads per sub-step
+    constexpr int NM = TM * TN;  // MFMAs per sub-step
+    constexpr int NM0 = NM / 2;  // MFMAs of sub-step 3 before the hand-over
     static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "tile shape");
-    static_assert(XCH * NT == BM * CPR && WCH * NT == BN * CPR, "load split");
-    static_assert(EPI != EPI_GROUP || (BK == 128 && BN <= NT), "group tiles");
+    static_assert(XIW * 8 * NW == BM && WIW * 8 * NW == BN, "load split");
+    static_assert(EPI != EPI_GROUP || BN % 64 == 0, "group scales load 64 at a time");
 
-    __shared__ __attribute__((aligned(16))) int8_t lx[2][BM * LDSW];
-    __shared__ __attribute__((aligned(16))) int8_t lw[2][BN * LDSW];
-    __shared__ __attribute__((aligned(16))) float lsg[2][EPI == EPI_GROUP ? BN : 4];
+    __shared__ __attribute__((aligned(1024))) int8_t lx0[BM * BK];
+    __shared__ __attribute__((aligned(1024))) int8_t lx1[BM * BK];
+    __shared__ __attribute__((aligned(1024))) int8_t lw0[BN * BK];
+    __shared__ __attribute__((aligned(1024))) int8_t lw1[BN * BK];
+    __shared__ __attribute__((aligned(16))) float ls0[EPI == EPI_GROUP ? BN : 4];
+    __shared__ __attribute__((aligned(16))) float ls1[EPI == EPI_GROUP ? BN : 4];
 
     const int M = p.M, N = p.N, K = p.K;
     const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
@@ -71,32 +139,62 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     const int tile_n = (id % per_group) / gsz;
     const int m0 = tile_m * BM, n0 = tile_n * BN;
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid % WM, wn = wid / WM;
+    const int hi = lane >> 5;
 
-    // This thread's global chunks: rows past the matrix edge are clamped to
-    // the last row (their products are computed and never stored).
-    const int8_t* xs[XCH];
-    int xo[XCH];
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-        const int cidx = tid + i * NT, r = cidx / CPR, q = cidx % CPR;
-        xs[i] = p.x + (int64_t)min(m0 + r, M - 1) * p.ldx + q * 16;
-        xo[i] = r * LDSW + q * 16;
-    }
-    const int8_t* ws[WCH];
-    int wo[WCH];
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-        const int cidx = tid + i * NT, r = cidx / CPR, q = cidx % CPR;
-        ws[i] = p.w + (int64_t)min(n0 + r, N - 1) * p.ldw + q * 16;
-        wo[i] = r * LDSW + q * 16;
-    }
+    // ---- direct loads: instruction i of wave wid fills rows
+    // (wid*XIW + i)*8 .. +8 of the tile; lane l writes LDS slot l%8 of row
+    // l/8 of that group, i.e. global chunk (l%8) ^ f(row), and f(row)
+    // = (l/8) ^ (parity of the instruction's 8-row group).
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, (uint32_t)((int64_t)M * p.ldx));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, (uint32_t)((int64_t)N * p.ldw));
     const int G = K >> 7;
-    const float* sg_src = p.s_w + (int64_t)min(n0 + tid, N - 1) * G;
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.s_w, (uint32_t)((int64_t)N * G * 4));
+    const int lrow = lane >> 3, lslot = lane & 7;
+    const int xv[2] = {lrow * (int)p.ldx + ((lslot ^ lrow) << 4),
+                       lrow * (int)p.ldx + ((lslot ^ lrow ^ 1) << 4)};
+    const int wv[2] = {lrow * (int)p.ldw + ((lslot ^ lrow) << 4),
+                       lrow * (int)p.ldw + ((lslot ^ lrow ^ 1) << 4)};
+    const int xs0 = (m0 + wid * XIW * 8) * (int)p.ldx;  // scalar row offsets
+    const int ws0 = (n0 + wid * WIW * 8) * (int)p.ldw;
+    const int sv = (n0 + lane) * G * 4;  // group scales: channel n0 + 64*i + lane
 
-    uint4 rx[XCH], rw[WCH];
-    float rsg = 0.0f;
+    auto issue = [&](int kt, int8_t* bx, int8_t* bw, float* bs) __attribute__((always_inline)) {
+        const int koff = kt * BK;
+#pragma unroll
+        for (int i = 0; i < XIW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (Q8_LDS void*)(bx + (wid * XIW + i) * 1024), 16, xv[(wid * XIW + i) & 1],
+                xs0 + i * 8 * (int)p.ldx + koff, 0, 0);
+#pragma unroll
+        for (int i = 0; i < WIW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wr, (Q8_LDS void*)(bw + (wid * WIW + i) * 1024), 16, wv[(wid * WIW + i) & 1],
+                ws0 + i * 8 * (int)p.ldw + koff, 0, 0);
+        if constexpr (SGI > 0) {
+#pragma unroll
+            for (int i = 0; i < (SGI + NW - 1) / NW; ++i) {
+                const int j = wid + i * NW;  // 64-channel block of this load
+                if (j < SGI)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (Q8_LDS void*)(bs + j * 64), 4, sv,
+                                                             j * 64 * G * 4 + kt * 4, 0, 0);
+            }
+        }
+    };
+
+    // ---- fragment reads: sub-step kk of 32-row block b sits at
+    // base[kk] + b*32*BK (f is the same for rows r and r + 32b)
+    int wbase[4], xbase[4];
+    {
+        const int rw0 = wn * WTN + (lane & 31), rx0 = wm * WTM + (lane & 31);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            wbase[kk] = rw0 * BK + (((kk * 2 + hi) ^ lds_swizzle(rw0)) << 4);
+            xbase[kk] = rx0 * BK + (((kk * 2 + hi) ^ lds_swizzle(rx0)) << 4);
+        }
+    }
 
     v16i acc[TM][TN];
     v16f facc[EPI == EPI_GROUP ? TM : 1][EPI == EPI_GROUP ? TN : 1];
@@ -110,54 +208,32 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
 #pragma unroll
             for (int b = 0; b < TN; ++b) facc[a][b] = v16f{};
     }
+    v4i fw[2][TN], fx[2][TM];
 
-    auto gload = [&](int kt) {
-        const int64_t koff = (int64_t)kt * BK;
+    auto read = [&](int set, int kk, const int8_t* bx, const int8_t* bw) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < XCH; ++i) rx[i] = *reinterpret_cast<const uint4*>(xs[i] + koff);
+        for (int b = 0; b < TN; ++b)
+            fw[set][b] = *reinterpret_cast<const v4i*>(bw + wbase[kk] + b * 32 * BK);
 #pragma unroll
-        for (int i = 0; i < WCH; ++i) rw[i] = *reinterpret_cast<const uint4*>(ws[i] + koff);
-        if constexpr (EPI == EPI_GROUP) {
-            if (tid < BN) rsg = sg_src[kt];
+        for (int a = 0; a < TM; ++a)
+            fx[set][a] = *reinterpret_cast<const v4i*>(bx + xbase[kk] + a * 32 * BK);
+    };
+    auto mfma = [&](int set, int from, int to) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = from; t < to; ++t) {
+            const int a = t / TN, b = t % TN;
+            acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[set][b], fx[set][a], acc[a][b], 0, 0, 0);
         }
     };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < XCH; ++i) *reinterpret_cast<uint4*>(&lx[buf][xo[i]]) = rx[i];
-#pragma unroll
-        for (int i = 0; i < WCH; ++i) *reinterpret_cast<uint4*>(&lw[buf][wo[i]]) = rw[i];
+    // EPI_GROUP: fold the stage's 128-wide block sums into the fp32
+    // accumulators (the stage is group kt; groups arrive in ascending order)
+    auto fold = [&](const float* bs) __attribute__((always_inline)) {
         if constexpr (EPI == EPI_GROUP) {
-            if (tid < BN) lsg[buf][tid] = rsg;
-        }
-    };
-
-    const int frow = lane & 31, fk = (lane >> 5) * 16;
-    auto compute = [&](int buf) {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            v4i fw[TN], fx[TM];
-#pragma unroll
-            for (int b = 0; b < TN; ++b)
-                fw[b] = *reinterpret_cast<const v4i*>(
-                    &lw[buf][(wn * WTN + b * 32 + frow) * LDSW + kk * 32 + fk]);
-#pragma unroll
-            for (int a = 0; a < TM; ++a)
-                fx[a] = *reinterpret_cast<const v4i*>(
-                    &lx[buf][(wm * WTM + a * 32 + frow) * LDSW + kk * 32 + fk]);
-#pragma unroll
-            for (int a = 0; a < TM; ++a)
-#pragma unroll
-                for (int b = 0; b < TN; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[b], fx[a], acc[a][b], 0, 0, 0);
-        }
-        if constexpr (EPI == EPI_GROUP) {
-            // fold this 128-wide group into the fp32 accumulators, ascending g
 #pragma unroll
             for (int b = 0; b < TN; ++b) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const v4f sc = *reinterpret_cast<const v4f*>(
-                        &lsg[buf][wn * WTN + b * 32 + g * 8 + (lane >> 5) * 4]);
+                    const v4f sc = *reinterpret_cast<const v4f*>(bs + wn * WTN + b * 32 + g * 8 + hi * 4);
 #pragma unroll
                     for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -171,17 +247,62 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
         }
     };
 
+    // One stage held in (cx, cw, cs); the next stage goes to (nx, nw, ns).
+    // The last stage also issues loads for a stage K..K+127 that is never
+    // read: with buffer loads those offsets stay inside the operand's rows or
+    // fall outside the resource and read as zero, so the loop needs no tail.
+    auto stage = [&](int kt, const int8_t* cx, const int8_t* cw, const float* cs, int8_t* nx,
+                     int8_t* nw, float* ns) __attribute__((always_inline)) {
+        // sub-step 0: MFMAs on set 0; next stage's direct loads; set 1 <- kk 1
+        issue(kt + 1, nx, nw, ns);
+        read(1, 1, cx, cw);
+        mfma(0, 0, NM);
+        interleave<NM, NR, LPS>();
+        __builtin_amdgcn_sched_barrier(0);
+        // sub-step 1
+        read(0, 2, cx, cw);
+        mfma(1, 0, NM);
+        interleave<NM, NR, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        // sub-step 2
+        read(1, 3, cx, cw);
+        mfma(0, 0, NM);
+        interleave<NM, NR, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        // sub-step 3: part of the MFMAs, then the stage hand-over
+        if constexpr (EPI == EPI_GROUP) {
+            // the group fold reads this stage's scales: do it before the
+            // hand-over frees the stage
+            mfma(1, 0, NM);
+            fold(cs);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm_lgkm0<0>();
+            block_barrier();
+            read(0, 0, nx, nw);
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            mfma(1, 0, NM0);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm_lgkm0<0>();
+            block_barrier();
+            read(0, 0, nx, nw);
+            mfma(1, NM0, NM);
+            interleave<NM - NM0, NR, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     const int KT = K / BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) gload(kt + 1);
-        compute(cur);
-        if (kt + 1 < KT) lstore(cur ^ 1);
-        __syncthreads();
+    issue(0, lx0, lw0, ls0);
+    wait_vm_lgkm0<0>();
+    block_barrier();
+    read(0, 0, lx0, lw0);
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+        stage(kt, lx0, lw0, ls0, lx1, lw1, ls1);
+        stage(kt + 1, lx1, lw1, ls1, lx0, lw0, ls0);
     }
+    if (kt < KT) stage(kt, lx0, lw0, ls0, lx1, lw1, ls1);
 
     // ---------------------------------------------------------- epilogue --
 #pragma unroll
@@ -193,15 +314,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
         for (int b = 0; b < TN; ++b) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int ch = n0 + wn * WTN + b * 32 + g * 8 + (lane >> 5) * 4;
+                const int ch = n0 + wn * WTN + b * 32 + g * 8 + hi * 4;
                 if (ch >= N) continue;
                 if constexpr (EPI == EPI_I32) {
-                    int4 o;
-                    o.x = acc[a][b][g * 4 + 0];
-                    o.y = acc[a][b][g * 4 + 1];
-                    o.z = acc[a][b][g * 4 + 2];
-                    o.w = acc[a][b][g * 4 + 3];
-                    *reinterpret_cast<int4*>(static_cast<int32_t*>(p.c) + (int64_t)j * p.ldc + ch) = o;
+                    v4i o;
+                    o[0] = acc[a][b][g * 4 + 0];
+                    o[1] = acc[a][b][g * 4 + 1];
+                    o[2] = acc[a][b][g * 4 + 2];
+                    o[3] = acc[a][b][g * 4 + 3];
+                    *reinterpret_cast<v4i*>(static_cast<int32_t*>(p.c) + (int64_t)j * p.ldc + ch) = o;
                 } else {
                     float v[4];
 #pragma unroll
@@ -213,21 +334,29 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
                             v[e] = facc[a][b][g * 4 + e] * st;
                         }
                     }
-                    uint2 o;
-                    o.x = pack_bf16x2(v[0], v[1]);
-                    o.y = pack_bf16x2(v[2], v[3]);
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.c) + (int64_t)j * p.ldc + ch) = o;
+                    v2u o;
+                    o[0] = pack_bf16x2(v[0], v[1]);
+                    o[1] = pack_bf16x2(v[2], v[3]);
+                    *reinterpret_cast<v2u*>(static_cast<uint16_t*>(p.c) + (int64_t)j * p.ldc + ch) = o;
                 }
             }
         }
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int EPI, int GM>
+// The kernel addresses operands with 32-bit buffer offsets: tiles past the
+// edge form row offsets up to (rows + 255) * ld, plus one stage beyond K.
+inline bool gemm_offsets_fit(const GemmArgs& p) {
+    const int64_t lim = (int64_t)1 << 31;
+    return ((int64_t)p.M + 256) * p.ldx + 256 < lim && ((int64_t)p.N + 256) * p.ldw + 256 < lim &&
+           ((int64_t)p.N + 256) * (p.K / 128) * 4 + 256 < lim;
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int GM>
 inline hipError_t launch_gemm_i8(const GemmArgs& p, hipStream_t stream) {
     const int nbm = (p.M + BM - 1) / BM, nbn = (p.N + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, EPI, GM>), dim3(nbm * nbn),
-                       dim3(WM * WN * 64), 0, stream, p);
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, EPI, GM>), dim3(nbm * nbn), dim3(WM * WN * 64),
+                       0, stream, p);
     return hipGetLastError();
 }
 

@@ -35,6 +35,9 @@ q8_status check_gemm(const void* a, int64_t lda, int64_t lda_mult, const void* b
     if (M > INT32_MAX / 2 || N > INT32_MAX / 2) return Q8_EUNSUPPORTED;
     if (lda % lda_mult != 0 || ldb % 16 != 0 || ldc % ldc_mult != 0) return Q8_EUNSUPPORTED;
     if (!al(a, 16) || !al(b, 16) || !al(c, 16)) return Q8_EUNSUPPORTED;
+    // 32-bit buffer offsets inside the kernels (see Q8_MAX_OPERAND_BYTES)
+    const int64_t lim = Q8_MAX_OPERAND_BYTES;
+    if ((M + 256) * lda * (lda_mult == 8 ? 2 : 1) >= lim || (N + 256) * ldb >= lim) return Q8_EUNSUPPORTED;
     return Q8_OK;
 }
 
@@ -44,16 +47,20 @@ inline q8_status check_scale(const float* s) {
     return al(s, 4) ? Q8_OK : Q8_EUNSUPPORTED;
 }
 
-// Tile configurations of the INT8 GEMM, chosen by the token count M.
+// Tile configurations of the INT8 GEMM, chosen by the problem size: 32-token
+// tiles for small batches, 256 x 256 tiles (8 waves of 128 x 64) once there
+// are enough of them to fill the 256 CUs, 128 x 128 tiles in between.
 template <int EPI>
 hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
-    if (p.M <= 64) return launch_gemm_i8<32, 128, 128, 1, 4, EPI, 8>(p, s);
-    return launch_gemm_i8<128, 128, 64, 2, 2, EPI, 8>(p, s);
+    if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
+    const int64_t big_tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
+    if (big_tiles >= 256) return launch_gemm_i8<256, 256, 2, 4, EPI, 8>(p, s);
+    return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
 }
 
 hipError_t run_gemm_group(const GemmArgs& p, hipStream_t s) {
-    if (p.M <= 64) return launch_gemm_i8<32, 128, 128, 1, 4, EPI_GROUP, 8>(p, s);
-    return launch_gemm_i8<128, 128, 128, 2, 2, EPI_GROUP, 8>(p, s);
+    if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI_GROUP, 8>(p, s);
+    return launch_gemm_i8<128, 128, 2, 2, EPI_GROUP, 8>(p, s);
 }
 
 hipError_t run_quant(const uint16_t* x, int64_t ldx, int8_t* xq, int64_t ldxq, float* s, int M,

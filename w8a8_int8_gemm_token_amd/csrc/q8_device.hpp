@@ -12,6 +12,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned u32;
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // bf16 bits -> fp32 (exact: the bf16 pattern is the top half of the fp32 one)
 __device__ __forceinline__ float bf16_lo(u32 w) { return __uint_as_float(w << 16); }

@@ -12,22 +12,22 @@
 
 namespace q8 {
 
-// Max |x| over the 8 bf16 values packed in a uint4 (exact).
-__device__ __forceinline__ float absmax8(uint4 v) {
-    float a = __builtin_fmaxf(__builtin_fabsf(bf16_lo(v.x)), __builtin_fabsf(bf16_hi(v.x)));
-    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v.y)), __builtin_fabsf(bf16_hi(v.y))));
-    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v.z)), __builtin_fabsf(bf16_hi(v.z))));
-    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v.w)), __builtin_fabsf(bf16_hi(v.w))));
+// Max |x| over the 8 bf16 values packed in a v4u (exact).
+__device__ __forceinline__ float absmax8(v4u v) {
+    float a = __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[0])), __builtin_fabsf(bf16_hi(v[0])));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[1])), __builtin_fabsf(bf16_hi(v[1]))));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[2])), __builtin_fabsf(bf16_hi(v[2]))));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[3])), __builtin_fabsf(bf16_hi(v[3]))));
     return a;
 }
 
-// The 8 codes of the 8 bf16 values in v, packed little-endian in a uint2.
-__device__ __forceinline__ uint2 codes8(uint4 v, float s) {
-    uint2 r;
-    r.x = pack_i8x4(code_of(bf16_lo(v.x), s), code_of(bf16_hi(v.x), s),
-                    code_of(bf16_lo(v.y), s), code_of(bf16_hi(v.y), s));
-    r.y = pack_i8x4(code_of(bf16_lo(v.z), s), code_of(bf16_hi(v.z), s),
-                    code_of(bf16_lo(v.w), s), code_of(bf16_hi(v.w), s));
+// The 8 codes of the 8 bf16 values in v, packed little-endian in a v2u.
+__device__ __forceinline__ v2u codes8(v4u v, float s) {
+    v2u r;
+    r[0] = pack_i8x4(code_of(bf16_lo(v[0]), s), code_of(bf16_hi(v[0]), s),
+                    code_of(bf16_lo(v[1]), s), code_of(bf16_hi(v[1]), s));
+    r[1] = pack_i8x4(code_of(bf16_lo(v[2]), s), code_of(bf16_hi(v[2]), s),
+                    code_of(bf16_lo(v[3]), s), code_of(bf16_hi(v[3]), s));
     return r;
 }
 
@@ -41,9 +41,9 @@ __global__ __launch_bounds__(256) void quant_per_token_reg(
     const int lane = threadIdx.x & 63;
     const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (m >= M) return;
-    const uint4* xr = reinterpret_cast<const uint4*>(x + (int64_t)m * ldx);
+    const v4u* xr = reinterpret_cast<const v4u*>(x + (int64_t)m * ldx);
     const int nch = K >> 3;
-    uint4 v[NC];
+    v4u v[NC];
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void quant_per_token_reg(
     a = wave_max(a);
     const float s = a / 127.0f;
     if (lane == 0) s_tok[m] = s;
-    uint2* qr = reinterpret_cast<uint2*>(xq + (int64_t)m * ldxq);
+    v2u* qr = reinterpret_cast<v2u*>(xq + (int64_t)m * ldxq);
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int c = lane + 64 * i;

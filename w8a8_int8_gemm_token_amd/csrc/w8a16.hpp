@@ -30,16 +30,14 @@ struct W8A16Args {
 };
 
 // 4 int8 codes (one dword) -> 4 exact bf16 values (two dwords).
-__device__ __forceinline__ uint2 i8x4_to_bf16x4(u32 d) {
+__device__ __forceinline__ v2u i8x4_to_bf16x4(u32 d) {
     const float f0 = (float)(int8_t)(d & 0xFF);
     const float f1 = (float)(int8_t)((d >> 8) & 0xFF);
     const float f2 = (float)(int8_t)((d >> 16) & 0xFF);
     const float f3 = (float)(int8_t)(d >> 24);
     // the conversions are exact, so truncating to the top 16 bits is exact
-    uint2 r;
-    r.x = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-    r.y = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
-    return r;
+    return v2u{(__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u),
+               (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u)};
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int GM>
@@ -89,33 +87,33 @@ __global__ __launch_bounds__(WM* WN * 64) void w8a16_kernel(W8A16Args p) {
         wo[i] = r * LDSW + q * 32;
     }
 
-    uint4 rx[XCH], rw[WCH];
+    v4i rx[XCH], rw[WCH];
     v16f acc[TM][TN];
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
         for (int b = 0; b < TN; ++b) acc[a][b] = v16f{};
 
-    auto gload = [&](int kt) {
+    auto gload = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < XCH; ++i) rx[i] = *reinterpret_cast<const uint4*>(xs[i] + (int64_t)kt * 2 * BK);
+        for (int i = 0; i < XCH; ++i) rx[i] = *reinterpret_cast<const v4i*>(xs[i] + (int64_t)kt * 2 * BK);
 #pragma unroll
-        for (int i = 0; i < WCH; ++i) rw[i] = *reinterpret_cast<const uint4*>(ws[i] + (int64_t)kt * BK);
+        for (int i = 0; i < WCH; ++i) rw[i] = *reinterpret_cast<const v4i*>(ws[i] + (int64_t)kt * BK);
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < XCH; ++i) *reinterpret_cast<uint4*>(&lx[buf][xo[i]]) = rx[i];
+        for (int i = 0; i < XCH; ++i) *reinterpret_cast<v4i*>(&lx[buf][xo[i]]) = rx[i];
 #pragma unroll
         for (int i = 0; i < WCH; ++i) {
-            const uint2 a = i8x4_to_bf16x4(rw[i].x), b = i8x4_to_bf16x4(rw[i].y);
-            const uint2 c = i8x4_to_bf16x4(rw[i].z), d = i8x4_to_bf16x4(rw[i].w);
-            *reinterpret_cast<uint4*>(&lw[buf][wo[i]]) = uint4{a.x, a.y, b.x, b.y};
-            *reinterpret_cast<uint4*>(&lw[buf][wo[i] + 16]) = uint4{c.x, c.y, d.x, d.y};
+            const v2u a = i8x4_to_bf16x4(rw[i][0]), b = i8x4_to_bf16x4(rw[i][1]);
+            const v2u c = i8x4_to_bf16x4(rw[i][2]), d = i8x4_to_bf16x4(rw[i][3]);
+            *reinterpret_cast<v4u*>(&lw[buf][wo[i]]) = v4u{a[0], a[1], b[0], b[1]};
+            *reinterpret_cast<v4u*>(&lw[buf][wo[i] + 16]) = v4u{c[0], c[1], d[0], d[1]};
         }
     };
 
     const int frow = lane & 31, fk = (lane >> 5) * 16;
-    auto compute = [&](int buf) {
+    auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             v8bf fw[TN], fx[TM];
@@ -160,10 +158,8 @@ __global__ __launch_bounds__(WM* WN * 64) void w8a16_kernel(W8A16Args p) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = p.s_ch[ch + e] * acc[a][b][g * 4 + e];
-                uint2 o;
-                o.x = pack_bf16x2(v[0], v[1]);
-                o.y = pack_bf16x2(v[2], v[3]);
-                *reinterpret_cast<uint2*>(p.c + (int64_t)j * p.ldc + ch) = o;
+                *reinterpret_cast<v2u*>(p.c + (int64_t)j * p.ldc + ch) =
+                    v2u{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             }
         }
     }
