@@ -103,6 +103,39 @@ def test_quant_zero_rows_and_ties():
     assert s_ref[1] == 0 and not xq_ref[1].any()
 
 
+def test_quant_near_ties_and_tiny_scales():
+    """Rows built from the bf16 values where x * fl(1/s) and x / s round to
+    different codes (the kernels' reciprocal route must detect each such
+    near-tie and divide), plus rows whose scale is subnormal."""
+    allbf = (np.arange(0, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    rng = np.random.default_rng(0)
+    rows = []
+    for _ in range(300):
+        a = allbf[rng.integers(0x3F00, 0x4400)]
+        s = np.float32(np.float64(a) / 127.0)
+        xs = allbf[allbf <= a]
+        qd = np.rint((xs.astype(np.float64) / np.float64(s)).astype(np.float32))
+        qr = np.rint((xs * (np.float32(1.0) / s)).astype(np.float32))
+        idx = np.nonzero(qd != qr)[0]
+        if len(idx):
+            rows.append(np.concatenate([[a], xs[idx], -xs[idx]]).astype(np.float32))
+    assert len(rows) >= 10
+    K = 512
+    mat = np.zeros((len(rows) + 3, K), np.float32)
+    for i, r in enumerate(rows):
+        mat[i, :len(r)] = r[:K]
+    # subnormal and near-subnormal scales: absmax 1e-38, 2e-37, 1e-40
+    for j, amax in enumerate([1e-38, 2e-37, 1e-40]):
+        mat[len(rows) + j, :7] = np.array([1, 0.5, -0.25, 0.75, 0.3, -1, 0.01], np.float32) * amax
+    x = torch.from_numpy(mat).to(torch.bfloat16)
+    for M in (len(rows) + 3, 300):  # workgroup-per-row and wave-per-row kernels
+        xx = torch.cat([x] * (1 + M // x.shape[0]))[:M]
+        xq_ref, s_ref = oracle.quant_per_token(bits(xx))
+        xq, st = q8.q8_quant_per_token(dev(xx))
+        np.testing.assert_array_equal(host(st).numpy(), s_ref)
+        np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+
+
 def test_quant_empty():
     x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
     xq, s = q8.q8_quant_per_token(x)

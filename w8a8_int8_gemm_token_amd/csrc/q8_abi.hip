@@ -6,9 +6,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "decode.hpp"
 #include "gemm_i8.hpp"
 #include "quant.hpp"
+#include "skinny.hpp"
 #include "w8a16.hpp"
 
 namespace {
@@ -52,6 +52,11 @@ inline q8_status check_scale(const float* s) {
 // are enough of them to fill the 256 CUs, 128 x 128 tiles in between.
 template <int EPI>
 hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
+    if constexpr (EPI == EPI_CHANNEL) {
+        const SkinnyArgs k{p.x, p.ldx, p.w, p.ldw, p.s_tok, p.s_w, static_cast<uint16_t*>(p.c), p.ldc,
+                           p.M, p.N, p.K};
+        if (skinny_fits(k)) return launch_skinny(k, s);
+    }
     if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
     const int64_t big_tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
     if (big_tiles >= 256) return launch_gemm_i8<256, 256, 2, 4, EPI, 8>(p, s);
@@ -67,7 +72,9 @@ hipError_t run_quant(const uint16_t* x, int64_t ldx, int8_t* xq, int64_t ldxq, f
                      int K, hipStream_t stream) {
     const dim3 grid((M + 3) / 4), block(256);
     const bool vec = K % 8 == 0 && ldx % 8 == 0 && ldxq % 8 == 0 && al(x, 16) && al(xq, 8);
-    if (vec && K <= 512)
+    if (vec && M <= 256 && K <= 8 * 512 * 2)  // few rows: a workgroup per row
+        hipLaunchKernelGGL((quant_per_token_wg<512, 2>), dim3(M), dim3(512), 0, stream, x, ldx, xq, ldxq, s, K);
+    else if (vec && K <= 512)
         hipLaunchKernelGGL(quant_per_token_reg<1>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
     else if (vec && K <= 2048)
         hipLaunchKernelGGL(quant_per_token_reg<4>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
@@ -154,10 +161,6 @@ q8_status q8_quant_scaled_mm(const q8_bf16* x, int64_t ldx, const int8_t* b, int
     if (r == Q8_OK && M > 0 && !al(xq, 16)) r = Q8_EUNSUPPORTED;
     if (r != Q8_OK || M == 0) return r;
     hipStream_t s = st(stream);
-    if (M <= DECODE_MAX_M && K <= DECODE_MAX_K) {
-        DecodeArgs p{x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok, (int)M, (int)N, (int)K};
-        return hip_status(launch_decode<1>(p, s));
-    }
     hipError_t e = run_quant(x, ldx, xq, K, scale_tok, (int)M, (int)K, s);
     if (e != hipSuccess) return Q8_EHIP;
     GemmArgs p{xq, K, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};

@@ -21,13 +21,58 @@ __device__ __forceinline__ float absmax8(v4u v) {
     return a;
 }
 
-// The 8 codes of the 8 bf16 values in v, packed little-endian in a v2u.
-__device__ __forceinline__ v2u codes8(v4u v, float s) {
+// The 8 codes of the 8 bf16 values in v, packed little-endian, each with a
+// full IEEE division (the reference route).
+__device__ __forceinline__ v2u codes8_div(v4u v, float s) {
     v2u r;
     r[0] = pack_i8x4(code_of(bf16_lo(v[0]), s), code_of(bf16_hi(v[0]), s),
                     code_of(bf16_lo(v[1]), s), code_of(bf16_hi(v[1]), s));
     r[1] = pack_i8x4(code_of(bf16_lo(v[2]), s), code_of(bf16_hi(v[2]), s),
                     code_of(bf16_lo(v[3]), s), code_of(bf16_hi(v[3]), s));
+    return r;
+}
+
+// Per-row constants of the code computation.
+struct RowScale {
+    float s;     // absmax / 127 (correctly rounded)
+    float r;     // fl(1 / s)
+    bool fast;   // s normal and 1/s finite: the reciprocal route applies
+};
+__device__ __forceinline__ RowScale row_scale(float absmax) {
+    RowScale q;
+    q.s = absmax / 127.0f;
+    q.fast = q.s >= 0x1p-125f;
+    q.r = q.fast ? 1.0f / q.s : 0.0f;
+    return q;
+}
+
+// Codes without a division per element, bit-identical to codes8_div.
+// t = fl(x * fl(1/s)) differs from x/s by at most |x/s| * 2^-23 (< 1.6e-5
+// for |x/s| <= 127.00002) and fl(x/s) differs from x/s by at most half an
+// ulp (< 7.7e-6), so unless t lies within 2^-14 of a half-integer, t and
+// fl(x/s) round to the same integer: rint(t), read from the low bits of
+// fl(t + 1.5*2^23) (which is also its int8 code, two's complement).  Such
+// near-ties (about one element in 8000) take the division route.  |t| stays
+// below 127.5 - 2^-14 on the fast route, so no clamp is needed there.
+__device__ __forceinline__ v2u codes8(v4u v, const RowScale& q) {
+    if (!q.fast) return codes8_div(v, q.s);
+    constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
+    constexpr float TIE_LO = 0.5f - 0x1p-14f;
+    u32 b[8];
+    bool near = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
+        const float t = x * q.r;
+        const float m = t + MAGIC;
+        const float d = t - (m - MAGIC);
+        near |= __builtin_fabsf(d) > TIE_LO;
+        b[e] = __float_as_uint(m);
+    }
+    v2u r;
+    r[0] = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | (__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u) << 16);
+    r[1] = __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u) | (__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u) << 16);
+    if (near) r = codes8_div(v, q.s);
     return r;
 }
 
@@ -54,13 +99,49 @@ __global__ __launch_bounds__(256) void quant_per_token_reg(
         }
     }
     a = wave_max(a);
-    const float s = a / 127.0f;
-    if (lane == 0) s_tok[m] = s;
+    const RowScale q = row_scale(a);
+    if (lane == 0) s_tok[m] = q.s;
     v2u* qr = reinterpret_cast<v2u*>(xq + (int64_t)m * ldxq);
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int c = lane + 64 * i;
-        if (c < nch) qr[c] = codes8(v[i], s);
+        if (c < nch) qr[c] = codes8(v[i], q);
+    }
+}
+
+// One workgroup (NT threads) per row, CPT 16-byte chunks per thread held in
+// registers (K <= 8 * NT * CPT): for few rows, where spreading each row over
+// a whole workgroup is what shortens the call.
+template <int NT, int CPT>
+__global__ __launch_bounds__(NT) void quant_per_token_wg(
+    const uint16_t* __restrict__ x, int64_t ldx, int8_t* __restrict__ xq, int64_t ldxq,
+    float* __restrict__ s_tok, int K) {
+    __shared__ float red[NT / 64];
+    const int m = blockIdx.x;
+    const v4u* xr = reinterpret_cast<const v4u*>(x + (int64_t)m * ldx);
+    const int nch = K >> 3;
+    v4u v[CPT];
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = threadIdx.x + NT * i;
+        if (c < nch) {
+            v[i] = xr[c];
+            a = __builtin_fmaxf(a, absmax8(v[i]));
+        }
+    }
+    a = wave_max(a);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) a = __builtin_fmaxf(a, red[w]);
+    const RowScale q = row_scale(a);
+    if (threadIdx.x == 0) s_tok[m] = q.s;
+    v2u* qr = reinterpret_cast<v2u*>(xq + (int64_t)m * ldxq);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = threadIdx.x + NT * i;
+        if (c < nch) qr[c] = codes8(v[i], q);
     }
 }
 
