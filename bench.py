@@ -1,6 +1,7 @@
 """Benchmark of the W8A8 INT8 linear layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--secondary decode,group128,w8a16 | none] [--calibrate-copy]
 
 A step is one pass of the W8A8 hot path over the prefill workload
 (X bf16 [8192, 5120] after the smoothing fold, W int8 [15360, 5120] with
@@ -14,12 +15,17 @@ region.  Prints one JSON line:
   roofline = the GEMM kernel alone, timed with events on the launch stream,
              against the INT8 dense MFMA peak (5.0 POP/s)
   cpu_baseline = the CPU oracle on a bounded sample of the same workload
-  secondary    = decode (M=8) GB/s of the fused kernel with the weight copies
-             rotated past the 256 MB last-level cache, and the other workloads
+  secondary    = decode (M=1, M=8) GB/s of the one-call layer with the weight
+             copies rotated past the 256 MB last-level cache, and the other
+             workloads
+--calibrate-copy adds a plain device-to-device copy of 512 MiB (torch's copy
+kernel), so that a hardware-counter run of this script also measures the
+bytes the counters report for a transfer of known size.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -38,6 +44,34 @@ METRIC = "W8A8 quant+GEMM TOPS at M=8192,K=5120,N=15360; % INT8 MFMA peak; M=8 G
 PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, published
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+
+
+# HBM bytes of the prefill GEMM from hardware counters (rocprofv3 --pmc
+# FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, mean of 7 dispatches of
+# gemm_i8_kernel<256,256,2,4,1,8>), scaled by what the same counters read for
+# a plain 512 MiB device copy.  Valid only for the kernel sources they were
+# taken on: if those files change, the figure is withdrawn (null).
+GEMM_COUNTERS = {
+    "sources_sha256": {
+        "gemm_i8.hpp": "52994d518b3e71349e0e5c5742ca286e0596ea322373ad6667247a10933e6edb",
+        "q8_device.hpp": "d4f2127e64227715d4ae11d84ffb5c1eb2a7e41146be4eadd6ffe7108b6cdd45",
+    },
+    "fetch_kib": 491354.4, "write_kib": 253377.1,
+    "copy_kib": 524288.0, "copy_fetch_kib": 262158.7, "copy_write_kib": 524288.0,
+}
+
+
+def gemm_traffic():
+    """(read bytes, write bytes) per GEMM launch, or None if stale."""
+    csrc = os.path.join(ROOT, "w8a8_int8_gemm_token_amd", "csrc")
+    for name, digest in GEMM_COUNTERS["sources_sha256"].items():
+        with open(os.path.join(csrc, name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    c = GEMM_COUNTERS
+    rd = c["fetch_kib"] * 1024 * c["copy_kib"] / c["copy_fetch_kib"]
+    wr = c["write_kib"] * 1024 * c["copy_kib"] / c["copy_write_kib"]
+    return rd, wr
 
 
 def log(*a):
@@ -70,7 +104,7 @@ def prefill_setup(dev):
     return wl, xo, wq, sc
 
 
-def cpu_baseline(target_s: float = 12.0):
+def cpu_baseline(target_s: float = 15.0):
     """The oracle (as it stands) on a bounded sample of the prefill workload:
     quantize a block of token rows and run the scaled INT8 GEMM for them
     against all 15360 channels.  Scaled to TOPS like the GPU figure."""
@@ -89,12 +123,15 @@ def cpu_baseline(target_s: float = 12.0):
         oracle.scaled_mm(xq, wq, st, sc)
         return time.perf_counter() - t0
 
-    rows = 4
+    rows = 16
     t = run(rows)
-    rows = int(max(4, min(wl.M, rows * target_s / max(t, 1e-3))))
+    while t < 1.0 and rows < wl.M:  # grow until the per-row cost is steady
+        rows = min(wl.M, rows * 4)
+        t = run(rows)
+    rows = int(max(16, min(wl.M, rows * target_s / t)))
     t = run(rows)
     ops = 2.0 * rows * wl.N * wl.K
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    threads = oracle.threads()
     return {"value": ops / t / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {wl.M} token rows x all {wl.N} channels, K={wl.K} "
                       f"(quant + INT32 GEMM + epilogue), {t:.1f} s"}
@@ -169,6 +206,19 @@ def w8a16_tflops(dev, iters=10):
     return {"us": ms * 1e3, "TFLOPS": t, "frac_bf16_peak": t / PEAK_BF16_TFLOPS}
 
 
+def copy_calibration(dev, nbytes=512 << 20, reps=3):
+    """A plain copy of known size, for scaling the HBM byte counters."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    ms = events_time(lambda: b.copy_(a), reps)
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "us": ms * 1e3,
+            "GB/s": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
+SECONDARY = {"decode": lambda dev: decode_gbs(dev), "group128": lambda dev: group_tops(dev),
+             "w8a16": lambda dev: w8a16_tflops(dev)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,6 +226,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary", default="decode,group128,w8a16",
+                    help="comma list of secondary workloads, or 'none'")
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -216,19 +269,26 @@ def main():
     quant_ms = events_time(quant, args.steps)
     achieved = ops / (gemm_ms * 1e-3) / 1e12
     quant_bytes = M * K * 2 + M * K + 4 * M
+    traffic = gemm_traffic()
+    algo_bytes = M * K + N * K + 4 * M + 4 * N + 2 * M * N
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_INT8_TOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_INT8_TOPS,
+                "traffic": None if traffic is None else sum(traffic),
+                "traffic_read_write": traffic, "algorithmic_bytes": algo_bytes,
                 "kernel": "gemm_i8_kernel (per-channel epilogue)",
                 "kernel_us": gemm_ms * 1e3}
     secondary = {"quant_kernel": {"us": quant_ms * 1e3,
                                   "GB/s": quant_bytes / (quant_ms * 1e-3) / 1e9}}
-    if not args.no_secondary:
-        log("secondary: decode")
-        secondary["decode"] = decode_gbs(dev)
-        log("secondary: group128")
-        secondary["group128"] = group_tops(dev)
-        log("secondary: w8a16")
-        secondary["w8a16"] = w8a16_tflops(dev)
+    names = [] if args.no_secondary or args.secondary == "none" else args.secondary.split(",")
+    for name in names:
+        if name not in SECONDARY:
+            print(f"unknown secondary workload {name!r}", file=sys.stderr)
+            sys.exit(2)
+        log(f"secondary: {name}")
+        secondary[name] = SECONDARY[name](dev)
+    if args.calibrate_copy:
+        log("copy calibration")
+        secondary["copy_calibration"] = copy_calibration(dev)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

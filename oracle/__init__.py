@@ -51,6 +51,7 @@ def _load():
         F = ctypes.c_float
         sig = {
             "q8o_env_ok": ([], ctypes.c_int),
+            "q8o_threads": ([], ctypes.c_int),
             "q8o_f32_to_bf16": ([F], ctypes.c_uint16),
             "q8o_bf16_to_f32": ([ctypes.c_uint16], F),
             "q8o_quant_per_token": ([P, I, I, P, P], None),
@@ -83,6 +84,11 @@ def _c(a: np.ndarray, dtype) -> np.ndarray:
 
 def _p(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def threads() -> int:
+    """Threads the oracle's parallel loops run on."""
+    return int(_load().q8o_threads())
 
 
 def f32_to_bf16(v: float) -> int:

@@ -51,6 +51,7 @@
  */
 #include <fenv.h>
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -82,6 +83,9 @@ float q8o_bf16_to_f32(uint16_t b) { return bf16_bits_to_f32(b); }
 
 /* 1 if the FPU is in round-to-nearest-even mode (every routine relies on it). */
 int q8o_env_ok(void) { return fegetround() == FE_TONEAREST; }
+
+/* Threads the parallel loops below run on. */
+int q8o_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------- symmetric INT8 codes -- */
 
