@@ -272,6 +272,48 @@ def test_quant_scaled_mm_token_counts(M):
     assert_ulp1(bits(host(y3)), y_ref, f"M={M} scaled_mm")
 
 
+@pytest.mark.parametrize("M,N,K,pad", [
+    (1, 16, 1024, 0),      # 4 channels per workgroup, 4 workgroups
+    (8, 1040, 3072, 16),   # 8 per workgroup, strided operands
+    (3, 4112, 2048, 0),    # 20 per workgroup, last one ragged (12 channels)
+    (8, 5120, 5120, 0),    # the decode workload's shape
+    (5, 8192, 2048, 32),   # 32 per workgroup: two weight rows per wave
+    (7, 2048, 8192, 0),    # the largest K of the one-kernel path
+    (8, 5120, 8192, 0),    # tile does not fit in LDS: two-kernel path
+    (9, 1024, 2048, 0),    # more tokens than the one-kernel path takes
+])
+def test_decode_one_call_shapes(M, N, K, pad):
+    """The one-call layer at decode batch sizes (one kernel for M <= 8 when
+    the channel tile fits in LDS, else quantizer + weight-streaming GEMM):
+    codes, scales and outputs against the oracle, with zero and near-tie
+    rows and strided x, w and y."""
+    say("decode one-call", M, N, K, pad)
+    xf, wf = synth.custom(M, K + pad, N, seed=N + K + M, outlier_cols=K // 100)
+    x = xf[:, :K].contiguous()
+    x[M // 2] = 0
+    if M > 2:  # a row whose codes come from the division fallback
+        x[M - 1, :4] = torch.tensor([1.0, 0.5, -0.5, 0.75])  # 0.5/fl(1/127) ~ 63.5
+        x[M - 1, 4:] = 0
+    xf[:, :K] = x
+    w = wf[:, :K].contiguous()
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y_ref = oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref)
+    wq_full = torch.zeros((N, K + pad), dtype=torch.int8, device=DEV)
+    wq_full[:, :K] = dev(torch.from_numpy(wq_ref))
+    wq = wq_full[:, :K]
+    sc = dev(torch.from_numpy(sc_ref))
+    yfull = torch.full((M, N + pad), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    y = yfull[:, :N]
+    xd = dev(xf)[:, :K]
+    y, xq, st = q8.q8_quant_scaled_mm(xd, wq, sc, out=y)
+    np.testing.assert_array_equal(host(st).numpy(), st_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    assert_ulp1(bits(host(y)), y_ref, f"decode M={M} N={N} K={K}")
+    if pad:  # the padding columns of y are untouched
+        assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
+
+
 def test_scaled_mm_ragged_and_zero_rows():
     M, N, K = 131, 208, 384
     x, w = synth.custom(M, K, N, seed=5, outlier_cols=4)

@@ -9,6 +9,7 @@
 #include "gemm_i8.hpp"
 #include "quant.hpp"
 #include "skinny.hpp"
+#include "decode_fused.hpp"
 #include "w8a16.hpp"
 
 namespace {
@@ -161,6 +162,11 @@ q8_status q8_quant_scaled_mm(const q8_bf16* x, int64_t ldx, const int8_t* b, int
     if (r == Q8_OK && M > 0 && !al(xq, 16)) r = Q8_EUNSUPPORTED;
     if (r != Q8_OK || M == 0) return r;
     hipStream_t s = st(stream);
+    if (decode_fits((int)M, (int)N, (int)K, ldb)) {
+        const DecodeArgs d{x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok,
+                           (int)M, (int)N, (int)K, decode_rows((int)N)};
+        return hip_status(launch_decode(d, s));
+    }
     hipError_t e = run_quant(x, ldx, xq, K, scale_tok, (int)M, (int)K, s);
     if (e != hipSuccess) return Q8_EHIP;
     GemmArgs p{xq, K, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};

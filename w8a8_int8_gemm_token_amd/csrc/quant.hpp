@@ -12,13 +12,19 @@
 
 namespace q8 {
 
-// Max |x| over the 8 bf16 values packed in a v4u (exact).
-__device__ __forceinline__ float absmax8(v4u v) {
-    float a = __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[0])), __builtin_fabsf(bf16_hi(v[0])));
-    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[1])), __builtin_fabsf(bf16_hi(v[1]))));
-    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[2])), __builtin_fabsf(bf16_hi(v[2]))));
-    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[3])), __builtin_fabsf(bf16_hi(v[3]))));
-    return a;
+// Running max of |x| over bf16 values, kept as two 16-bit magnitudes: for
+// finite bf16 the magnitude bits (sign cleared) order the same way as |x|,
+// so a packed unsigned max gives the exact absmax at one VALU op per value.
+typedef unsigned short v2h __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v2h mag_max8(v2h acc, v4u v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        acc = __builtin_elementwise_max(acc, __builtin_bit_cast(v2h, v[e] & 0x7FFF7FFFu));
+    return acc;
+}
+__device__ __forceinline__ float mag_to_f32(v2h acc) {
+    const u32 m = acc[0] > acc[1] ? acc[0] : acc[1];
+    return __uint_as_float(m << 16);
 }
 
 // The 8 codes of the 8 bf16 values in v, packed little-endian, each with a
@@ -47,32 +53,33 @@ __device__ __forceinline__ RowScale row_scale(float absmax) {
 }
 
 // Codes without a division per element, bit-identical to codes8_div.
-// t = fl(x * fl(1/s)) differs from x/s by at most |x/s| * 2^-23 (< 1.6e-5
-// for |x/s| <= 127.00002) and fl(x/s) differs from x/s by at most half an
-// ulp (< 7.7e-6), so unless t lies within 2^-14 of a half-integer, t and
-// fl(x/s) round to the same integer: rint(t), read from the low bits of
-// fl(t + 1.5*2^23) (which is also its int8 code, two's complement).  Such
-// near-ties (about one element in 8000) take the division route.  |t| stays
-// below 127.5 - 2^-14 on the fast route, so no clamp is needed there.
+// With r = fl(1/s): m = fl(x*r + 1.5*2^23) (one fused rounding) holds
+// n = rint(x*r) in its low bits (ulp 1 in [2^23, 2^24); its low byte is the
+// int8 code, two's complement), and d = fl(x*r - n) (fused again) is the
+// distance of the exact product from that integer.  x*r differs from x/s by
+// at most |x/s| * 2^-23 (< 1.6e-5 for |x/s| <= 127.00002) and fl(x/s) from
+// x/s by at most half an ulp (< 7.7e-6), so when |d| <= 0.5 - 2^-14 the
+// correctly rounded quotient fl(x/s) rounds to the same n.  Otherwise (a
+// near-tie, about one element in 8000) the eight codes take the division
+// route.  |x*r| < 127.5 on the fast route, so no clamp is needed there.
 __device__ __forceinline__ v2u codes8(v4u v, const RowScale& q) {
     if (!q.fast) return codes8_div(v, q.s);
     constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
     constexpr float TIE_LO = 0.5f - 0x1p-14f;
     u32 b[8];
-    bool near = false;
+    float dmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
-        const float t = x * q.r;
-        const float m = t + MAGIC;
-        const float d = t - (m - MAGIC);
-        near |= __builtin_fabsf(d) > TIE_LO;
+        const float m = __builtin_fmaf(x, q.r, MAGIC);
+        const float d = __builtin_fmaf(x, q.r, MAGIC - m);  // MAGIC - m = -n exactly
+        dmax = __builtin_fmaxf(dmax, __builtin_fabsf(d));
         b[e] = __float_as_uint(m);
     }
     v2u r;
     r[0] = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | (__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u) << 16);
     r[1] = __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u) | (__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u) << 16);
-    if (near) r = codes8_div(v, q.s);
+    if (dmax > TIE_LO) r = codes8_div(v, q.s);
     return r;
 }
 
@@ -89,16 +96,16 @@ __global__ __launch_bounds__(256) void quant_per_token_reg(
     const v4u* xr = reinterpret_cast<const v4u*>(x + (int64_t)m * ldx);
     const int nch = K >> 3;
     v4u v[NC];
-    float a = 0.0f;
+    v2h mx = v2h{0, 0};
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int c = lane + 64 * i;
         if (c < nch) {
             v[i] = xr[c];
-            a = __builtin_fmaxf(a, absmax8(v[i]));
+            mx = mag_max8(mx, v[i]);
         }
     }
-    a = wave_max(a);
+    const float a = wave_max(mag_to_f32(mx));
     const RowScale q = row_scale(a);
     if (lane == 0) s_tok[m] = q.s;
     v2u* qr = reinterpret_cast<v2u*>(xq + (int64_t)m * ldxq);
@@ -121,16 +128,16 @@ __global__ __launch_bounds__(NT) void quant_per_token_wg(
     const v4u* xr = reinterpret_cast<const v4u*>(x + (int64_t)m * ldx);
     const int nch = K >> 3;
     v4u v[CPT];
-    float a = 0.0f;
+    v2h mx = v2h{0, 0};
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
         const int c = threadIdx.x + NT * i;
         if (c < nch) {
             v[i] = xr[c];
-            a = __builtin_fmaxf(a, absmax8(v[i]));
+            mx = mag_max8(mx, v[i]);
         }
     }
-    a = wave_max(a);
+    float a = wave_max(mag_to_f32(mx));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
     __syncthreads();
 #pragma unroll
