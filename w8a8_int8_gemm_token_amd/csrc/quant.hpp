@@ -53,33 +53,40 @@ __device__ __forceinline__ RowScale row_scale(float absmax) {
 }
 
 // Codes without a division per element, bit-identical to codes8_div.
-// With r = fl(1/s): m = fl(x*r + 1.5*2^23) (one fused rounding) holds
-// n = rint(x*r) in its low bits (ulp 1 in [2^23, 2^24); its low byte is the
-// int8 code, two's complement), and d = fl(x*r - n) (fused again) is the
-// distance of the exact product from that integer.  x*r differs from x/s by
-// at most |x/s| * 2^-23 (< 1.6e-5 for |x/s| <= 127.00002) and fl(x/s) from
-// x/s by at most half an ulp (< 7.7e-6), so when |d| <= 0.5 - 2^-14 the
-// correctly rounded quotient fl(x/s) rounds to the same n.  Otherwise (a
-// near-tie, about one element in 8000) the eight codes take the division
-// route.  |x*r| < 127.5 on the fast route, so no clamp is needed there.
+// With r = fl(1/s) = (1/s)(1 + e), |e| <= 2^-24: m = fl(x*r + 1.5*2^23) (one
+// fused rounding) holds n = rint(x*r) in its low bits (ulp 1 in [2^23, 2^24);
+// its low byte is the int8 code, two's complement), and d = fl(x*r - n)
+// (fused again) is the distance of the exact product from that integer.
+// x*r differs from x/s by |x/s| * |e| <= 127.0000076 * 2^-24 < 7.6e-6, fl(x/s)
+// from x/s by at most half an ulp (< 3.9e-6 below 128), and d from x*r - n
+// by at most 2^-25.  So when |d| <= 0.5 - 2^-16 the correctly rounded
+// quotient fl(x/s) lies strictly within 0.5 of n and rounds to n.  Any other
+// element (a near-tie, about one in 30000) is recomputed by division on its
+// own.  |x*r| < 127.5 on the fast route, so no clamp is needed there.
 __device__ __forceinline__ v2u codes8(v4u v, const RowScale& q) {
     if (!q.fast) return codes8_div(v, q.s);
     constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
-    constexpr float TIE_LO = 0.5f - 0x1p-14f;
+    constexpr float TIE_LO = 0.5f - 0x1p-16f;
     u32 b[8];
-    float dmax = 0.0f;
+    float d[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
         const float m = __builtin_fmaf(x, q.r, MAGIC);
-        const float d = __builtin_fmaf(x, q.r, MAGIC - m);  // MAGIC - m = -n exactly
-        dmax = __builtin_fmaxf(dmax, __builtin_fabsf(d));
+        d[e] = __builtin_fmaf(x, q.r, MAGIC - m);  // MAGIC - m = -n exactly
         b[e] = __float_as_uint(m);
     }
     v2u r;
     r[0] = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | (__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u) << 16);
     r[1] = __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u) | (__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u) << 16);
-    if (dmax > TIE_LO) r = codes8_div(v, q.s);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (__builtin_fabsf(d[e]) > TIE_LO) {
+            const float x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
+            const u32 sh = 8 * (e & 3);
+            r[e >> 2] = (r[e >> 2] & ~(0xFFu << sh)) | ((u32)(code_of(x, q.s) & 0xFF) << sh);
+        }
+    }
     return r;
 }
 
