@@ -64,6 +64,7 @@ def _load():
             "q8o_smooth_scales": ([P, I, I, F, P], ctypes.c_int),
             "q8o_smooth_fold_x": ([P, P, I, I, P], None),
             "q8o_smooth_fold_w": ([P, P, I, I, P], None),
+            "q8o_rmsnorm_quant": ([P, P, P, F, I, I, P, P, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -101,7 +102,7 @@ def bf16_to_f32(bits: int) -> float:
 
 
 def quant_per_token(x_bf16: np.ndarray):
-    """a1-a3.  x_bf16: uint16 [M,K] (bf16 bits) -> (xq int8 [M,K], s fp32 [M])."""
+    """Per-token quant.  x_bf16: uint16 [M,K] (bf16 bits) -> (xq int8 [M,K], s fp32 [M])."""
     x = _c(x_bf16, np.uint16)
     M, K = x.shape
     xq = np.empty((M, K), np.int8)
@@ -111,7 +112,7 @@ def quant_per_token(x_bf16: np.ndarray):
 
 
 def quant_weight(w_f32: np.ndarray, group: int | None = None):
-    """a0.  w: fp32 [N,K] -> (wq int8 [N,K], s fp32 [N] or [N,K/group])."""
+    """Weight quant.  w: fp32 [N,K] -> (wq int8 [N,K], s fp32 [N] or [N,K/group])."""
     w = _c(w_f32, np.float32)
     N, K = w.shape
     g = K if group is None else group
@@ -123,7 +124,7 @@ def quant_weight(w_f32: np.ndarray, group: int | None = None):
 
 
 def mm_i32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
-    """a4.  a int8 [M,K], b int8 [N,K] -> exact int32 [M,N]."""
+    """INT8 GEMM.  a int8 [M,K], b int8 [N,K] -> exact int32 [M,N]."""
     a = _c(a, np.int8)
     b = _c(b, np.int8)
     M, K = a.shape
@@ -136,7 +137,7 @@ def mm_i32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
 
 
 def epilogue_channel(acc: np.ndarray, s_tok: np.ndarray, s_ch: np.ndarray):
-    """a5.  int32 [M,N] -> bf16 bits uint16 [M,N]."""
+    """Per-channel epilogue.  int32 [M,N] -> bf16 bits uint16 [M,N]."""
     acc = _c(acc, np.int32)
     s_tok = _c(s_tok, np.float32)
     s_ch = _c(s_ch, np.float32)
@@ -147,7 +148,7 @@ def epilogue_channel(acc: np.ndarray, s_tok: np.ndarray, s_ch: np.ndarray):
 
 
 def scaled_mm(a, b, s_tok, s_ch) -> np.ndarray:
-    """a4+a5.  -> bf16 bits uint16 [M,N]."""
+    """GEMM + per-channel epilogue.  -> bf16 bits uint16 [M,N]."""
     a = _c(a, np.int8)
     b = _c(b, np.int8)
     s_tok = _c(s_tok, np.float32)
@@ -162,7 +163,7 @@ def scaled_mm(a, b, s_tok, s_ch) -> np.ndarray:
 
 
 def scaled_mm_group128(a, b, s_tok, s_grp) -> np.ndarray:
-    """a4+a5g.  s_grp fp32 [N, K/128] -> bf16 bits uint16 [M,N]."""
+    """GEMM with group-128 weights.  s_grp fp32 [N, K/128] -> bf16 bits uint16 [M,N]."""
     a = _c(a, np.int8)
     b = _c(b, np.int8)
     s_tok = _c(s_tok, np.float32)
@@ -178,7 +179,7 @@ def scaled_mm_group128(a, b, s_tok, s_grp) -> np.ndarray:
 
 
 def w8a16_ref(x_bf16, wq, s_ch, with_mag: bool = False):
-    """a6 reference.  -> fp64 y_ref [M,N] (and fp64 magnitude sums)."""
+    """W8A16 reference.  -> fp64 y_ref [M,N] (and fp64 magnitude sums)."""
     x = _c(x_bf16, np.uint16)
     wq = _c(wq, np.int8)
     s_ch = _c(s_ch, np.float32)
@@ -217,3 +218,23 @@ def smooth_fold_w(w_f32, s) -> np.ndarray:
     out = np.empty((N, K), np.float32)
     _load().q8o_smooth_fold_w(_p(w), _p(s), N, K, _p(out))
     return out
+
+
+def rmsnorm_quant(x_bf16, gamma_bf16, eps: float, res_bf16=None):
+    """Residual add (optional) + RMSNorm + per-token INT8 quant.
+    Returns (xq int8 [M,K], scale fp32 [M], y bf16 bits [M,K], res_out bf16
+    bits [M,K] or None)."""
+    x = _c(x_bf16, np.uint16)
+    g = _c(gamma_bf16, np.uint16)
+    M, K = x.shape
+    if g.shape != (K,):
+        raise ValueError("gamma must have K entries")
+    res = None if res_bf16 is None else np.array(res_bf16, dtype=np.uint16, copy=True, order="C")
+    xq = np.empty((M, K), np.int8)
+    s = np.empty((M,), np.float32)
+    y = np.empty((M, K), np.uint16)
+    rc = _load().q8o_rmsnorm_quant(_p(x), None if res is None else _p(res), _p(g), float(eps),
+                                   M, K, _p(xq), _p(s), _p(y))
+    if rc != 0:
+        raise ValueError(f"oracle rmsnorm_quant failed ({rc}): K must be a multiple of 8")
+    return xq, s, y, res

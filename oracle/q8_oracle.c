@@ -116,7 +116,7 @@ static int8_t code_of(float x, float s)
     return (int8_t)r;
 }
 
-/* a1-a3: per-token dynamic quantization of a bf16 activation matrix.
+/* Per-token dynamic quantization of a bf16 activation matrix.
  * x: [M][K] bf16 bits, row-major.  xq: [M][K] int8.  s_tok: [M] fp32.
  * [P1 "Recipe": INT8 per-token dynamic activations; P4 "Quantization"] */
 void q8o_quant_per_token(const uint16_t *x, int64_t M, int64_t K,
@@ -135,7 +135,7 @@ void q8o_quant_per_token(const uint16_t *x, int64_t M, int64_t K,
     }
 }
 
-/* a0: offline symmetric weight quantization of an fp32 weight W [N][K].
+/* Offline symmetric weight quantization of an fp32 weight W [N][K].
  * group == K: one scale per output channel (s: [N]).
  * group == 128: one scale per (channel, contiguous 128-wide K block),
  * s: [N][K/128] row-major.
@@ -163,7 +163,7 @@ int q8o_quant_weight(const float *w, int64_t N, int64_t K, int64_t group,
 
 /* ---------------------------------------------------------- INT8 GEMM -- */
 
-/* a4: acc[m][n] = sum_k a[m][k] * b[n][k], exact (int64 loop).
+/* INT8 GEMM: acc[m][n] = sum_k a[m][k] * b[n][k], exact (int64 loop).
  * a: [M][K] int8, b: [N][K] int8 (PyTorch Linear layout), acc: [M][N] int32.
  * [P1 "Serving": INT8 x INT8 on tensor cores; P5: true int8 x int8 compute]
  * Returns 0, or -1 if some sum does not fit in int32 (then acc is clamped). */
@@ -191,7 +191,7 @@ int q8o_mm_i32(const int8_t *a, const int8_t *b, int64_t M, int64_t N,
     return bad ? -1 : 0;
 }
 
-/* a5: y[m][n] = bf16_rne( fl32( fl32((float)acc * s_tok[m]) * s_ch[n] ) ).
+/* Per-channel epilogue: y[m][n] = bf16_rne( fl32( fl32((float)acc * s_tok[m]) * s_ch[n] ) ).
  * [P1 "Recipe": per-token x per-channel scales; "Serving": bf16 dtype] */
 void q8o_epilogue_channel(const int32_t *acc, const float *s_tok,
                           const float *s_ch, int64_t M, int64_t N,
@@ -208,7 +208,8 @@ void q8o_epilogue_channel(const int32_t *acc, const float *s_tok,
     }
 }
 
-/* a4+a5 in one call, without storing the int32 matrix. */
+/* GEMM and per-channel epilogue in one call, without storing the int32
+ * matrix. */
 int q8o_scaled_mm(const int8_t *a, const int8_t *b, const float *s_tok,
                   const float *s_ch, int64_t M, int64_t N, int64_t K,
                   uint16_t *y)
@@ -231,7 +232,7 @@ int q8o_scaled_mm(const int8_t *a, const int8_t *b, const float *s_tok,
     return bad ? -1 : 0;
 }
 
-/* a4+a5g: group-128 weights.  For g = 0 .. K/128-1 in order:
+/* GEMM with group-128 weights.  For g = 0 .. K/128-1 in order:
  *   p_g = sum_{k in [128g, 128g+128)} a[m][k]*b[n][k]   (int32, exact;
  *         |p_g| <= 128*128*128 < 2^24 so (float)p_g is exact)
  *   acc = fmaf((float)p_g, s_grp[n][g], acc)           (acc starts at 0)
@@ -262,7 +263,7 @@ int q8o_scaled_mm_group128(const int8_t *a, const int8_t *b,
     return 0;
 }
 
-/* a6 reference: W8A16.  y_ref[m][n] = s_ch[n] * sum_k x[m][k] * q[n][k] in
+/* W8A16 reference.  y_ref[m][n] = s_ch[n] * sum_k x[m][k] * q[n][k] in
  * fp64 (each product is exact in fp64), plus the magnitude sum
  * mag[m][n] = s_ch[n] * sum_k |x[m][k]| * |q[n][k]| that sizes the
  * floating-point error bound of any summation order.
@@ -289,7 +290,7 @@ void q8o_w8a16_ref(const uint16_t *x, const int8_t *q, const float *s_ch,
     }
 }
 
-/* ------------------------------------------------ smoothing fold (a0) -- */
+/* ------------------------------------------------------ smoothing fold -- */
 
 /* s_j = min(cap, sqrtf(max_m |x[m][j]|)), j < K.  [P1 "Recipe": SmoothQuant
  * folds, scales capped at 16; the plain column maximum with exponent 0.5
@@ -336,4 +337,74 @@ void q8o_smooth_fold_w(const float *w, const float *s, int64_t N, int64_t K,
     for (int64_t n = 0; n < N; ++n)
         for (int64_t j = 0; j < K; ++j)
             wo[n * K + j] = w[n * K + j] * s[j];
+}
+
+/* ------------------------------- residual add + RMSNorm + per-token quant --
+ * The step before a W8A8 linear layer in the model: the normalization whose
+ * weight absorbs the smoothing divisor, fused with the per-token INT8 quant
+ * of its output [P1 "Recipe": smoothing folded into the preceding norm; P3
+ * "Recipe": the same fold; P5 "Serving (vLLM, gfx908 fork)": residual add,
+ * RMSNorm and INT8 quantization fused into one output step].
+ * Readings (the pages give no RMSNorm numerics):
+ *  - with a residual stream: h = bf16_rne(fl32(x) + fl32(res)), and res := h;
+ *    without one: h = x;
+ *  - ss = sum of h^2 in fp32 in this order: 64 partial sums, partial l
+ *    adding h[k]^2 for the 8-element chunks c = l, l + 64, l + 128, ... in
+ *    ascending k; then for o = 32, 16, 8, 4, 2, 1 every partial l becomes
+ *    p[l] + p[l ^ o]; ss = p[0].  (Any order is a valid RMSNorm; fixing one
+ *    makes the codes checkable bit for bit.)  K must be a multiple of 8;
+ *  - rstd = 1 / sqrtf(ss / K + eps) (correctly rounded division and root);
+ *  - y[k] = bf16_rne(fl32(fl32(h[k] * rstd) * gamma[k]));
+ *  - then the per-token quantization above, applied to the bf16 row y.
+ * y_out (optional) receives y.  Returns -1 if K is not a multiple of 8. */
+int q8o_rmsnorm_quant(const uint16_t *x, uint16_t *res, const uint16_t *gamma,
+                      float eps, int64_t M, int64_t K, int8_t *xq, float *s,
+                      uint16_t *y_out)
+{
+    if (K % 8 != 0) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; ++m) {
+        uint16_t *h = (uint16_t *)malloc((size_t)K * sizeof(uint16_t));
+        uint16_t *y = (uint16_t *)malloc((size_t)K * sizeof(uint16_t));
+        float *yf = (float *)malloc((size_t)K * sizeof(float));
+        if (!h || !y || !yf) { bad = 1; free(h); free(y); free(yf); continue; }
+        for (int64_t k = 0; k < K; ++k) {
+            if (res) {
+                const float sum = bf16_bits_to_f32(x[m * K + k]) + bf16_bits_to_f32(res[m * K + k]);
+                h[k] = q8o_f32_to_bf16(sum);
+                res[m * K + k] = h[k];
+            } else {
+                h[k] = x[m * K + k];
+            }
+        }
+        float p[64];
+        for (int l = 0; l < 64; ++l) {
+            p[l] = 0.0f;
+            for (int64_t c = l; c < K / 8; c += 64)
+                for (int e = 0; e < 8; ++e) {
+                    const float v = bf16_bits_to_f32(h[c * 8 + e]);
+                    const float sq = v * v;
+                    p[l] = p[l] + sq;
+                }
+        }
+        for (int o = 32; o >= 1; o >>= 1) {
+            float q[64];
+            for (int l = 0; l < 64; ++l) q[l] = p[l] + p[l ^ o];
+            memcpy(p, q, sizeof(p));
+        }
+        const float var = p[0] / (float)K;
+        const float rstd = 1.0f / sqrtf(var + eps);
+        for (int64_t k = 0; k < K; ++k) {
+            const float t = bf16_bits_to_f32(h[k]) * rstd;
+            y[k] = q8o_f32_to_bf16(t * bf16_bits_to_f32(gamma[k]));
+            yf[k] = bf16_bits_to_f32(y[k]);
+        }
+        const float sc = absmax_scale(yf, K);
+        s[m] = sc;
+        for (int64_t k = 0; k < K; ++k) xq[m * K + k] = code_of(yf[k], sc);
+        if (y_out) memcpy(y_out + m * K, y, (size_t)K * sizeof(uint16_t));
+        free(h); free(y); free(yf);
+    }
+    return bad ? -2 : 0;
 }

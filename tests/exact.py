@@ -70,3 +70,36 @@ def bf16_bits_of(v: Fraction) -> int:
     u = struct.unpack("<I", struct.pack("<f", f))[0]
     assert u & 0xFFFF == 0, "value not representable in bf16"
     return u >> 16
+
+
+def _fp32_neighbors(v: Fraction):
+    """The fp32 values just below and above a positive fp32 value v."""
+    f = float(v)
+    u = struct.unpack("<I", struct.pack("<f", f))[0]
+    lo = Fraction(struct.unpack("<f", struct.pack("<I", u - 1))[0])
+    hi = Fraction(struct.unpack("<f", struct.pack("<I", u + 1))[0])
+    return lo, hi
+
+
+def sqrt_fp32(r: Fraction) -> Fraction:
+    """Correctly rounded fp32 square root of a positive rational: the fp32
+    value nearest to sqrt(r) (ties to even), decided by exact comparisons of
+    squares against r (no floating-point square root is trusted)."""
+    assert r > 0
+    c = fp32(Fraction(math.sqrt(float(r))))  # estimate, then correct exactly
+    while c * c > r:
+        c = _fp32_neighbors(c)[0]
+    while True:
+        d = _fp32_neighbors(c)[1]
+        if d * d <= r:
+            c = d
+        else:
+            break
+    # now c <= sqrt(r) < d: round by the midpoint
+    m = (c + d) / 2
+    if r < m * m:
+        return c
+    if r > m * m:
+        return d
+    even = (struct.unpack("<I", struct.pack("<f", float(c)))[0] & 1) == 0
+    return c if even else d

@@ -429,3 +429,160 @@ def test_end_to_end_within_quantization_bound(name):
     assert np.all(np.abs(y - exact) <= bound)
     # and a wrong sign / transposed operand would be far outside it
     assert not np.all(np.abs(-y - exact) <= bound)
+
+
+# ------------------------------- residual add + RMSNorm + per-token quant --
+# Fused normalization before the linear layer: "Qwen3.8-27B -- SmoothQuant +
+# activation-aware GPTQ, W8A8 INT8 (v3)", "Recipe" (smoothing folded into the
+# preceding norm); "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", "Serving (vLLM, gfx908
+# fork)" (residual add, RMSNorm and INT8 quantization fused).
+
+def _norm_inputs(M, K, seed, scale=1.0):
+    g = np.random.default_rng(seed)
+    x = synth.bf16_bits(torch.from_numpy((g.standard_normal((M, K)) * scale).astype(np.float32)).to(torch.bfloat16))
+    gam = synth.bf16_bits(torch.from_numpy((0.5 + g.random(K)).astype(np.float32)).to(torch.bfloat16))
+    return x, gam
+
+
+def test_rmsnorm_power_of_two_scale_invariance():
+    """With eps = 0, RMSNorm of 2^j * x equals RMSNorm of x bit for bit
+    (squares, the sum, the mean and the root all scale exactly)."""
+    x, gam = _norm_inputs(6, 768, 1)
+    ref = oracle.rmsnorm_quant(x, gam, 0.0)
+    for j in (-3, 2, 5):
+        xs = synth.bf16_bits(torch.from_numpy(_f32(x) * np.float32(2.0 ** j)).to(torch.bfloat16))
+        assert np.array_equal(_f32(xs), _f32(x) * np.float32(2.0 ** j))  # exact scaling
+        got = oracle.rmsnorm_quant(xs, gam, 0.0)
+        for a, b in zip(ref[:3], got[:3]):
+            np.testing.assert_array_equal(a, b)
+
+
+def test_rmsnorm_constant_row_closed_form():
+    """Row of ones, eps = 3: mean square 1, rstd = 1/sqrt(4) = 0.5 exactly,
+    so y = gamma / 2 exactly (pins the division by K and the + eps)."""
+    K = 512
+    x = _bits([[1.0] * K, [-1.0] * K])
+    _, gam = _norm_inputs(1, K, 2)
+    xq, s, y, _ = oracle.rmsnorm_quant(x, gam, 3.0)
+    np.testing.assert_array_equal(_f32(y[0]), _f32(gam) / 2)
+    np.testing.assert_array_equal(_f32(y[1]), -_f32(gam) / 2)
+    np.testing.assert_array_equal(s, np.float32(np.abs(_f32(gam)).max() / 2) / np.float32(127))
+
+
+@pytest.mark.parametrize("k", [0, 5, 8, 63 * 8 + 7, 64 * 8, 64 * 8 + 3, 100 * 8 + 6, 1023])
+def test_rmsnorm_single_element_rows_cover_every_position(k):
+    """One nonzero v = -4 at position k of a K = 1024 row, eps = 0: mean
+    square 16/1024, rstd = 1/sqrt(1/64) = 8, so y[k] = -32 * gamma[k]
+    exactly and zero elsewhere.  A dropped or doubled element in the sum of
+    squares changes y[k]."""
+    K = 1024
+    row = [0.0] * K
+    row[k] = -4.0
+    x = _bits([row])
+    _, gam = _norm_inputs(1, K, 3)
+    xq, s, y, _ = oracle.rmsnorm_quant(x, gam, 0.0)
+    expect = np.zeros(K, np.float32)
+    expect[k] = -32.0 * _f32(gam)[k]
+    np.testing.assert_array_equal(_f32(y[0]), expect)
+    assert xq[0, k] == -127 and np.count_nonzero(xq[0]) == 1
+
+
+def test_rmsnorm_matches_torch_rms_norm():
+    """Against torch's RMSNorm in fp32 (its own summation order and rsqrt):
+    every output within 1 bf16 ulp, nearly all identical."""
+    M, K = 16, 5120
+    x, gam = _norm_inputs(M, K, 4, scale=3.0)
+    eps = 1e-6
+    _, _, y, _ = oracle.rmsnorm_quant(x, gam, eps)
+    h = torch.from_numpy(_f32(x))
+    t = torch.nn.functional.rms_norm(h, (K,), torch.from_numpy(_f32(gam)), eps)
+    tb = synth.bf16_bits(t.to(torch.bfloat16))
+
+    def ordered(u):
+        u = u.astype(np.int32)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    d = np.abs(ordered(y) - ordered(tb))
+    assert d.max() <= 1 and (d == 0).mean() > 0.99
+
+
+def test_rmsnorm_residual_add_matches_torch_bf16_add():
+    """The residual stream becomes bf16(x + res) (torch's bf16 addition), and
+    the norm is taken of that sum."""
+    M, K = 5, 640
+    x, gam = _norm_inputs(M, K, 5)
+    r, _ = _norm_inputs(M, K, 6, scale=4.0)
+    xq, s, y, res_out = oracle.rmsnorm_quant(x, gam, 1e-6, res_bf16=r)
+    tsum = synth.bits_to_bf16(x) + synth.bits_to_bf16(r)
+    np.testing.assert_array_equal(res_out, synth.bf16_bits(tsum))
+    ref = oracle.rmsnorm_quant(res_out, gam, 1e-6)
+    for a, b in zip((xq, s, y), ref[:3]):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_rmsnorm_quant_is_the_per_token_quant_of_y():
+    x, gam = _norm_inputs(9, 1024, 7)
+    xq, s, y, _ = oracle.rmsnorm_quant(x, gam, 1e-6)
+    xq2, s2 = oracle.quant_per_token(y)
+    np.testing.assert_array_equal(xq, xq2)
+    np.testing.assert_array_equal(s, s2)
+
+
+def test_rmsnorm_rejects_k_not_multiple_of_8():
+    x, gam = _norm_inputs(1, 12, 8)
+    with pytest.raises(ValueError):
+        oracle.rmsnorm_quant(x, gam, 1e-6)
+
+
+def test_rmsnorm_product_order_targeted():
+    """The normalized value is (h * rstd) * gamma, each product rounded to
+    fp32, then to bf16.  Rows of K = 256 with h = 1 except one entry v, and
+    eps = fl(1/3), so rstd is not a power of two.  Candidate (v, gamma) pairs
+    where h * (rstd * gamma) would round to a different bf16 are found with a
+    float64 search (every step is a product or quotient of fp32/bf16 values,
+    which float64 rounds innocuously to fp32); each found pair is confirmed
+    with exact rationals and a correctly rounded root, and the oracle must
+    give the stated order."""
+    from tests.exact import sqrt_fp32
+
+    def to_bf16_f64(a):  # fp32 values (as float64) -> bf16 RNE (as float64)
+        u = a.astype(np.float32).view(np.uint32).astype(np.uint64)
+        u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+        return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+    K = 256
+    vs = np.unique(to_bf16_f64(np.linspace(1.0, 4.0, 700)))
+    gms = np.unique(to_bf16_f64(np.linspace(0.5, 2.0, 600)))
+    pairs = []
+    for e in range(400):
+        eps32 = np.float32(np.float32(1.0) / np.float32(3.0 + e))
+        for v in vs:
+            ss = np.float64(K - 1) + v * v
+            var = np.float32(ss / K)
+            ve = np.float32(np.float64(var) + np.float64(eps32))
+            rstd = np.float32(1.0 / np.float64(np.float32(np.sqrt(np.float64(ve)))))
+            t = np.float64(np.float32(v * np.float64(rstd)))
+            stated = to_bf16_f64(np.float32(t * gms).astype(np.float64))
+            rg = np.float32(np.float64(rstd) * gms).astype(np.float64)
+            other = to_bf16_f64(np.float32(v * rg).astype(np.float64))
+            hit = np.nonzero(stated != other)[0]
+            if len(hit):
+                pairs.append((float(v), float(gms[hit[0]]), float(eps32)))
+                break
+        if len(pairs) >= 4:
+            break
+    assert len(pairs) >= 3
+    for v, gm, e32 in pairs:
+        v, gm, eps = Fraction(v), Fraction(gm), Fraction(e32)
+        ss = Fraction(K - 1) + v * v
+        var = fp32(ss / K)
+        rstd = fp32(1 / sqrt_fp32(fp32(var + eps)))
+        stated = bf16(fp32(fp32(v * rstd) * gm))
+        other = bf16(fp32(v * fp32(rstd * gm)))
+        assert stated != other  # the float64 search agrees with exact arithmetic
+        row = [1.0] * K
+        row[100] = float(v)
+        gam = [0.75] * K
+        gam[100] = float(gm)
+        _, _, y, _ = oracle.rmsnorm_quant(_bits([row]), _bits(gam), e32)
+        assert bf16_bits_value(int(y[0, 100])) == stated
+        assert bf16_bits_value(int(y[0, 0])) == bf16(fp32(fp32(rstd) * Fraction(3, 4)))
