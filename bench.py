@@ -1,7 +1,8 @@
 """Benchmark of the W8A8 INT8 linear layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--secondary decode,group128,w8a16 | none] [--calibrate-copy]
+                    [--secondary decode,group128,w8a16,rmsnorm_quant | none]
+                    [--calibrate-copy]
 
 A step is one pass of the W8A8 hot path over the prefill workload
 (X bf16 [8192, 5120] after the smoothing fold, W int8 [15360, 5120] with
@@ -215,8 +216,28 @@ def copy_calibration(dev, nbytes=512 << 20, reps=3):
             "GB/s": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
+def rmsnorm_quant_gbs(dev, iters=20):
+    """Residual add + RMSNorm + per-token quant at the prefill shape: bytes
+    = x read + residual read and write + codes + scales (+ gamma), over the
+    kernel time (events)."""
+    wl = synth.WORKLOADS["prefill"]
+    x = synth.activations(wl, 0).to(dev)
+    res = synth.activations(wl, 1).to(dev)
+    gam = torch.ones((wl.K,), dtype=torch.bfloat16, device=dev)
+    xq = torch.empty((wl.M, wl.K), dtype=torch.int8, device=dev)
+    st = torch.empty((wl.M,), dtype=torch.float32, device=dev)
+    f = lambda: q8.q8_rmsnorm_quant(x, gam, 1e-6, residual=res, out=xq, scale_out=st)  # noqa: E731
+    for _ in range(3):
+        f()
+    ms = events_time(f, iters)
+    nbytes = 2 * wl.M * wl.K * 3 + wl.M * wl.K + 4 * wl.M + 2 * wl.K
+    return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": nbytes,
+            "shape": [wl.M, wl.K]}
+
+
 SECONDARY = {"decode": lambda dev: decode_gbs(dev), "group128": lambda dev: group_tops(dev),
-             "w8a16": lambda dev: w8a16_tflops(dev)}
+             "w8a16": lambda dev: w8a16_tflops(dev), "rmsnorm_quant": lambda dev: rmsnorm_quant_gbs(dev)}
 
 
 def main():
@@ -226,7 +247,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--secondary", default="decode,group128,w8a16",
+    ap.add_argument("--secondary", default="decode,group128,w8a16,rmsnorm_quant",
                     help="comma list of secondary workloads, or 'none'")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()

@@ -216,6 +216,39 @@ q8_status q8_smooth_fold(const q8_bf16 *x, int64_t ldx, const float *w,
                          float *wo, int64_t ldwo, int64_t M, int64_t N,
                          int64_t K, float cap, q8_stream stream);
 
+/* ------------------------------------------------------------------------
+ * q8_rmsnorm_quant -- residual add + RMSNorm + per-token INT8 quantization
+ * in one pass: the step that feeds a W8A8 linear layer, whose smoothing
+ * divisor is folded into gamma offline.  Per row m (K a multiple of 8):
+ *   h = bf16_rne(x + residual), residual := h   (residual != NULL)
+ *   h = x                                       (residual == NULL)
+ *   ss = sum of h[k]^2 in fp32: 64 partial sums, partial l adding the
+ *        8-element chunks l, l+64, ... in ascending k, then combined by a
+ *        xor butterfly (p_l + p_{l^o}, o = 32, 16, ..., 1); ss = p_0
+ *   rstd = 1 / sqrtf(ss / K + eps)              (correctly rounded)
+ *   y[k] = bf16_rne((h[k] * rstd) * gamma[k])   (fp32 products)
+ *   xq, scale_tok = q8_quant_per_token of the bf16 row y
+ * Cited: "...W8A8 INT8 (v3)", "Recipe" (smoothing folded into the preceding
+ * norm); "Qwen3.8-27B -- FP8 block + AWQ", "Recipe" (the same fold);
+ * "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", "Serving (vLLM, gfx908 fork)"
+ * (residual add, RMSNorm and INT8 quantization fused into one step).
+ *   x        [M, ldx]  bf16, read
+ *   residual [M, ldr]  bf16, read and overwritten with h (may be NULL; may
+ *                      be the same buffer as x)
+ *   gamma    [K]       bf16, read
+ *   xq       [M, ldxq] int8, written; scale_tok [M] fp32, written
+ * Rules: M >= 0, 8 <= K <= 8192 with K % 8 == 0 (else Q8_EUNSUPPORTED);
+ * eps >= 0 (else Q8_EINVAL); ldx, ldr >= K and multiples of 8 with x,
+ * residual and gamma 16-byte aligned; ldxq >= K, a multiple of 8, xq
+ * 8-byte aligned.  The normalized row itself is not stored.  With eps == 0
+ * an all-zero row has no defined norm (0 * inf) and its outputs are
+ * unspecified; with eps > 0 it gives scale 0 and all-zero codes.
+ * ---------------------------------------------------------------------- */
+q8_status q8_rmsnorm_quant(const q8_bf16 *x, int64_t ldx, q8_bf16 *residual,
+                           int64_t ldr, const q8_bf16 *gamma, float eps,
+                           int8_t *xq, int64_t ldxq, float *scale_tok,
+                           int64_t M, int64_t K, q8_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

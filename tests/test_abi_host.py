@@ -89,6 +89,22 @@ def test_other_entry_points_validation(lib):
     assert lib.q8_smooth_fold(A, 256, B, 256, S, C, 256, C, 256, 4, 8, 256, f(0.0), None) == EINVAL
 
 
+def test_rmsnorm_quant_validation(lib):
+    f = ctypes.c_float
+    rn = lib.q8_rmsnorm_quant
+    assert rn(A, 256, None, 0, B, f(1e-6), C, 256, S, 0, 256, None) == OK   # M == 0
+    assert rn(None, 256, None, 0, B, f(1e-6), C, 256, S, 4, 256, None) == EINVAL
+    assert rn(A, 256, None, 0, None, f(1e-6), C, 256, S, 4, 256, None) == EINVAL
+    assert rn(A, 200, None, 0, B, f(1e-6), C, 256, S, 4, 256, None) == EINVAL  # ldx < K
+    assert rn(A, 256, A, 128, B, f(1e-6), C, 256, S, 4, 256, None) == EINVAL   # ldr < K
+    assert rn(A, 256, None, 0, B, f(-1.0), C, 256, S, 4, 256, None) == EINVAL  # eps < 0
+    assert rn(A, 256, None, 0, B, f(1e-6), C, 256, S, 4, 12, None) == EUNSUP   # K % 8
+    assert rn(A, 9000, None, 0, B, f(1e-6), C, 9000, S, 4, 8200, None) == EUNSUP  # K > 8192
+    assert rn(A + 8, 256, None, 0, B, f(1e-6), C, 256, S, 4, 256, None) == EUNSUP  # x misaligned
+    assert rn(A, 260, None, 0, B, f(1e-6), C, 256, S, 4, 256, None) == EUNSUP  # ldx % 8
+    assert rn(A, 256, None, 0, B, f(1e-6), C + 4, 256, S, 4, 256, None) == EUNSUP  # xq misaligned
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     x = torch.zeros((4, 256), dtype=torch.bfloat16)

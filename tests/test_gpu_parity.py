@@ -142,6 +142,69 @@ def test_quant_empty():
     assert xq.shape == (0, 256) and s.shape == (0,)
 
 
+# ------------------------------------ residual add + RMSNorm + quant --
+
+def _norm_case(M, K, pad, seed, with_res):
+    xf, _ = synth.custom(M, K + pad, 16, seed=seed, outlier_cols=max(1, K // 100))
+    g = np.random.default_rng(seed)
+    gam = torch.from_numpy((0.25 + g.random(K)).astype(np.float32)).to(torch.bfloat16)
+    rf = None
+    if with_res:
+        rf = torch.from_numpy((g.standard_normal((M, K + pad)) * 2).astype(np.float32)).to(torch.bfloat16)
+    return xf, gam, rf
+
+
+@pytest.mark.parametrize("M,K,with_res,pad", [(1, 8, False, 0), (3, 64, True, 0), (5, 520, False, 8),
+                                              (8, 5120, True, 0), (7, 8192, True, 16),
+                                              (33, 4096, True, 0), (200, 5120, False, 0),
+                                              (130, 1032, True, 24)])
+def test_rmsnorm_quant_shapes(M, K, with_res, pad):
+    say("rmsnorm_quant", M, K, with_res, pad)
+    eps = 1e-6
+    xf, gam, rf = _norm_case(M, K, pad, M * 7 + K, with_res)
+    x = xf[:, :K].contiguous()
+    x[M // 2] = 0
+    if with_res:
+        rf[M // 2, :K] = 0
+    r = None if rf is None else bits(rf[:, :K].contiguous())
+    xq_ref, s_ref, _, res_ref = oracle.rmsnorm_quant(bits(x), bits(gam), eps, res_bf16=r)
+    xfd = dev(xf)
+    xfd[:, :K] = dev(x)
+    rd = None if rf is None else dev(rf)
+    xq, s = q8.q8_rmsnorm_quant(xfd[:, :K], dev(gam), eps,
+                                residual=None if rd is None else rd[:, :K])
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    assert s_ref[M // 2] == 0
+    if with_res:
+        np.testing.assert_array_equal(bits(host(rd)[:, :K].contiguous()), res_ref)
+        if pad:  # columns past K of the residual are untouched
+            assert torch.equal(host(rd)[:, K:].view(torch.int16), rf[:, K:].view(torch.int16))
+
+
+def test_rmsnorm_quant_in_place_residual_and_prefill_size():
+    """The prefill workload's shape (8192 x 5120), with the residual stream
+    updated in place in the buffer x itself."""
+    wl = synth.WORKLOADS["prefill"]
+    say("rmsnorm_quant prefill size, in place")
+    x = synth.activations(wl, 0)
+    g = np.random.default_rng(3)
+    gam = torch.from_numpy((0.25 + g.random(wl.K)).astype(np.float32)).to(torch.bfloat16)
+    r = torch.from_numpy(g.standard_normal((wl.M, wl.K)).astype(np.float32)).to(torch.bfloat16)
+    xq_ref, s_ref, _, res_ref = oracle.rmsnorm_quant(bits(r), bits(gam), 1e-6, res_bf16=bits(x))
+    buf = dev(x)
+    xq, s = q8.q8_rmsnorm_quant(dev(r), dev(gam), 1e-6, residual=buf)
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    np.testing.assert_array_equal(bits(host(buf)), res_ref)
+    # x and the residual the same buffer: h = bf16(x + x) = 2x
+    b2 = dev(r)
+    xq2, s2 = q8.q8_rmsnorm_quant(b2, dev(gam), 1e-6, residual=b2)
+    xq2_ref, s2_ref, _, res2_ref = oracle.rmsnorm_quant(bits(r), bits(gam), 1e-6, res_bf16=bits(r))
+    np.testing.assert_array_equal(host(xq2).numpy(), xq2_ref)
+    np.testing.assert_array_equal(bits(host(b2)), res2_ref)
+
+
 # --------------------------------------------------------- weight quant --
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "group128", "w8a16"])

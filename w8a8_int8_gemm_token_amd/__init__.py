@@ -28,7 +28,7 @@ import torch
 __all__ = [
     "Q8Error", "lib_path", "load", "q8_quant_per_token", "q8_scaled_mm",
     "q8_scaled_mm_group128", "w8a16_mm", "q8_quant_scaled_mm", "q8_mm_i32",
-    "q8_quant_weight", "q8_smooth_fold", "EXPORTS", "MAX_K",
+    "q8_quant_weight", "q8_smooth_fold", "q8_rmsnorm_quant", "EXPORTS", "MAX_K",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +36,7 @@ MAX_K = 130944
 EXPORTS = (
     "q8_status_str", "q8_quant_per_token", "q8_scaled_mm",
     "q8_scaled_mm_group128", "w8a16_mm", "q8_quant_scaled_mm", "q8_mm_i32",
-    "q8_quant_weight", "q8_smooth_fold",
+    "q8_quant_weight", "q8_smooth_fold", "q8_rmsnorm_quant",
 )
 _STATUS = {0: "Q8_OK", 1: "Q8_EINVAL", 2: "Q8_EUNSUPPORTED", 3: "Q8_EHIP"}
 
@@ -77,6 +77,7 @@ def load():
         "q8_mm_i32": ([P, I, P, I, P, I, I, I, I, P], S),
         "q8_quant_weight": ([P, I, P, I, P, I, I, I, P], S),
         "q8_smooth_fold": ([P, I, P, I, P, P, I, P, I, I, I, I, F, P], S),
+        "q8_rmsnorm_quant": ([P, I, P, I, P, F, P, I, P, I, I, P], S),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -253,3 +254,26 @@ def q8_smooth_fold(x, w, cap: float = 16.0, x_out=None, w_out=None, s_out=None):
         _ptr(x), _ld(x), _ptr(w), _ld(w), _ptr(s), _ptr(xo), _ld(xo), _ptr(wo),
         _ld(wo), M, N, K, ctypes.c_float(cap), _stream(x.device)))
     return xo, wo, s
+
+
+def q8_rmsnorm_quant(x, gamma, eps: float, residual=None, out=None, scale_out=None):
+    """Residual add (optional, in place on `residual`) + RMSNorm + per-token
+    INT8 quant: returns (xq int8 [M,K], scale_tok fp32 [M])."""
+    _dev(x, torch.bfloat16, "x", 2)
+    _dev(gamma, torch.bfloat16, "gamma", 1)
+    M, K = x.shape
+    if gamma.numel() != K:
+        raise ValueError("gamma must have K entries")
+    if residual is not None:
+        _dev(residual, torch.bfloat16, "residual", 2)
+        if tuple(residual.shape) != (M, K):
+            raise ValueError("residual shape must match x")
+    xq = out if out is not None else torch.empty((M, K), dtype=torch.int8, device=x.device)
+    s = scale_out if scale_out is not None else torch.empty((M,), dtype=torch.float32, device=x.device)
+    _dev(xq, torch.int8, "out", 2)
+    _dev(s, torch.float32, "scale_out", 1)
+    _check("q8_rmsnorm_quant", load().q8_rmsnorm_quant(
+        _ptr(x), _ld(x), None if residual is None else _ptr(residual),
+        0 if residual is None else _ld(residual), _ptr(gamma), ctypes.c_float(eps),
+        _ptr(xq), _ld(xq), _ptr(s), M, K, _stream(x.device)))
+    return xq, s

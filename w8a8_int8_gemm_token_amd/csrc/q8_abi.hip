@@ -10,6 +10,7 @@
 #include "quant.hpp"
 #include "skinny.hpp"
 #include "decode_fused.hpp"
+#include "norm_quant.hpp"
 #include "w8a16.hpp"
 
 namespace {
@@ -208,6 +209,22 @@ q8_status q8_smooth_fold(const q8_bf16* x, int64_t ldx, const float* w, int64_t 
     hipLaunchKernelGGL(fold_w_f32, dim3(kb, (unsigned)(N < 65535 ? N : 65535)), dim3(256), 0, h, w,
                        ldw, s, wo, ldwo, iN, iK);
     return hip_status(hipGetLastError());
+}
+
+q8_status q8_rmsnorm_quant(const q8_bf16* x, int64_t ldx, q8_bf16* residual, int64_t ldr,
+                           const q8_bf16* gamma, float eps, int8_t* xq, int64_t ldxq,
+                           float* scale_tok, int64_t M, int64_t K, q8_stream stream) {
+    if (M < 0 || K < 0) return Q8_EINVAL;
+    if (M == 0) return Q8_OK;
+    if (!x || !gamma || !xq || !scale_tok || K == 0) return Q8_EINVAL;
+    if (ldx < K || ldxq < K || (residual && ldr < K) || !(eps >= 0.0f)) return Q8_EINVAL;
+    if (K % 8 != 0 || K > NORM_MAX_K || M > INT32_MAX / 2) return Q8_EUNSUPPORTED;
+    if (ldx % 8 != 0 || ldxq % 8 != 0 || (residual && ldr % 8 != 0)) return Q8_EUNSUPPORTED;
+    if (!al(x, 16) || !al(gamma, 16) || !al(xq, 8) || !al(scale_tok, 4) ||
+        (residual && !al(residual, 16)))
+        return Q8_EUNSUPPORTED;
+    return hip_status(launch_rmsnorm_quant(x, ldx, residual, residual ? ldr : 0, gamma, eps, xq,
+                                           ldxq, scale_tok, (int)M, (int)K, st(stream)));
 }
 
 }  // extern "C"
