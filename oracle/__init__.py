@@ -65,6 +65,8 @@ def _load():
             "q8o_smooth_fold_x": ([P, P, I, I, P], None),
             "q8o_smooth_fold_w": ([P, P, I, I, P], None),
             "q8o_rmsnorm_quant": ([P, P, P, F, I, I, P, P, P], ctypes.c_int),
+            "q8o_quant_per_group128": ([P, I, I, P, P], ctypes.c_int),
+            "q8o_scaled_mm_group128_act": ([P, P, P, P, I, I, I, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -238,3 +240,30 @@ def rmsnorm_quant(x_bf16, gamma_bf16, eps: float, res_bf16=None):
     if rc != 0:
         raise ValueError(f"oracle rmsnorm_quant failed ({rc}): K must be a multiple of 8")
     return xq, s, y, res
+
+
+def quant_per_group128(x_bf16):
+    """Per-token-per-128-group quant: -> (xq int8 [M,K], s_x fp32 [M,K/128])."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    xq = np.empty((M, K), np.int8)
+    s = np.empty((M, K // 128), np.float32)
+    if _load().q8o_quant_per_group128(_p(x), M, K, _p(xq), _p(s)) != 0:
+        raise ValueError("oracle: K must be a multiple of 128")
+    return xq, s
+
+
+def scaled_mm_group128_act(a, b, s_x, s_w) -> np.ndarray:
+    """GEMM with per-(token, block) and per-(channel, block) scales:
+    s_x fp32 [M, K/128], s_w fp32 [N, K/128] -> bf16 bits uint16 [M,N]."""
+    a = _c(a, np.int8)
+    b = _c(b, np.int8)
+    s_x = _c(s_x, np.float32)
+    s_w = _c(s_w, np.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    assert s_x.shape == (M, K // 128) and s_w.shape == (N, K // 128)
+    y = np.empty((M, N), np.uint16)
+    if _load().q8o_scaled_mm_group128_act(_p(a), _p(b), _p(s_x), _p(s_w), M, N, K, _p(y)) != 0:
+        raise ValueError("oracle: K must be a multiple of 128")
+    return y

@@ -408,3 +408,59 @@ int q8o_rmsnorm_quant(const uint16_t *x, uint16_t *res, const uint16_t *gamma,
     }
     return bad ? -2 : 0;
 }
+
+/* --------------------- per-token-per-group activations, group-128 weights --
+ * Activations quantized with one scale per (token, 128-wide K block) and
+ * weights with one scale per (channel, 128-wide K block) [P5 "Serving
+ * (vLLM, gfx908 fork)": per-group INT8 quant-out before the GEMM; P3
+ * "Recipe": dynamic per-group activation scales; P5 "Quantization details":
+ * group size 128, natural K order].
+ * Quantization: every 128-wide block of a row is quantized like a token row
+ * on its own: s_x[m][g] = fl32(absmax / 127), codes RNE of fl32(x / s),
+ * clamped to [-127, 127]; s_x is [M][K/128] row-major. */
+int q8o_quant_per_group128(const uint16_t *x, int64_t M, int64_t K,
+                           int8_t *xq, float *s_x)
+{
+    if (K % 128 != 0) return -1;
+    const int64_t G = K / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float v[128];
+        for (int64_t g = 0; g < G; ++g) {
+            for (int k = 0; k < 128; ++k) v[k] = bf16_bits_to_f32(x[m * K + g * 128 + k]);
+            const float sc = absmax_scale(v, 128);
+            s_x[m * G + g] = sc;
+            for (int k = 0; k < 128; ++k) xq[m * K + g * 128 + k] = code_of(v[k], sc);
+        }
+    }
+    return 0;
+}
+
+/* GEMM with both scales per 128-wide K block.  For g = 0 .. K/128-1 in
+ * order (reading: the two scales are multiplied first, as block-scaled
+ * GEMMs do, then one fused multiply-add per block):
+ *   p_g = sum_{k in [128g, 128g+128)} a[m][k]*b[n][k]    (exact int32)
+ *   acc = fmaf((float)p_g, fl32(s_x[m][g] * s_w[n][g]), acc)   (from 0)
+ * y = bf16_rne(acc).  Returns -1 if K is not a multiple of 128. */
+int q8o_scaled_mm_group128_act(const int8_t *a, const int8_t *b,
+                               const float *s_x, const float *s_w,
+                               int64_t M, int64_t N, int64_t K, uint16_t *y)
+{
+    if (K % 128 != 0) return -1;
+    const int64_t G = K / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float acc = 0.0f;
+            for (int64_t g = 0; g < G; ++g) {
+                int32_t p = 0;
+                for (int64_t k = g * 128; k < g * 128 + 128; ++k)
+                    p += (int32_t)a[m * K + k] * (int32_t)b[n * K + k];
+                const float sc = s_x[m * G + g] * s_w[n * G + g];
+                acc = fmaf((float)p, sc, acc);
+            }
+            y[m * N + n] = q8o_f32_to_bf16(acc);
+        }
+    }
+    return 0;
+}

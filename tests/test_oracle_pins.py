@@ -586,3 +586,94 @@ def test_rmsnorm_product_order_targeted():
         _, _, y, _ = oracle.rmsnorm_quant(_bits([row]), _bits(gam), e32)
         assert bf16_bits_value(int(y[0, 100])) == stated
         assert bf16_bits_value(int(y[0, 0])) == bf16(fp32(fp32(rstd) * Fraction(3, 4)))
+
+
+# -------------------- per-token-per-group activations, group-128 weights --
+# "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", "Serving (vLLM, gfx908 fork)"
+# (per-group INT8 quant-out before the GEMM) and "Quantization details"
+# (group 128, natural K order); "Qwen3.8-27B -- FP8 block + AWQ", "Recipe"
+# (dynamic per-group activation scales).
+
+def test_quant_per_group128_is_per_token_quant_of_each_block():
+    """Grouping only: each 128-wide block equals the (separately pinned)
+    per-token quantizer applied to that block as a row."""
+    x = synth.activations(synth.WORKLOADS["decode"], 0)[:, :1024].contiguous()
+    xb = synth.bf16_bits(x)
+    xq, s = oracle.quant_per_group128(xb)
+    M, K = xb.shape
+    xq2, s2 = oracle.quant_per_token(xb.reshape(M * K // 128, 128))
+    np.testing.assert_array_equal(xq, xq2.reshape(M, K))
+    np.testing.assert_array_equal(s, s2.reshape(M, K // 128))
+    # invariants: range, block absmax -> +-127, round trip within s/2
+    assert np.abs(xq.astype(np.int32)).max() <= 127
+    blocks = np.abs(_f32(xb)).reshape(M, K // 128, 128)
+    codes = np.abs(xq.astype(np.int32)).reshape(M, K // 128, 128)
+    am = blocks.argmax(axis=2)
+    assert (np.take_along_axis(codes, am[..., None], 2) == 127).all()
+    err = np.abs(_f32(xb).reshape(M, K // 128, 128).astype(np.float64)
+                 - xq.reshape(M, K // 128, 128) * s[..., None].astype(np.float64))
+    assert (err <= s[..., None] * (0.5 + 2 ** -15)).all()
+
+
+def test_group128_act_exact_rational_chain():
+    """fl32(s_x * s_w) first, then one fused multiply-add per block in
+    ascending order, bf16 at the end: exact rationals, one rounding each."""
+    M, N, K = 3, 4, 640
+    a = synth.int8_uniform((M, K), seed=31)
+    b = synth.int8_uniform((N, K), seed=32)
+    s_x = synth.uniform_f32((M, K // 128), 33, 1e-3, 0.5)
+    s_w = synth.uniform_f32((N, K // 128), 34, 1e-5, 1e-3)
+    y = oracle.scaled_mm_group128_act(a, b, s_x, s_w)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for g in range(K // 128):
+                p = int(np.dot(a[m, 128 * g:128 * g + 128].astype(np.int64),
+                               b[n, 128 * g:128 * g + 128].astype(np.int64)))
+                sc = fp32(Fraction(float(s_x[m, g])) * Fraction(float(s_w[n, g])))
+                acc = fp32(Fraction(p) * sc + acc)
+            assert y[m, n] == bf16_bits_of(bf16(acc)), (m, n)
+
+
+def test_group128_act_reduces_to_group128_with_unit_activation_scales():
+    """With every activation block scale 1, the result is the group-128
+    weight-scale GEMM with token scale 1, bit for bit."""
+    M, N, K = 7, 32, 1024
+    a = synth.int8_uniform((M, K), seed=35)
+    b = synth.int8_uniform((N, K), seed=36)
+    s_w = synth.uniform_f32((N, K // 128), 37, 1e-5, 1e-3)
+    y = oracle.scaled_mm_group128_act(a, b, np.ones((M, K // 128), np.float32), s_w)
+    y2 = oracle.scaled_mm_group128(a, b, np.ones(M, np.float32), s_w)
+    np.testing.assert_array_equal(y, y2)
+
+
+def test_group128_act_scale_product_order_targeted():
+    """The block scale is fl32(s_x * s_w), applied to the exact block sum in
+    one rounding (not fl32(p * s_x) * s_w).  Scale pairs where the two
+    readings give different bf16 results are found by a float64 search
+    (products of fp32 values round innocuously from float64), confirmed with
+    exact rationals, and the oracle must give the stated one."""
+    g = np.random.default_rng(41)
+    a = synth.int8_uniform((1, 128), seed=42)
+    b = synth.int8_uniform((1, 128), seed=43)
+    p = int(np.dot(a[0].astype(np.int64), b[0].astype(np.int64)))
+    assert p != 0
+    sx = g.uniform(1e-3, 1.0, 400000).astype(np.float32).astype(np.float64)
+    sw = g.uniform(1e-4, 1e-2, 400000).astype(np.float32).astype(np.float64)
+
+    def bf16_of(v32):
+        u = v32.astype(np.float32).view(np.uint32).astype(np.uint64)
+        return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    sc = (sx * sw).astype(np.float32).astype(np.float64)
+    stated = bf16_of((p * sc).astype(np.float32))
+    other = bf16_of(((p * sx).astype(np.float32).astype(np.float64) * sw).astype(np.float32))
+    idx = np.nonzero(stated != other)[0][:3]
+    assert len(idx) >= 2
+    for i in idx:
+        fx, fw = Fraction(float(sx[i])), Fraction(float(sw[i]))
+        exact_stated = bf16(fp32(Fraction(p) * fp32(fx * fw)))
+        exact_other = bf16(fp32(fp32(Fraction(p) * fx) * fw))
+        assert exact_stated != exact_other
+        y = oracle.scaled_mm_group128_act(a, b, np.array([[sx[i]]], np.float32),
+                                          np.array([[sw[i]]], np.float32))
+        assert bf16_bits_value(int(y[0, 0])) == exact_stated
