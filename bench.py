@@ -1,7 +1,8 @@
 """Benchmark of the W8A8 INT8 linear layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--secondary decode,group128,w8a16,rmsnorm_quant | none]
+                    [--secondary decode,group128,group128_act,w8a16,rmsnorm_quant
+                                 | none]
                     [--calibrate-copy]
 
 A step is one pass of the W8A8 hot path over the prefill workload
@@ -236,7 +237,31 @@ def rmsnorm_quant_gbs(dev, iters=20):
             "shape": [wl.M, wl.K]}
 
 
+def group_act_tops(dev, iters=20):
+    """Per-token-per-group activation quant + the GEMM with both block
+    scales, at the group-128 workload shape."""
+    wl = synth.WORKLOADS["group128"]
+    x = synth.activations(wl, 0).to(dev)
+    w = synth.weights(wl, 0).to(dev)
+    wq, sw = q8.q8_quant_weight(w, group=128)
+    del w
+    xq, sx = q8.q8_quant_per_group128(x)
+    y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
+    g = lambda: q8.q8_scaled_mm_group128_act(xq, wq, sx, sw, out=y)  # noqa: E731
+    qf = lambda: q8.q8_quant_per_group128(x, out=xq, scale_out=sx)  # noqa: E731
+    for _ in range(3):
+        qf()
+        g()
+    gms = events_time(g, iters)
+    qms = events_time(qf, iters)
+    t = 2.0 * wl.M * wl.N * wl.K / (gms * 1e-3) / 1e12
+    qbytes = 3 * wl.M * wl.K + 4 * wl.M * (wl.K // 128)
+    return {"gemm_us": gms * 1e3, "TOPS": t, "frac_int8_peak": t / PEAK_INT8_TOPS,
+            "quant_us": qms * 1e3, "quant_GB/s": qbytes / (qms * 1e-3) / 1e9}
+
+
 SECONDARY = {"decode": lambda dev: decode_gbs(dev), "group128": lambda dev: group_tops(dev),
+             "group128_act": lambda dev: group_act_tops(dev),
              "w8a16": lambda dev: w8a16_tflops(dev), "rmsnorm_quant": lambda dev: rmsnorm_quant_gbs(dev)}
 
 
@@ -247,7 +272,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--secondary", default="decode,group128,w8a16,rmsnorm_quant",
+    ap.add_argument("--secondary", default="decode,group128,group128_act,w8a16,rmsnorm_quant",
                     help="comma list of secondary workloads, or 'none'")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()

@@ -249,6 +249,44 @@ q8_status q8_rmsnorm_quant(const q8_bf16 *x, int64_t ldx, q8_bf16 *residual,
                            int8_t *xq, int64_t ldxq, float *scale_tok,
                            int64_t M, int64_t K, q8_stream stream);
 
+/* ------------------------------------------------------------------------
+ * q8_quant_per_group128 -- per-token-per-group dynamic INT8 quantization:
+ * one scale per (row m, 128-wide K block g), each block quantized like a
+ * token row of 128 values:
+ *   scale_grp[m*(K/128) + g] = max_{k in block} |x[m,k]| / 127 (correctly
+ *                              rounded; 0 for an all-zero block)
+ *   xq[m,k] = clamp(rne(x[m,k] / scale), -127, 127)
+ * Cited: "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", "Serving (vLLM, gfx908 fork)"
+ * (per-group INT8 quantization of the activations) and "Quantization
+ * details" (group size 128); "Qwen3.8-27B -- FP8 block + AWQ", "Recipe"
+ * (dynamic per-group activation scales).
+ *   x [M, ldx] bf16; xq [M, ldxq] int8; scale_grp [M, K/128] fp32 (dense)
+ * Rules: M >= 0; K % 128 == 0 (else Q8_EUNSUPPORTED); ldx, ldxq >= K and
+ * multiples of 8; x 16-byte, xq 8-byte aligned.
+ * ---------------------------------------------------------------------- */
+q8_status q8_quant_per_group128(const q8_bf16 *x, int64_t ldx, int8_t *xq,
+                                int64_t ldxq, float *scale_grp, int64_t M,
+                                int64_t K, q8_stream stream);
+
+/* ------------------------------------------------------------------------
+ * q8_scaled_mm_group128_act -- INT8 GEMM with one scale per (token, 128-wide
+ * K block) on the activations and one per (channel, 128-wide K block) on
+ * the weights, bf16 out.  For g = 0..K/128-1 in ascending order:
+ *   p_g = sum_{k in [128g, 128g+128)} a[m,k] * b[n,k]        (exact int32)
+ *   acc = fmaf((float)p_g, fl32(scale_x[m,g] * scale_w[n,g]), acc)  (from 0)
+ * then c[m,n] = bf16_rne(acc).  (The two block scales are multiplied first,
+ * then applied to the block sum with one rounding.)
+ * Cited: as q8_quant_per_group128 and q8_scaled_mm_group128.
+ *   a [M, lda] int8 codes of q8_quant_per_group128; b [N, ldb] int8;
+ *   scale_x [M, K/128], scale_w [N, K/128] fp32 row-major; c [M, ldc] bf16.
+ * Rules: as q8_scaled_mm_group128.
+ * ---------------------------------------------------------------------- */
+q8_status q8_scaled_mm_group128_act(const int8_t *a, int64_t lda,
+                                    const int8_t *b, int64_t ldb,
+                                    const float *scale_x, const float *scale_w,
+                                    q8_bf16 *c, int64_t ldc, int64_t M,
+                                    int64_t N, int64_t K, q8_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -105,6 +105,19 @@ def test_rmsnorm_quant_validation(lib):
     assert rn(A, 256, None, 0, B, f(1e-6), C + 4, 256, S, 4, 256, None) == EUNSUP  # xq misaligned
 
 
+def test_per_group_entry_points_validation(lib):
+    qg = lib.q8_quant_per_group128
+    assert qg(A, 256, B, 256, S, 0, 256, None) == OK
+    assert qg(None, 256, B, 256, S, 4, 256, None) == EINVAL
+    assert qg(A, 256, B, 256, S, 4, 192, None) == EUNSUP     # K % 128
+    assert qg(A, 260, B, 256, S, 4, 256, None) == EUNSUP     # ldx % 8
+    assert qg(A, 256, B + 4, 256, S, 4, 256, None) == EUNSUP  # xq misaligned
+    ga = lib.q8_scaled_mm_group128_act
+    assert ga(A, 256, B, 256, None, S, C, 128, 16, 128, 256, None) == EINVAL
+    assert ga(A, 256, B, 256, S, None, C, 128, 16, 128, 256, None) == EINVAL
+    assert ga(A, 256, B, 256, S, S, C, 128, 16, 128, 192, None) == EUNSUP
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     x = torch.zeros((4, 256), dtype=torch.bfloat16)

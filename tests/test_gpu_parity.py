@@ -421,6 +421,55 @@ def test_prefill_full_size_sampled_rows():
     assert_ulp1(yh[rows], y_ref, "prefill sampled rows")
 
 
+# ----------------------------- per-group activations, group-128 weights --
+
+@pytest.mark.parametrize("M,K,pad", [(1, 128, 0), (3, 640, 8), (8, 5120, 0), (130, 1024, 16),
+                                     (33, 4096, 0)])
+def test_quant_per_group128(M, K, pad):
+    say("quant per group128", M, K, pad)
+    xf, _ = synth.custom(M, K + pad, 16, seed=M + K, outlier_cols=max(1, K // 100))
+    x = xf[:, :K].contiguous()
+    x[M // 2, :128] = 0  # an all-zero block
+    xf[:, :K] = x
+    xq_ref, s_ref = oracle.quant_per_group128(bits(x))
+    xq, s = q8.q8_quant_per_group128(dev(xf)[:, :K])
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (8, 256, 1024), (64, 144, 640),
+                                   (65, 272, 1152), (200, 384, 2048), (257, 128, 256)])
+def test_scaled_mm_group128_act_shapes(M, N, K):
+    say("group128 act", M, N, K)
+    x, w = synth.custom(M, K, N, seed=M * 3 + N, outlier_cols=3)
+    xq_ref, sx_ref = oracle.quant_per_group128(bits(x))
+    wq_ref, sw_ref = oracle.quant_weight(w.numpy(), group=128)
+    y_ref = oracle.scaled_mm_group128_act(xq_ref, wq_ref, sx_ref, sw_ref)
+    xq, sx = q8.q8_quant_per_group128(dev(x))
+    wq, sw = q8.q8_quant_weight(dev(w), group=128)
+    y = q8.q8_scaled_mm_group128_act(xq, wq, sx, sw)
+    assert_ulp1(bits(host(y)), y_ref, f"group128 act {M}x{N}x{K}")
+
+
+def test_group128_act_full_size_sampled_rows():
+    """The group-128 workload's shape (4096 x 5120 x 5120) with per-group
+    activation scales, in one launch; sampled rows against the oracle."""
+    wl = synth.WORKLOADS["group128"]
+    say("group128 act full size")
+    x = synth.activations(wl, 0)
+    w = synth.weights(wl, 0)
+    xq_ref, sx_ref = oracle.quant_per_group128(bits(x))
+    wq_ref, sw_ref = oracle.quant_weight(w.numpy(), group=128)
+    xq, sx = q8.q8_quant_per_group128(dev(x))
+    wq, sw = q8.q8_quant_weight(dev(w), group=128)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    np.testing.assert_array_equal(host(sx).numpy(), sx_ref)
+    y = q8.q8_scaled_mm_group128_act(xq, wq, sx, sw)
+    rows = np.array([0, 1, 127, 128, 2047, 4094, 4095, 777, 3333])
+    y_ref = oracle.scaled_mm_group128_act(xq_ref[rows], wq_ref, sx_ref[rows], sw_ref)
+    assert_ulp1(bits(host(y))[rows], y_ref, "group128 act sampled rows")
+
+
 # ------------------------------------------------------------ group 128 --
 
 @pytest.mark.parametrize("M,N,K", [(16, 128, 256), (33, 144, 384), (130, 256, 1024),

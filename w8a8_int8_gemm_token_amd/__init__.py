@@ -28,7 +28,8 @@ import torch
 __all__ = [
     "Q8Error", "lib_path", "load", "q8_quant_per_token", "q8_scaled_mm",
     "q8_scaled_mm_group128", "w8a16_mm", "q8_quant_scaled_mm", "q8_mm_i32",
-    "q8_quant_weight", "q8_smooth_fold", "q8_rmsnorm_quant", "EXPORTS", "MAX_K",
+    "q8_quant_weight", "q8_smooth_fold", "q8_rmsnorm_quant", "q8_quant_per_group128",
+    "q8_scaled_mm_group128_act", "EXPORTS", "MAX_K",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +37,8 @@ MAX_K = 130944
 EXPORTS = (
     "q8_status_str", "q8_quant_per_token", "q8_scaled_mm",
     "q8_scaled_mm_group128", "w8a16_mm", "q8_quant_scaled_mm", "q8_mm_i32",
-    "q8_quant_weight", "q8_smooth_fold", "q8_rmsnorm_quant",
+    "q8_quant_weight", "q8_smooth_fold", "q8_rmsnorm_quant", "q8_quant_per_group128",
+    "q8_scaled_mm_group128_act",
 )
 _STATUS = {0: "Q8_OK", 1: "Q8_EINVAL", 2: "Q8_EUNSUPPORTED", 3: "Q8_EHIP"}
 
@@ -78,6 +80,8 @@ def load():
         "q8_quant_weight": ([P, I, P, I, P, I, I, I, P], S),
         "q8_smooth_fold": ([P, I, P, I, P, P, I, P, I, I, I, I, F, P], S),
         "q8_rmsnorm_quant": ([P, I, P, I, P, F, P, I, P, I, I, P], S),
+        "q8_quant_per_group128": ([P, I, P, I, P, I, I, P], S),
+        "q8_scaled_mm_group128_act": ([P, I, P, I, P, P, P, I, I, I, I, P], S),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -277,3 +281,36 @@ def q8_rmsnorm_quant(x, gamma, eps: float, residual=None, out=None, scale_out=No
         0 if residual is None else _ld(residual), _ptr(gamma), ctypes.c_float(eps),
         _ptr(xq), _ld(xq), _ptr(s), M, K, _stream(x.device)))
     return xq, s
+
+
+def q8_quant_per_group128(x, out=None, scale_out=None):
+    """Per-token-per-128-group INT8: x bf16 [M,K] -> (xq int8 [M,K],
+    scale fp32 [M, K/128])."""
+    _dev(x, torch.bfloat16, "x", 2)
+    M, K = x.shape
+    xq = out if out is not None else torch.empty((M, K), dtype=torch.int8, device=x.device)
+    s = scale_out if scale_out is not None else torch.empty((M, K // 128), dtype=torch.float32,
+                                                           device=x.device)
+    _dev(xq, torch.int8, "out", 2)
+    _dev(s, torch.float32, "scale_out", 2)
+    if not s.is_contiguous():
+        raise ValueError("scale_out must be contiguous")
+    _check("q8_quant_per_group128", load().q8_quant_per_group128(
+        _ptr(x), _ld(x), _ptr(xq), _ld(xq), _ptr(s), M, K, _stream(x.device)))
+    return xq, s
+
+
+def q8_scaled_mm_group128_act(a, b, scale_x, scale_w, out=None):
+    """bf16 [M,N]: per 128-block fmaf((float)p_g, fl(s_x[m,g]*s_w[n,g]), acc)."""
+    M, N, K = _mk(a, b)
+    _dev(scale_x, torch.float32, "scale_x", 2)
+    _dev(scale_w, torch.float32, "scale_w", 2)
+    if tuple(scale_x.shape) != (M, K // 128) or tuple(scale_w.shape) != (N, K // 128):
+        raise ValueError("block scale shapes must be [M, K/128] and [N, K/128]")
+    if not scale_x.is_contiguous() or not scale_w.is_contiguous():
+        raise ValueError("block scales must be contiguous")
+    c = _gemm_out(M, N, a.device, out)
+    _check("q8_scaled_mm_group128_act", load().q8_scaled_mm_group128_act(
+        _ptr(a), _ld(a), _ptr(b), _ld(b), _ptr(scale_x), _ptr(scale_w), _ptr(c), _ld(c),
+        M, N, K, _stream(a.device)))
+    return c

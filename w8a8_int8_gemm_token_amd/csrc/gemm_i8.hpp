@@ -6,6 +6,9 @@
 //   EPI_GROUP:   for each 128-wide K block g in ascending order, the exact
 //                int32 block sum p_g is folded as f = fmaf((float)p_g,
 //                s_grp[n,g], f); y = bf16_rne(f * s_tok[m])
+//   EPI_GROUP_ACT: as EPI_GROUP with one activation scale per (token,
+//                128-wide K block) as well: f = fmaf((float)p_g,
+//                fl(s_x[m,g] * s_w[n,g]), f); y = bf16_rne(f)
 //   EPI_I32:     the raw int32 acc
 // "Qwen3.8-27B -- SmoothQuant + activation-aware GPTQ, W8A8 INT8 (v3)",
 // sections "Recipe" and "Serving" (INT8 x INT8 with per-token x per-channel
@@ -52,14 +55,14 @@
 
 namespace q8 {
 
-enum { EPI_I32 = 0, EPI_CHANNEL = 1, EPI_GROUP = 2 };
+enum { EPI_I32 = 0, EPI_CHANNEL = 1, EPI_GROUP = 2, EPI_GROUP_ACT = 3 };
 
 struct GemmArgs {
     const int8_t* x;  // activations (tokens) [M, ldx]
     int64_t ldx;
     const int8_t* w;  // weights (channels) [N, ldw]
     int64_t ldw;
-    const float* s_tok;  // [M]
+    const float* s_tok;  // [M]; EPI_GROUP_ACT: [M, K/128] per (token, block)
     const float* s_w;    // [N] per channel, or [N, K/128] per group
     void* c;             // [M, ldc] bf16 bits, or int32
     int64_t ldc;
@@ -113,21 +116,27 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     constexpr int XIW = BM / 8 / NW, WIW = BN / 8 / NW;  // 8-row loads per wave and stage
-    constexpr int SGI = (EPI == EPI_GROUP) ? BN / 64 : 0;  // 64-scale loads per stage
-    constexpr int LPS = XIW + WIW + (SGI + NW - 1) / NW;
+    constexpr bool GRP = EPI == EPI_GROUP || EPI == EPI_GROUP_ACT;
+    constexpr bool ACT = EPI == EPI_GROUP_ACT;
+    constexpr int SGI = GRP ? BN / 64 : 0;             // 64-scale weight loads per stage
+    constexpr int SXI = ACT ? (BM + 63) / 64 : 0;      // 64-scale activation loads per stage
+    constexpr int LPS = XIW + WIW + (SGI + NW - 1) / NW + (SXI + NW - 1) / NW;
+    constexpr int LSN = GRP ? BN + (ACT ? SXI * 64 : 0) : 4;  // scale floats per stage
     constexpr int NR = TM + TN;  // fragment reads per sub-step
     constexpr int NM = TM * TN;  // MFMAs per sub-step
     constexpr int NM0 = NM / 2;  // MFMAs of sub-step 3 before the hand-over
     static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "tile shape");
     static_assert(XIW * 8 * NW == BM && WIW * 8 * NW == BN, "load split");
-    static_assert(EPI != EPI_GROUP || BN % 64 == 0, "group scales load 64 at a time");
+    static_assert(!GRP || BN % 64 == 0, "group scales load 64 at a time");
 
     __shared__ __attribute__((aligned(1024))) int8_t lx0[BM * BK];
     __shared__ __attribute__((aligned(1024))) int8_t lx1[BM * BK];
     __shared__ __attribute__((aligned(1024))) int8_t lw0[BN * BK];
     __shared__ __attribute__((aligned(1024))) int8_t lw1[BN * BK];
-    __shared__ __attribute__((aligned(16))) float ls0[EPI == EPI_GROUP ? BN : 4];
-    __shared__ __attribute__((aligned(16))) float ls1[EPI == EPI_GROUP ? BN : 4];
+    // per stage: the tile's BN weight block scales, then (EPI_GROUP_ACT) its
+    // activation block scales
+    __shared__ __attribute__((aligned(16))) float ls0[LSN];
+    __shared__ __attribute__((aligned(16))) float ls1[LSN];
 
     const int M = p.M, N = p.N, K = p.K;
     const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
@@ -160,6 +169,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     const int xs0 = (m0 + wid * XIW * 8) * (int)p.ldx;  // scalar row offsets
     const int ws0 = (n0 + wid * WIW * 8) * (int)p.ldw;
     const int sv = (n0 + lane) * G * 4;  // group scales: channel n0 + 64*i + lane
+    const __amdgpu_buffer_rsrc_t sxr = make_rsrc(p.s_tok, (uint32_t)((int64_t)M * G * 4));
+    const int svx = (m0 + lane) * G * 4;  // activation block scales: token m0 + 64*i + lane
 
     auto issue = [&](int kt, int8_t* bx, int8_t* bw, float* bs) __attribute__((always_inline)) {
         const int koff = kt * BK;
@@ -182,6 +193,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
                                                              j * 64 * G * 4 + kt * 4, 0, 0);
             }
         }
+        if constexpr (SXI > 0) {
+#pragma unroll
+            for (int i = 0; i < (SXI + NW - 1) / NW; ++i) {
+                const int j = wid + i * NW;
+                if (j < SXI)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(sxr, (Q8_LDS void*)(bs + BN + j * 64), 4,
+                                                             svx, j * 64 * G * 4 + kt * 4, 0, 0);
+            }
+        }
     };
 
     // ---- fragment reads: sub-step kk of 32-row block b sits at
@@ -197,12 +217,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     }
 
     v16i acc[TM][TN];
-    v16f facc[EPI == EPI_GROUP ? TM : 1][EPI == EPI_GROUP ? TN : 1];
+    v16f facc[GRP ? TM : 1][GRP ? TN : 1];
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
         for (int b = 0; b < TN; ++b) acc[a][b] = v16i{};
-    if constexpr (EPI == EPI_GROUP) {
+    if constexpr (GRP) {
 #pragma unroll
         for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -228,7 +248,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     // EPI_GROUP: fold the stage's 128-wide block sums into the fp32
     // accumulators (the stage is group kt; groups arrive in ascending order)
     auto fold = [&](const float* bs) __attribute__((always_inline)) {
-        if constexpr (EPI == EPI_GROUP) {
+        if constexpr (GRP) {
+            float sx[TM];  // EPI_GROUP_ACT: block scale of this lane's token in block a
+#pragma unroll
+            for (int a = 0; a < TM; ++a) sx[a] = ACT ? bs[BN + wm * WTM + a * 32 + (lane & 31)] : 1.0f;
 #pragma unroll
             for (int b = 0; b < TN; ++b) {
 #pragma unroll
@@ -239,7 +262,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             facc[a][b][g * 4 + e] = __builtin_fmaf(
-                                (float)acc[a][b][g * 4 + e], sc[e], facc[a][b][g * 4 + e]);
+                                (float)acc[a][b][g * 4 + e], ACT ? sx[a] * sc[e] : sc[e],
+                                facc[a][b][g * 4 + e]);
                 }
 #pragma unroll
                 for (int a = 0; a < TM; ++a) acc[a][b] = v16i{};
@@ -270,7 +294,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
         interleave<NM, NR, 0>();
         __builtin_amdgcn_sched_barrier(0);
         // sub-step 3: part of the MFMAs, then the stage hand-over
-        if constexpr (EPI == EPI_GROUP) {
+        if constexpr (GRP) {
             // the group fold reads this stage's scales: do it before the
             // hand-over frees the stage
             mfma(1, 0, NM);
@@ -309,7 +333,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     for (int a = 0; a < TM; ++a) {
         const int j = m0 + wm * WTM + a * 32 + (lane & 31);  // token
         if (j >= M) continue;
-        const float st = (EPI == EPI_I32) ? 0.0f : p.s_tok[j];
+        const float st = (EPI == EPI_I32 || EPI == EPI_GROUP_ACT) ? 0.0f : p.s_tok[j];
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
 #pragma unroll
@@ -330,8 +354,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
                         if constexpr (EPI == EPI_CHANNEL) {
                             float t = (float)acc[a][b][g * 4 + e] * st;
                             v[e] = t * p.s_w[ch + e];
-                        } else {
+                        } else if constexpr (EPI == EPI_GROUP) {
                             v[e] = facc[a][b][g * 4 + e] * st;
+                        } else {
+                            v[e] = facc[a][b][g * 4 + e];
                         }
                     }
                     v2u o;
@@ -349,7 +375,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
 inline bool gemm_offsets_fit(const GemmArgs& p) {
     const int64_t lim = (int64_t)1 << 31;
     return ((int64_t)p.M + 256) * p.ldx + 256 < lim && ((int64_t)p.N + 256) * p.ldw + 256 < lim &&
-           ((int64_t)p.N + 256) * (p.K / 128) * 4 + 256 < lim;
+           ((int64_t)p.N + 256) * (p.K / 128) * 4 + 256 < lim &&
+           ((int64_t)p.M + 256) * (p.K / 128) * 4 + 256 < lim;
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int GM>

@@ -65,6 +65,11 @@ hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
     return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
 }
 
+hipError_t run_gemm_group_act(const GemmArgs& p, hipStream_t s) {
+    if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI_GROUP_ACT, 8>(p, s);
+    return launch_gemm_i8<128, 128, 2, 2, EPI_GROUP_ACT, 8>(p, s);
+}
+
 hipError_t run_gemm_group(const GemmArgs& p, hipStream_t s) {
     if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI_GROUP, 8>(p, s);
     return launch_gemm_i8<128, 128, 2, 2, EPI_GROUP, 8>(p, s);
@@ -80,6 +85,12 @@ hipError_t run_quant(const uint16_t* x, int64_t ldx, int8_t* xq, int64_t ldxq, f
         hipLaunchKernelGGL(quant_per_token_reg<1>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
     else if (vec && K <= 2048)
         hipLaunchKernelGGL(quant_per_token_reg<4>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
+    else if (vec && K <= 3072)
+        hipLaunchKernelGGL(quant_per_token_reg<6>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
+    else if (vec && K <= 4096)
+        hipLaunchKernelGGL(quant_per_token_reg<8>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
+    else if (vec && K <= 5120)
+        hipLaunchKernelGGL(quant_per_token_reg<10>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
     else if (vec && K <= 8192)
         hipLaunchKernelGGL(quant_per_token_reg<16>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
     else
@@ -225,6 +236,34 @@ q8_status q8_rmsnorm_quant(const q8_bf16* x, int64_t ldx, q8_bf16* residual, int
         return Q8_EUNSUPPORTED;
     return hip_status(launch_rmsnorm_quant(x, ldx, residual, residual ? ldr : 0, gamma, eps, xq,
                                            ldxq, scale_tok, (int)M, (int)K, st(stream)));
+}
+
+q8_status q8_quant_per_group128(const q8_bf16* x, int64_t ldx, int8_t* xq, int64_t ldxq,
+                                float* scale_grp, int64_t M, int64_t K, q8_stream stream) {
+    if (M < 0 || K < 0) return Q8_EINVAL;
+    if (M == 0) return Q8_OK;
+    if (!x || !xq || !scale_grp || K == 0 || ldx < K || ldxq < K) return Q8_EINVAL;
+    if (K % 128 != 0 || M > INT32_MAX / 2 || K > INT32_MAX / 2) return Q8_EUNSUPPORTED;
+    if (ldx % 8 != 0 || ldxq % 8 != 0 || !al(x, 16) || !al(xq, 8) || !al(scale_grp, 4))
+        return Q8_EUNSUPPORTED;
+    const int64_t waves = M * ((K + 511) / 512);
+    if ((waves + 3) / 4 > INT32_MAX) return Q8_EUNSUPPORTED;
+    hipLaunchKernelGGL(quant_per_group128_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                       st(stream), x, ldx, xq, ldxq, scale_grp, (int)M, (int)K);
+    return hip_status(hipGetLastError());
+}
+
+q8_status q8_scaled_mm_group128_act(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
+                                    const float* scale_x, const float* scale_w, q8_bf16* c,
+                                    int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                    q8_stream stream) {
+    q8_status r = check_gemm(a, lda, 16, b, ldb, c, ldc, 8, M, N, K);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_x);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_w);
+    if (r != Q8_OK || M == 0) return r;
+    GemmArgs p{a, lda, b, ldb, scale_x, scale_w, c, ldc, (int)M, (int)N, (int)K};
+    if (!gemm_offsets_fit(p)) return Q8_EUNSUPPORTED;
+    return hip_status(run_gemm_group_act(p, st(stream)));
 }
 
 }  // extern "C"

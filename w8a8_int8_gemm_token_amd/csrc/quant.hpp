@@ -69,25 +69,55 @@ __device__ __forceinline__ v2u codes8(v4u v, const RowScale& q) {
     constexpr float TIE_LO = 0.5f - 0x1p-16f;
     u32 b[8];
     float d[8];
+    float dmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
         const float m = __builtin_fmaf(x, q.r, MAGIC);
         d[e] = __builtin_fmaf(x, q.r, MAGIC - m);  // MAGIC - m = -n exactly
+        dmax = __builtin_fmaxf(dmax, __builtin_fabsf(d[e]));
         b[e] = __float_as_uint(m);
     }
     v2u r;
     r[0] = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | (__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u) << 16);
     r[1] = __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u) | (__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u) << 16);
+    if (dmax > TIE_LO) {  // rare: redo only the near-tie elements by division
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        if (__builtin_fabsf(d[e]) > TIE_LO) {
-            const float x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
-            const u32 sh = 8 * (e & 3);
-            r[e >> 2] = (r[e >> 2] & ~(0xFFu << sh)) | ((u32)(code_of(x, q.s) & 0xFF) << sh);
+        for (int e = 0; e < 8; ++e) {
+            if (__builtin_fabsf(d[e]) > TIE_LO) {
+                const float x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
+                const u32 sh = 8 * (e & 3);
+                r[e >> 2] = (r[e >> 2] & ~(0xFFu << sh)) | ((u32)(code_of(x, q.s) & 0xFF) << sh);
+            }
         }
     }
     return r;
+}
+
+// Per-token-per-group activations: one scale per (row, 128-wide K block),
+// every block quantized like a row of 128 values.  One wave per 512-value
+// span of a row: lane l holds chunk l (8 values), lanes 16g .. 16g+15 form
+// block g of the span, whose absmax takes four lane swaps.  K % 128 == 0;
+// 16-byte aligned x rows, 8-byte aligned xq rows; s [M, K/128] dense.
+__global__ __launch_bounds__(256) void quant_per_group128_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int8_t* __restrict__ xq, int64_t ldxq,
+    float* __restrict__ s, int M, int K) {
+    const int lane = threadIdx.x & 63;
+    const int spans = (K + 511) >> 9;
+    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int m = wave / spans, sp = wave - m * spans;
+    if (m >= M) return;
+    const int c = sp * 64 + lane;  // chunk of 8 values in the row
+    const bool ok = c < (K >> 3);
+    v4u v = v4u{};
+    if (ok) v = reinterpret_cast<const v4u*>(x + (int64_t)m * ldx)[c];
+    float a = mag_to_f32(mag_max8(v2h{0, 0}, v));
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, o, 64));
+    const RowScale q = row_scale(a);
+    if (!ok) return;
+    reinterpret_cast<v2u*>(xq + (int64_t)m * ldxq)[c] = codes8(v, q);
+    if ((lane & 15) == 0) s[(int64_t)m * (K >> 7) + (c >> 4)] = q.s;
 }
 
 // One wave per row; the row stays in registers (NC 16-byte chunks per lane,
