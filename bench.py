@@ -1,8 +1,8 @@
 """Benchmark of the W8A8 INT8 linear layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--secondary decode,group128,group128_act,w8a16,rmsnorm_quant
-                                 | none]
+                    [--secondary decode,group128,group128_act,w8a16,rmsnorm_quant,
+                                 m_sweep | none]
                     [--calibrate-copy]
 
 A step is one pass of the W8A8 hot path over the prefill workload
@@ -260,7 +260,63 @@ def group_act_tops(dev, iters=20):
             "quant_us": qms * 1e3, "quant_GB/s": qbytes / (qms * 1e-3) / 1e9}
 
 
+# The model's Linear shapes (hidden 5120, intermediate 17408): W8A8 modules
+# (q/k/v-like 15360 x 5120, gate/up 17408 x 5120, o-like 5120 x 5120) and
+# the W8A16 down projection (5120 x 17408).
+SWEEP_SHAPES = (("qkv", "w8a8", 15360, 5120), ("gate_up", "w8a8", 17408, 5120),
+                ("o_proj", "w8a8", 5120, 5120), ("down_proj", "w8a16", 5120, 17408))
+SWEEP_M = (1, 2, 4, 8, 16, 32, 64)
+
+
+def m_sweep(dev, reps=10):
+    """Per-call time of each model shape at small token counts (decode,
+    speculative verify, small batches): calls cycle through enough weight
+    copies to exceed 2x the 256 MB last-level cache, captured in a HIP graph.
+    GB/s counts the weights, scales, activations and outputs once."""
+    out = {}
+    for name, kind, N, K in SWEEP_SHAPES:
+        w = synth.weights(synth.WORKLOADS["decode"], 0, N=N, K=K).to(dev)
+        wq, sc = q8.q8_quant_weight(w)
+        del w
+        ncopy = max(2, -(-600_000_000 // (N * K)))
+        wqs = [wq] + [wq.clone() for _ in range(ncopy - 1)]
+        row = {}
+        for M in SWEEP_M:
+            x = synth.activations(synth.WORKLOADS["decode"], 0, M=M, K=K).to(dev)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            if kind == "w8a8":
+                xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+                st = torch.empty((M,), dtype=torch.float32, device=dev)
+
+                def call(wi):
+                    q8.q8_quant_scaled_mm(x, wi, sc, out=y, xq_out=xq, scale_tok_out=st)
+                nbytes = N * K + 4 * N + 2 * M * K + M * K + 4 * M + 2 * M * N
+            else:
+                def call(wi):
+                    q8.w8a16_mm(x, wi, sc, out=y)
+                nbytes = N * K + 4 * N + 2 * M * K + 2 * M * N
+
+            def cycle():
+                for wi in wqs:
+                    call(wi)
+            cycle()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cycle()
+            g.replay()
+            torch.cuda.synchronize()
+            ms = events_time(g.replay, reps) / ncopy
+            row[f"M{M}"] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            del g
+        out[f"{name} {kind} N={N} K={K}"] = row
+        del wqs, wq
+        torch.cuda.empty_cache()
+    return out
+
+
 SECONDARY = {"decode": lambda dev: decode_gbs(dev), "group128": lambda dev: group_tops(dev),
+             "m_sweep": lambda dev: m_sweep(dev),
              "group128_act": lambda dev: group_act_tops(dev),
              "w8a16": lambda dev: w8a16_tflops(dev), "rmsnorm_quant": lambda dev: rmsnorm_quant_gbs(dev)}
 
@@ -272,7 +328,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--secondary", default="decode,group128,group128_act,w8a16,rmsnorm_quant",
+    ap.add_argument("--secondary",
+                    default="decode,group128,group128_act,w8a16,rmsnorm_quant,m_sweep",
                     help="comma list of secondary workloads, or 'none'")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()

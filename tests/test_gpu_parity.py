@@ -342,6 +342,8 @@ def test_quant_scaled_mm_token_counts(M):
     (8, 5120, 5120, 0),    # the decode workload's shape
     (5, 8192, 2048, 32),   # 32 per workgroup: two weight rows per wave
     (7, 2048, 8192, 0),    # the largest K of the one-kernel path
+    (8, 17408, 5120, 0),   # gate/up: 871 workgroups of 20 channels, several per CU
+    (2, 15360, 5120, 16),  # q/k/v-like: three workgroups per CU
     (8, 5120, 8192, 0),    # tile does not fit in LDS: two-kernel path
     (9, 1024, 2048, 0),    # more tokens than the one-kernel path takes
 ])
@@ -527,6 +529,32 @@ def test_w8a16_shapes(M, N, K):
     wq, sc = q8.q8_quant_weight(dev(w))
     y = q8.w8a16_mm(dev(x), wq, sc)
     _check_w8a16(bits(host(y)), bits(x), wq_ref, sc_ref, f"w8a16 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,pad", [(1, 16, 1024, 0), (2, 1040, 3072, 16), (5, 4112, 2048, 0),
+                                       (8, 5120, 17408, 0), (16, 5120, 5120, 32),
+                                       (3, 17408, 5120, 0), (16, 8192, 1024, 0),
+                                       (17, 5120, 3072, 16), (33, 1040, 4096, 0),
+                                       (64, 5120, 17408, 0)])
+def test_w8a16_few_tokens_weight_stream(M, N, K, pad):
+    """M <= 64 with K a multiple of 1024: the weight-streaming kernel (ring
+    of K segments in LDS; 1, 2 or 4 groups of 16 tokens), including the down
+    projection's 5120 x 17408 and several workgroups per CU for large N;
+    strided x, w and y."""
+    say("w8a16 stream", M, N, K, pad)
+    wl = synth.WORKLOADS["w8a16"]
+    xf = synth.activations(wl, 1, M=M, K=K + pad)
+    xf[0] = xf[0] * 50  # a position-outlier row (as in the W8A16 workload)
+    x = xf[:, :K].contiguous()
+    w = synth.weights(wl, 1, N=N, K=K)
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    wq_full = torch.zeros((N, K + pad), dtype=torch.int8, device=DEV)
+    wq_full[:, :K] = dev(torch.from_numpy(wq_ref))
+    yfull = torch.full((M, N + pad), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    y = q8.w8a16_mm(dev(xf)[:, :K], wq_full[:, :K], dev(torch.from_numpy(sc_ref)), out=yfull[:, :N])
+    _check_w8a16(bits(host(y).contiguous()), bits(x), wq_ref, sc_ref, f"w8a16 stream {M}x{N}x{K}")
+    if pad:
+        assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
 
 
 def test_w8a16_full_size_sampled_rows():

@@ -7,10 +7,11 @@
 // weight-bandwidth-bound); per-token dynamic INT8 activations with per-channel
 // INT8 weights ("Qwen3.8-27B -- SmoothQuant + activation-aware GPTQ, W8A8
 // INT8 (v3)", section "Recipe").  One workgroup of 16 waves per CU:
-//  * the grid is ~256 workgroups, workgroup b owning R consecutive output
-//    channels (R a multiple of 4, R <= 32): one workgroup per CU streams the
-//    matrix at the rate of a plain coalesced read, where a grid that is not
-//    a whole number of workgroups per CU leaves a straggler tail;
+//  * workgroup b owns R consecutive output channels (R a multiple of 4, at
+//    most 32): for N up to 256 * 32 the grid is ~256 workgroups, one per
+//    CU, which streams the matrix at the rate of a plain coalesced read (a
+//    grid that is not a whole number of workgroups per CU leaves a
+//    straggler tail); larger N runs in whole waves of 256 (decode_rows);
 //  * waves 0..7 quantize: wave m loads token row m (1 KB per instruction),
 //    takes its absmax with a wave reduction and writes the exact codes of
 //    quant.hpp into an M x K code tile in LDS.  Every workgroup does this for
@@ -60,8 +61,6 @@ struct DecodeArgs {
     int rows;       // R: channels per workgroup (multiple of 4)
 };
 
-// Channels per workgroup for N channels: about N / 256, a multiple of 4.
-inline int decode_rows(int N) { return (((N + 255) / 256) + 3) & ~3; }
 
 // LDS: weight tile (or, after the MFMA phase, the 16 waves' partial tiles),
 // code tile [8][K], token scales.
@@ -230,11 +229,30 @@ inline hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream) {
 // M <= 8 tokens, K a multiple of 1024 up to 8192, ~N/256 channels per
 // workgroup (at most 32) whose tile and the code tile fit in LDS, and 32-bit
 // buffer offsets.
+// Channels per workgroup (a multiple of 4), or 0 if no size fits LDS.  Up
+// to 256 * 32 channels, one workgroup per CU: R = N / 256 rounded up.
+// Beyond that the CUs take several workgroups in turn, and R (at least 16,
+// so the per-workgroup quantization stays small next to its weight stream)
+// minimizes the channels the busiest CU streams: ceil(ceil(N/R) / 256) * R.
+inline int decode_rows(int N, int K) {
+    int rmax = DECODE_MAX_ROWS;
+    while (rmax >= 4 && decode_lds_bytes(K, rmax) > (size_t)DECODE_LDS_BYTES) rmax -= 4;
+    if (rmax < 4) return 0;
+    const int r1 = (((N + 255) / 256) + 3) & ~3;
+    if (r1 <= rmax) return r1;
+    int best = 0;
+    int64_t cost = INT64_MAX;
+    for (int r = rmax; r >= 16 && r >= 4; r -= 4) {
+        const int64_t c = (int64_t)((((int64_t)N + r - 1) / r + 255) / 256) * r;
+        if (c < cost) cost = c, best = r;
+    }
+    return best;
+}
+
 inline bool decode_fits(int M, int N, int K, int64_t ldw) {
     if (M < 1 || M > DECODE_MAX_M || K % 1024 != 0 || K > 8192) return false;
-    const int R = decode_rows(N);
-    if (R > DECODE_MAX_ROWS) return false;
-    if (decode_lds_bytes(K, R) > (size_t)DECODE_LDS_BYTES) return false;
+    const int R = decode_rows(N, K);
+    if (R < 4) return false;
     return (int64_t)R * ldw < ((int64_t)1 << 31);
 }
 

@@ -12,6 +12,7 @@
 #include "decode_fused.hpp"
 #include "norm_quant.hpp"
 #include "w8a16.hpp"
+#include "stream_gemm.hpp"
 
 namespace {
 
@@ -55,6 +56,14 @@ inline q8_status check_scale(const float* s) {
 template <int EPI>
 hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
     if constexpr (EPI == EPI_CHANNEL) {
+        // few tokens: stream the weights once, unless the tiled kernel already
+        // has half a wave of tiles or more (M > 32 with many channels)
+        const bool few = p.M <= 32 || ((p.N + 127) / 128) * ((p.M + 31) / 32) < 128;
+        if (few && sg_fits(p.M, p.N, p.K, p.ldw, SG_MAX_M)) {
+            const StreamArgs q{p.x, p.ldx, p.w, p.ldw, p.s_tok, p.s_w, static_cast<uint16_t*>(p.c), p.ldc,
+                               p.M, p.N, p.K, 0, 0};
+            return launch_stream<true>(q, s);
+        }
         const SkinnyArgs k{p.x, p.ldx, p.w, p.ldw, p.s_tok, p.s_w, static_cast<uint16_t*>(p.c), p.ldc,
                            p.M, p.N, p.K};
         if (skinny_fits(k)) return launch_skinny(k, s);
@@ -158,6 +167,10 @@ q8_status w8a16_mm(const q8_bf16* x, int64_t ldx, const int8_t* w, int64_t ldw,
     q8_status r = check_gemm(x, ldx, 8, w, ldw, c, ldc, 8, M, N, K);
     if (r == Q8_OK && M > 0) r = check_scale(scale_ch);
     if (r != Q8_OK || M == 0) return r;
+    if (sg_fits((int)M, (int)N, (int)K, ldw, SG_MAX_M)) {  // few tokens: stream the weights once
+        const StreamArgs q{x, ldx, w, ldw, nullptr, scale_ch, c, ldc, (int)M, (int)N, (int)K, 0, 0};
+        return hip_status(launch_stream<false>(q, st(stream)));
+    }
     W8A16Args p{x, ldx, w, ldw, scale_ch, c, ldc, (int)M, (int)N, (int)K};
     if (M <= 64) return hip_status(launch_w8a16<32, 128, 64, 1, 4, 8>(p, st(stream)));
     return hip_status(launch_w8a16<128, 128, 64, 2, 2, 8>(p, st(stream)));
@@ -176,7 +189,7 @@ q8_status q8_quant_scaled_mm(const q8_bf16* x, int64_t ldx, const int8_t* b, int
     hipStream_t s = st(stream);
     if (decode_fits((int)M, (int)N, (int)K, ldb)) {
         const DecodeArgs d{x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok,
-                           (int)M, (int)N, (int)K, decode_rows((int)N)};
+                           (int)M, (int)N, (int)K, decode_rows((int)N, (int)K)};
         return hip_status(launch_decode(d, s));
     }
     hipError_t e = run_quant(x, ldx, xq, K, scale_tok, (int)M, (int)K, s);

@@ -1,0 +1,328 @@
+// stream_gemm.hpp -- GEMMs for a few tokens (M <= 64), which stream the
+// weight matrix once and are bound by HBM bandwidth:
+//   I8 (W8A8):  y[m,n] = bf16_rne(((float)sum_k xq[m,k]*w[n,k] * s_tok[m]) * s_ch[n])
+//               exact int32 sums of the per-token codes
+//   bf16 (W8A16): y[m,n] = bf16_rne(s_ch[n] * sum_k x[m,k] * bf16(w[n,k]))
+// "Qwen3.8-27B -- SmoothQuant + activation-aware GPTQ, W8A8 INT8 (v3)",
+// sections "Recipe" (the W8A8 and W8A16 module groups) and "Results"
+// (single-stream decode); "Qwen3.8-27B-INT8-W8A8", section "Throughput"
+// (decode is weight-bandwidth-bound); "lued/Qwen3.8-27B-INT8-W8A16-MTP",
+// section "Why W8A16 on Ampere" (weights rebuilt in 16 bits).
+//
+// One 16-wave workgroup per CU owns R consecutive channels and all of K:
+//  * waves 8..15 load: rows d, d+8, ... of the tile, K segment by K segment
+//    (1 KB of one row per buffer_load_dwordx4 ... lds), into a ring of 3
+//    segment slots in LDS; after each
+//    segment lands (vmcnt) a wave increments that segment's `ready`
+//    counter, and before reusing a slot it waits until all 8 multiplying
+//    waves have released it (`freed`);
+//  * waves 0..7 multiply: wave c takes its share of the K blocks of every
+//    segment, reads the activation fragments (codes or bf16) straight from
+//    global memory (the M x K block stays in L2) for MG groups of 16 tokens,
+//    and runs 16x16 MFMAs (v_mfma_i32_16x16x64_i8, or
+//    v_mfma_f32_16x16x32_bf16 on weights converted to bf16 as they are read:
+//    exact, |q| <= 128) on both 16-row tiles;
+//  * the 8 partial tiles are summed in LDS (exact int32 for I8), and waves
+//    0 .. 2*MG-1 apply the epilogue.
+// Progress: a loading wave signals segment s before it waits on any
+// counter, and a multiplying wave releases segment s before it waits on
+// segment s+1, so every wait is on an event that needs no further waiting;
+// the polls are bounded all the same.  Rows and tokens past the ends repeat
+// the last valid one; their outputs are never stored.
+// Segment slot layout: [R][1024] bytes, 16-byte unit u of row r stored at
+// unit u ^ (r & 15), so the fragment reads of 16 rows are conflict-free.
+#pragma once
+
+#include <type_traits>
+
+#include "decode_fused.hpp"
+#include "gemm_i8.hpp"
+#include "w8a16.hpp"
+
+namespace q8 {
+
+constexpr int SG_MAX_M = 64;
+constexpr int SG_SEG = 1024;       // K per segment
+constexpr int SG_MAX_SEG = 128;    // K <= 131072
+constexpr int SG_MAX_ROWS = 32;
+constexpr int SG_RING_BYTES = 150 * 1024;
+constexpr int SG_NBUF = 3;
+
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+
+struct StreamArgs {
+    const void* x;  // [M, ldx]: int8 codes (I8) or bf16
+    int64_t ldx;
+    const int8_t* w;  // [N, ldw] int8
+    int64_t ldw;
+    const float* s_tok;  // [M] (I8 only)
+    const float* s_ch;   // [N]
+    uint16_t* c;         // [M, ldc] bf16
+    int64_t ldc;
+    int M, N, K;
+    int rows;  // channels per workgroup (multiple of 4, <= 32)
+    int nbuf;  // segment slots in the ring
+};
+
+// Three slots: a deeper ring issues most of a short K at once, and the
+// loading waves then stall at issue the way a whole-tile load does
+// (measured slower for K = 5120; no faster for K = 17408).
+inline int sg_nbuf(int rows) {
+    const int n = SG_RING_BYTES / (rows * SG_SEG);
+    return n < SG_NBUF ? n : SG_NBUF;
+}
+__host__ __device__ inline size_t sg_lds_bytes(int rows, int nbuf, int mg) {
+    const size_t ring = (size_t)nbuf * rows * SG_SEG;
+    const size_t red = (size_t)2 * mg * 8 * 64 * 16;  // partial tiles of the 8 multiplying waves
+    return ring > red ? ring : red;
+}
+
+// Spin (short sleeps) until an LDS counter reaches target; bounded (about
+// 2^20 polls, tens of milliseconds) so a broken invariant gives wrong
+// output, not a hung device.  The poll is a ds_read written out (and waited
+// for inside the same statement): a compiler-visible LDS read would first
+// drain the loading waves' in-flight direct loads.
+__device__ __forceinline__ void sg_wait_ge(int* c, int target) {
+    const uint32_t a = (uint32_t)(uintptr_t)(Q8_LDS int*)c;
+    for (int it = 0; it < (1 << 20); ++it) {
+        int v;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+        if (__builtin_amdgcn_readfirstlane(v) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
+// Increment an LDS counter (one lane).  A returnless ds_add written out, so
+// that the compiler does not drain this wave's direct-to-LDS loads first (it
+// cannot tell the counter from their targets); the caller has waited for
+// exactly the loads the signal announces.
+__device__ __forceinline__ void sg_signal(int* c) {
+    const uint32_t a = (uint32_t)(uintptr_t)(Q8_LDS int*)c;
+    asm volatile("ds_add_u32 %0, %1" ::"v"(a), "v"(1) : "memory");
+}
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 63]; other counters untouched.
+__device__ __forceinline__ void sg_wait_vm(int n) {
+    switch (n) {
+#define Q8_W(k) case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
+#define Q8_W8(b) Q8_W(b) Q8_W(b + 1) Q8_W(b + 2) Q8_W(b + 3) Q8_W(b + 4) Q8_W(b + 5) Q8_W(b + 6) Q8_W(b + 7)
+        Q8_W8(0) Q8_W8(8) Q8_W8(16) Q8_W8(24) Q8_W8(32) Q8_W8(40) Q8_W8(48) Q8_W8(56)
+#undef Q8_W8
+#undef Q8_W
+        default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
+    }
+}
+
+__device__ __forceinline__ v8bf16 i8x8_to_bf16x8(v2u raw) {
+    const v2u lo = i8x4_to_bf16x4(raw[0]), hi = i8x4_to_bf16x4(raw[1]);
+    return __builtin_bit_cast(v8bf16, v4u{lo[0], lo[1], hi[0], hi[1]});
+}
+
+template <bool I8, int MG>
+__global__ __launch_bounds__(1024) void stream_gemm_kernel(StreamArgs p) {
+    // K blocks per MFMA: 64 (int8) or 32 (bf16); per segment and wave
+    constexpr int KB = I8 ? 64 : 32;
+    constexpr int BPW = SG_SEG / KB / 8;
+    typedef typename std::conditional<I8, v4i, v4f>::type acc_t;
+    extern __shared__ __attribute__((aligned(1024))) int8_t lds[];
+    __shared__ int ready[SG_MAX_SEG];  // loading waves done with segment s (8 = landed)
+    __shared__ int freed[SG_MAX_SEG];  // multiplying waves done with segment s (8 = free)
+
+    const int M = p.M, K = p.K, nseg = K / SG_SEG, nbuf = p.nbuf;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int R = p.rows;
+    const int n0 = blockIdx.x * R;
+    const int rows = min(R, p.N - n0);
+    const int tok = lane & 15, kg = lane >> 4;
+    const int slot_bytes = R * SG_SEG;
+
+    // epilogue operands: wave w < 2*MG writes tile t = w / MG, token group
+    // g = w % MG: token 16g + tok, channels n0 + 16t + 4kg + e
+    const int et = wid / MG, eg = wid % MG;
+    const int em = 16 * eg + tok;
+    const int ch = n0 + 16 * et + 4 * kg;
+    const bool writer = wid < 2 * MG && em < M && 16 * et + 4 * kg < rows;
+    v4f sc = v4f{};
+    float st = 1.0f;
+    if (writer) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[e] = p.s_ch[ch + e];
+        if constexpr (I8) st = p.s_tok[em];
+    }
+    for (int i = threadIdx.x; i < nseg; i += 1024) ready[i] = freed[i] = 0;
+    wait_lgkm0();
+    block_barrier();
+
+    acc_t acc[2][MG];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int g = 0; g < MG; ++g) acc[t][g] = acc_t{};
+    if (wid < 8) {
+        // ---- multiplying wave: K blocks BPW*wid .. BPW*wid + BPW-1 of
+        // every segment
+        const int r0 = min(tok, rows - 1), r1 = min(16 + tok, rows - 1);
+        const int8_t* xb[MG];
+#pragma unroll
+        for (int g = 0; g < MG; ++g) {
+            const int tc = min(16 * g + tok, M - 1);
+            xb[g] = static_cast<const int8_t*>(p.x) + ((int64_t)tc * p.ldx + (I8 ? 16 : 8) * kg) * (I8 ? 1 : 2);
+        }
+        // activation fragments (16 bytes per lane: 16 codes or 8 bf16) are
+        // loaded before the wait on the segment when they fit in registers
+        constexpr bool PRE = BPW * MG <= 8;
+        auto bload = [&](int sg, int j, int g) __attribute__((always_inline)) {
+            return *reinterpret_cast<const v4u*>(xb[g] + (int64_t)(sg * SG_SEG + KB * (BPW * wid + j)) *
+                                                             (I8 ? 1 : 2));
+        };
+        for (int sg = 0; sg < nseg; ++sg) {
+            v4u b[PRE ? BPW : 1][MG];
+            if constexpr (PRE) {
+#pragma unroll
+                for (int j = 0; j < BPW; ++j)
+#pragma unroll
+                    for (int g = 0; g < MG; ++g) b[j][g] = bload(sg, j, g);
+            }
+            sg_wait_ge(&ready[sg], 8);
+            const int8_t* slot = lds + (sg % nbuf) * slot_bytes;
+#pragma unroll
+            for (int jj = 0; jj < BPW; ++jj) {
+                const int j = PRE ? jj : 0;
+                if constexpr (!PRE) {
+#pragma unroll
+                    for (int g = 0; g < MG; ++g) b[0][g] = bload(sg, jj, g);
+                }
+                const int o = KB * (BPW * wid + jj) + (I8 ? 16 : 8) * kg;  // byte of K in the row
+                const int u = o >> 4;
+                if constexpr (I8) {
+                    const v4i a0 = *reinterpret_cast<const v4i*>(slot + r0 * SG_SEG + ((u ^ (r0 & 15)) << 4));
+                    const v4i a1 = *reinterpret_cast<const v4i*>(slot + r1 * SG_SEG + ((u ^ (r1 & 15)) << 4));
+#pragma unroll
+                    for (int g = 0; g < MG; ++g) {
+                        const v4i bg = __builtin_bit_cast(v4i, b[j][g]);
+                        acc[0][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bg, acc[0][g], 0, 0, 0);
+                        acc[1][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bg, acc[1][g], 0, 0, 0);
+                    }
+                } else {
+                    const int h = (o >> 3) & 1;
+                    const v8bf16 a0 = i8x8_to_bf16x8(
+                        *reinterpret_cast<const v2u*>(slot + r0 * SG_SEG + ((u ^ (r0 & 15)) << 4) + (h << 3)));
+                    const v8bf16 a1 = i8x8_to_bf16x8(
+                        *reinterpret_cast<const v2u*>(slot + r1 * SG_SEG + ((u ^ (r1 & 15)) << 4) + (h << 3)));
+#pragma unroll
+                    for (int g = 0; g < MG; ++g) {
+                        const v8bf16 bg = __builtin_bit_cast(v8bf16, b[j][g]);
+                        acc[0][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bg, acc[0][g], 0, 0, 0);
+                        acc[1][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bg, acc[1][g], 0, 0, 0);
+                    }
+                }
+            }
+            wait_lgkm0();  // this wave's reads of the slot are done
+            if (lane == 0) sg_signal(&freed[sg]);
+        }
+    } else {
+        // ---- loading wave d: rows d + 8 j, segment by segment
+        const int d = wid - 8;
+        const int cnt = rows > d ? (rows - d + 7) / 8 : 0;
+        const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + (int64_t)n0 * p.ldw,
+                                                    (uint32_t)((int64_t)rows * p.ldw));
+        auto issue = [&](int sg) __attribute__((always_inline)) {
+            int8_t* slot = lds + (sg % nbuf) * slot_bytes;
+            for (int j = 0; j < cnt; ++j) {
+                const int r = d + 8 * j;
+                const int voff = r * (int)p.ldw + sg * SG_SEG + ((lane ^ (r & 15)) << 4);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (Q8_LDS void*)(slot + r * SG_SEG), 16, voff,
+                                                         0, 0, 0);
+            }
+        };
+        const int first = min(nbuf, nseg);
+        for (int sg = 0; sg < first; ++sg) issue(sg);
+        int issued = first;
+        for (int sg = 0; sg < nseg; ++sg) {
+            sg_wait_vm((issued - 1 - sg) * cnt);  // segments 0..sg landed
+            if (lane == 0) sg_signal(&ready[sg]);
+            if (issued < nseg) {
+                sg_wait_ge(&freed[sg], 8);  // slot of sg free again
+                issue(issued);
+                ++issued;
+            }
+        }
+    }
+
+    // ---- sum the 8 multiplying waves' partial tiles, epilogue
+    block_barrier();  // every wave is done with the ring
+    acc_t* red = reinterpret_cast<acc_t*>(lds);
+    if (wid < 8) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int g = 0; g < MG; ++g) red[((t * MG + g) * 8 + wid) * 64 + lane] = acc[t][g];
+    }
+    wait_lgkm0();
+    block_barrier();
+    if (!writer) return;
+    acc_t s = acc_t{};
+#pragma unroll
+    for (int w = 0; w < 8; ++w) s += red[(wid * 8 + w) * 64 + lane];
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (I8) {
+            const float u = (float)s[e] * st;
+            y[e] = u * sc[e];
+        } else {
+            y[e] = s[e] * sc[e];
+        }
+    }
+    v2u o;
+    o[0] = pack_bf16x2(y[0], y[1]);
+    o[1] = pack_bf16x2(y[2], y[3]);
+    *reinterpret_cast<v2u*>(p.c + (int64_t)em * p.ldc + ch) = o;
+}
+
+// Channels per workgroup: N / 256 rounded up to a multiple of 4 when that is
+// at most 32 (one workgroup per CU); otherwise the size in [16, 32] that
+// minimizes the channels the busiest CU streams over whole waves of 256.
+inline int sg_rows(int N) {
+    const int r1 = (((N + 255) / 256) + 3) & ~3;
+    if (r1 <= SG_MAX_ROWS) return r1;
+    int best = SG_MAX_ROWS;
+    int64_t cost = INT64_MAX;
+    for (int r = SG_MAX_ROWS; r >= 16; r -= 4) {
+        const int64_t c = (int64_t)((((int64_t)N + r - 1) / r + 255) / 256) * r;
+        if (c < cost) cost = c, best = r;
+    }
+    return best;
+}
+
+// M <= max_m, K a multiple of 1024, 32-bit buffer offsets for the tile.
+inline bool sg_fits(int M, int N, int K, int64_t ldw, int max_m) {
+    if (M < 1 || M > max_m || K % SG_SEG != 0 || K / SG_SEG > SG_MAX_SEG) return false;
+    return (int64_t)sg_rows(N) * ldw < ((int64_t)1 << 31);
+}
+
+template <bool I8, int MG>
+inline hipError_t launch_stream_t(const StreamArgs& p, hipStream_t stream) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&stream_gemm_kernel<I8, MG>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, SG_RING_BYTES);
+    if (attr != hipSuccess) return attr;
+    const int grid = (p.N + p.rows - 1) / p.rows;
+    hipLaunchKernelGGL((stream_gemm_kernel<I8, MG>), dim3(grid), dim3(1024),
+                       sg_lds_bytes(p.rows, p.nbuf, MG), stream, p);
+    return hipGetLastError();
+}
+
+// Fills rows and nbuf from N, then launches for the token count.
+template <bool I8>
+inline hipError_t launch_stream(StreamArgs p, hipStream_t stream) {
+    p.rows = sg_rows(p.N);
+    p.nbuf = sg_nbuf(p.rows);
+    if (p.M <= 16) return launch_stream_t<I8, 1>(p, stream);
+    if (p.M <= 32) return launch_stream_t<I8, 2>(p, stream);
+    return launch_stream_t<I8, 4>(p, stream);
+}
+
+}  // namespace q8
