@@ -8,7 +8,6 @@
 
 #include "gemm_i8.hpp"
 #include "quant.hpp"
-#include "skinny.hpp"
 #include "decode_fused.hpp"
 #include "norm_quant.hpp"
 #include "w8a16.hpp"
@@ -64,9 +63,6 @@ hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
                                p.M, p.N, p.K, 0, 0};
             return launch_stream<true>(q, s);
         }
-        const SkinnyArgs k{p.x, p.ldx, p.w, p.ldw, p.s_tok, p.s_w, static_cast<uint16_t*>(p.c), p.ldc,
-                           p.M, p.N, p.K};
-        if (skinny_fits(k)) return launch_skinny(k, s);
     }
     if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
     const int64_t big_tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
