@@ -55,6 +55,11 @@ def _load():
             "q8o_f32_to_bf16": ([F], ctypes.c_uint16),
             "q8o_bf16_to_f32": ([ctypes.c_uint16], F),
             "q8o_quant_per_token": ([P, I, I, P, P], None),
+            "q8o_e4m3_value": ([ctypes.c_uint8], ctypes.c_double),
+            "q8o_e4m3_rne": ([F], ctypes.c_uint8),
+            "q8o_quant_fp8_per_group128": ([P, I, I, P, P], ctypes.c_int),
+            "q8o_quant_weight_fp8_block128": ([P, I, I, P, P], ctypes.c_int),
+            "q8o_fp8_block_mm": ([P, P, P, P, I, I, I, P, P], ctypes.c_int),
             "q8o_quant_weight": ([P, I, I, I, P, P], ctypes.c_int),
             "q8o_mm_i32": ([P, P, I, I, I, P], ctypes.c_int),
             "q8o_epilogue_channel": ([P, P, P, I, I, P], None),
@@ -267,3 +272,59 @@ def scaled_mm_group128_act(a, b, s_x, s_w) -> np.ndarray:
     if _load().q8o_scaled_mm_group128_act(_p(a), _p(b), _p(s_x), _p(s_w), M, N, K, _p(y)) != 0:
         raise ValueError("oracle: K must be a multiple of 128")
     return y
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one E4M3 byte (OCP FP8, bias 7, max 448; NaN for 0x7F/0xFF)."""
+    return _load().q8o_e4m3_value(int(code) & 0xFF)
+
+
+def e4m3_rne(v: float) -> int:
+    """E4M3 byte nearest to the fp32 value v (ties to even, saturating at 448)."""
+    return int(_load().q8o_e4m3_rne(float(np.float32(v))))
+
+
+def quant_fp8_per_group128(x_bf16):
+    """Per-token-per-128-group FP8 quant: -> (xq E4M3 bytes uint8 [M,K],
+    s_x fp32 [M,K/128])."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    xq = np.empty((M, K), np.uint8)
+    s = np.empty((M, K // 128), np.float32)
+    if _load().q8o_quant_fp8_per_group128(_p(x), M, K, _p(xq), _p(s)) != 0:
+        raise ValueError("oracle: K must be a multiple of 128")
+    return xq, s
+
+
+def quant_weight_fp8_block128(w_f32):
+    """FP8 [128,128] block weights: -> (wq E4M3 bytes uint8 [N,K],
+    s_w fp32 [N/128, K/128])."""
+    w = _c(w_f32, np.float32)
+    N, K = w.shape
+    wq = np.empty((N, K), np.uint8)
+    s = np.empty((N // 128, K // 128), np.float32)
+    if _load().q8o_quant_weight_fp8_block128(_p(w), N, K, _p(wq), _p(s)) != 0:
+        raise ValueError("oracle: N and K must be multiples of 128")
+    return wq, s
+
+
+def fp8_block_mm(a, b, s_x, s_w, with_mag: bool = False):
+    """FP8 block-scaled GEMM in fp64: a [M,K], b [N,K] E4M3 bytes, s_x
+    [M,K/128], s_w [N/128,K/128] -> y float64 [M,N] (and the magnitude sum
+    used for error bounds when with_mag)."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    s_x = _c(s_x, np.float32)
+    s_w = _c(s_w, np.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K and s_x.shape == (M, K // 128) and s_w.shape == (N // 128, K // 128)
+    y = np.empty((M, N), np.float64)
+    mag = np.empty((M, N), np.float64) if with_mag else None
+    rc = _load().q8o_fp8_block_mm(_p(a), _p(b), _p(s_x), _p(s_w), M, N, K, _p(y),
+                                  None if mag is None else _p(mag))
+    if rc == -1:
+        raise ValueError("oracle: N and K must be multiples of 128")
+    if rc == -2:
+        raise ValueError("oracle: NaN E4M3 code in an operand")
+    return (y, mag) if with_mag else y

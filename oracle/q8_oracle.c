@@ -48,6 +48,15 @@
  *  - the smoothing scale is s_j = min(cap, sqrtf(max_m |X[m,j]|)) with cap 16
  *    (exponent 0.5 on the plain column maximum), X' = bf16_rne(X / s_j) and
  *    W' = fl32(W * s_j).
+ *  - FP8 block W8A8 ([P3] "Recipe": FP8 block-scaled [128,128] weights with
+ *    dynamic per-group activations; its "KV cache" section scales E4M3 by
+ *    amax/448): E4M3 is the OCP 8-bit float with 4 exponent bits (bias 7)
+ *    and 3 mantissa bits, largest finite value 448; a scale is
+ *    fl32(absmax / 448) over the block (0 for an all-zero block, whose codes
+ *    are all +0); a code is the E4M3 value nearest to the correctly rounded
+ *    fp32 quotient x/s, ties to the even mantissa, magnitudes from 448 up
+ *    saturating to 448, the sign always kept (so -0 and tiny negatives give
+ *    the -0 code).
  */
 #include <fenv.h>
 #include <math.h>
@@ -460,6 +469,176 @@ int q8o_scaled_mm_group128_act(const int8_t *a, const int8_t *b,
                 acc = fmaf((float)p, sc, acc);
             }
             y[m * N + n] = q8o_f32_to_bf16(acc);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------- FP8 block W8A8 -- */
+
+/* Value of an E4M3 code, by its definition: sign bit 7, exponent field
+ * E = bits 6..3 (bias 7), mantissa m = bits 2..0.  E == 0: m * 2^-9
+ * (subnormal); E == 15 with m == 7: NaN; otherwise (1 + m/8) * 2^(E-7).
+ * [P3 "Recipe": FP8 block weights; its "KV cache" section: E4M3, 448] */
+double q8o_e4m3_value(uint8_t c)
+{
+    const int E = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (E == 15 && m == 7)
+        return NAN;
+    if (E == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp((double)(8 + m), E - 10);
+    return (c & 0x80) ? -v : v;
+}
+
+/* E4M3 code of v: the nearest value of the non-negative codes 0x00..0x7E
+ * (found by bisection: their values increase with the code), ties to the
+ * code with an even mantissa, |v| >= 448 saturating to 0x7E, sign bit from
+ * v.  NaN gives 0x7F. */
+uint8_t q8o_e4m3_rne(float v)
+{
+    if (isnan(v))
+        return 0x7F;
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const double a = fabs((double)v);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    int lo = 0, hi = 0x7E; /* largest c with value(c) <= a */
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (q8o_e4m3_value((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    int c = lo;
+    const double below = a - q8o_e4m3_value((uint8_t)c);       /* exact */
+    const double above = q8o_e4m3_value((uint8_t)(c + 1)) - a; /* exact */
+    if (below > above || (below == above && (c & 1)))
+        c += 1;
+    return sign | (uint8_t)c;
+}
+
+/* Absmax scale for E4M3: fl32(absmax / 448); 0 for a zero span. */
+static float absmax_scale_e4m3(const float *v, int64_t n)
+{
+    float a = 0.0f;
+    for (int64_t k = 0; k < n; ++k) {
+        float m = fabsf(v[k]);
+        if (m > a)
+            a = m;
+    }
+    return a / 448.0f;
+}
+
+/* E4M3 code of x under scale s: the code of the correctly rounded quotient;
+ * s == 0 (an all-zero span) gives +0. */
+static uint8_t e4m3_code_of(float x, float s)
+{
+    if (s == 0.0f)
+        return 0x00;
+    return q8o_e4m3_rne(x / s);
+}
+
+/* Dynamic per-token-per-group FP8 activations: every 128-wide K block of a
+ * bf16 row gets s_x[m][g] = fl32(absmax / 448) and E4M3 codes of x / s.
+ * x: [M][K] bf16 bits; xq: [M][K] E4M3 bytes; s_x: [M][K/128].
+ * [P3 "Recipe": dynamic per-group activations, dimensions divisible by 128]
+ * Returns -1 if K is not a multiple of 128. */
+int q8o_quant_fp8_per_group128(const uint16_t *x, int64_t M, int64_t K,
+                               uint8_t *xq, float *s_x)
+{
+    if (K % 128 != 0)
+        return -1;
+    const int64_t G = K / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float v[128];
+        for (int64_t g = 0; g < G; ++g) {
+            for (int k = 0; k < 128; ++k)
+                v[k] = bf16_bits_to_f32(x[m * K + g * 128 + k]);
+            const float sc = absmax_scale_e4m3(v, 128);
+            s_x[m * G + g] = sc;
+            for (int k = 0; k < 128; ++k)
+                xq[m * K + g * 128 + k] = e4m3_code_of(v[k], sc);
+        }
+    }
+    return 0;
+}
+
+/* Offline FP8 block weights: one scale per [128,128] block of the fp32
+ * weight W [N][K], s_w[nb][g] = fl32(absmax over rows 128nb.. and columns
+ * 128g.. / 448), row-major [N/128][K/128]; wq [N][K] E4M3 codes.
+ * [P3 "Recipe": FP8 block-scaled [128,128] weights, scales from the weight
+ * tensor alone]  Returns -1 unless N and K are multiples of 128. */
+int q8o_quant_weight_fp8_block128(const float *w, int64_t N, int64_t K,
+                                  uint8_t *wq, float *s_w)
+{
+    if (N % 128 != 0 || K % 128 != 0)
+        return -1;
+    const int64_t NB = N / 128, G = K / 128;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t nb = 0; nb < NB; ++nb) {
+        for (int64_t g = 0; g < G; ++g) {
+            float a = 0.0f;
+            for (int64_t n = nb * 128; n < nb * 128 + 128; ++n)
+                for (int64_t k = g * 128; k < g * 128 + 128; ++k) {
+                    float m = fabsf(w[n * K + k]);
+                    if (m > a)
+                        a = m;
+                }
+            const float sc = a / 448.0f;
+            s_w[nb * G + g] = sc;
+            for (int64_t n = nb * 128; n < nb * 128 + 128; ++n)
+                for (int64_t k = g * 128; k < g * 128 + 128; ++k)
+                    wq[n * K + k] = e4m3_code_of(w[n * K + k], sc);
+        }
+    }
+    return 0;
+}
+
+/* FP8 block-scaled GEMM, the value the method defines:
+ *   y[m][n] = sum_g s_x[m][g] * s_w[n/128][g] * P_g,
+ *   P_g     = sum_{k in [128g, 128g+128)} e4m3(a[m][k]) * e4m3(b[n][k]).
+ * P_g is exact in fp64 (each product of two E4M3 values is a multiple of
+ * 2^-18 below 2^18, so a block sum needs at most 44 bits); the scale
+ * products and the sum over g are fp64.  mag (if not NULL) receives
+ * sum_g |s_x * s_w| * sum_k |e4m3(a) * e4m3(b)|, the size that error bounds
+ * of fp32 accumulation are stated in.  Returns -1 unless N and K are
+ * multiples of 128, -2 if a NaN code is met. */
+int q8o_fp8_block_mm(const uint8_t *a, const uint8_t *b, const float *s_x,
+                     const float *s_w, int64_t M, int64_t N, int64_t K,
+                     double *y, double *mag)
+{
+    if (N % 128 != 0 || K % 128 != 0)
+        return -1;
+    const int64_t G = K / 128;
+    for (int64_t i = 0; i < M * K; ++i)
+        if (isnan(q8o_e4m3_value(a[i])))
+            return -2;
+    for (int64_t i = 0; i < N * K; ++i)
+        if (isnan(q8o_e4m3_value(b[i])))
+            return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, am = 0.0;
+            for (int64_t g = 0; g < G; ++g) {
+                double p = 0.0, pa = 0.0;
+                for (int64_t k = g * 128; k < g * 128 + 128; ++k) {
+                    const double t = q8o_e4m3_value(a[m * K + k]) * q8o_e4m3_value(b[n * K + k]);
+                    p += t;
+                    pa += fabs(t);
+                }
+                const double sc = (double)s_x[m * G + g] * (double)s_w[(n / 128) * G + g];
+                acc += sc * p;
+                am += fabs(sc) * pa;
+            }
+            y[m * N + n] = acc;
+            if (mag)
+                mag[m * N + n] = am;
         }
     }
     return 0;

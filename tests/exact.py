@@ -103,3 +103,13 @@ def sqrt_fp32(r: Fraction) -> Fraction:
         return d
     even = (struct.unpack("<I", struct.pack("<f", float(c)))[0] & 1) == 0
     return c if even else d
+
+
+def e4m3(r: Fraction) -> Fraction:
+    """Nearest E4M3 value (4 significant bits, normal exponents -6 .. 8,
+    subnormal quantum 2**-9; ties to even), magnitudes beyond the largest
+    finite value 448 saturating to it."""
+    v = round_to_format(r, 4, -6, 8)
+    if abs(v) > 448:
+        return Fraction(448) if v > 0 else Fraction(-448)
+    return v
