@@ -45,6 +45,7 @@ import w8a8_int8_gemm_token_amd as q8  # noqa: E402
 METRIC = "W8A8 quant+GEMM TOPS at M=8192,K=5120,N=15360; % INT8 MFMA peak; M=8 GB/s"
 PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, published
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 
 
@@ -260,6 +261,39 @@ def group_act_tops(dev, iters=20):
             "quant_us": qms * 1e3, "quant_GB/s": qbytes / (qms * 1e-3) / 1e9}
 
 
+def fp8_block_tflops(dev, iters=10):
+    """FP8 block W8A8 at the prefill shape: per-token-per-group E4M3
+    activation quant + the [128,128] block-scaled FP8 GEMM.  GEMM, quant and
+    the whole step are timed separately with events."""
+    wl = synth.WORKLOADS["fp8_block"]
+    x = synth.activations(wl, 0).to(dev)
+    w = synth.weights(wl, 0).to(dev)
+    xo, wo, _ = q8.q8_smooth_fold(x, w)
+    del x, w
+    wq, sw = q8.q8_quant_weight_fp8_block128(wo)
+    del wo
+    xq, sx = q8.q8_quant_fp8_per_group128(xo)
+    y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
+    g = lambda: q8.q8_fp8_block_scaled_mm(xq, wq, sx, sw, out=y)  # noqa: E731
+    qf = lambda: q8.q8_quant_fp8_per_group128(xo, out=xq, scale_out=sx)  # noqa: E731
+
+    def step():
+        qf()
+        g()
+    for _ in range(2):
+        step()
+    gms = events_time(g, iters)
+    qms = events_time(qf, iters)
+    sms = events_time(step, iters)
+    flops = 2.0 * wl.M * wl.N * wl.K
+    t = flops / (gms * 1e-3) / 1e12
+    qbytes = 3 * wl.M * wl.K + 4 * wl.M * (wl.K // 128)
+    return {"gemm_us": gms * 1e3, "TFLOPS": t, "frac_fp8_peak": t / PEAK_FP8_TFLOPS,
+            "quant_us": qms * 1e3, "quant_GB/s": qbytes / (qms * 1e-3) / 1e9,
+            "step_us": sms * 1e3, "step_TFLOPS": flops / (sms * 1e-3) / 1e12,
+            "shape": [wl.M, wl.N, wl.K]}
+
+
 # The model's Linear shapes (hidden 5120, intermediate 17408): W8A8 modules
 # (q/k/v-like 15360 x 5120, gate/up 17408 x 5120, o-like 5120 x 5120) and
 # the W8A16 down projection (5120 x 17408).
@@ -318,7 +352,8 @@ def m_sweep(dev, reps=10):
 SECONDARY = {"decode": lambda dev: decode_gbs(dev), "group128": lambda dev: group_tops(dev),
              "m_sweep": lambda dev: m_sweep(dev),
              "group128_act": lambda dev: group_act_tops(dev),
-             "w8a16": lambda dev: w8a16_tflops(dev), "rmsnorm_quant": lambda dev: rmsnorm_quant_gbs(dev)}
+             "w8a16": lambda dev: w8a16_tflops(dev), "rmsnorm_quant": lambda dev: rmsnorm_quant_gbs(dev),
+             "fp8_block": lambda dev: fp8_block_tflops(dev)}
 
 
 def main():
@@ -329,7 +364,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary",
-                    default="decode,group128,group128_act,w8a16,rmsnorm_quant,m_sweep",
+                    default="decode,group128,group128_act,w8a16,rmsnorm_quant,fp8_block,m_sweep",
                     help="comma list of secondary workloads, or 'none'")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()

@@ -61,6 +61,10 @@ WORKLOADS = {
                       w8a16=True),
     "group128": Workload("group128", 5, 4096, 5120, 5120, "cols", 30.0, 0.02,
                          group=128),
+    # FP8 block W8A8 at the prefill shape; the smoothing fold stands in for
+    # the FP8 page's smoothing pre-pass
+    "fp8_block": Workload("fp8_block", 6, 8192, 5120, 15360, "cols", 30.0, 0.02,
+                          smooth=True),
 }
 
 _TAG_X, _TAG_W, _TAG_OUT = 1, 2, 3

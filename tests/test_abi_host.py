@@ -118,6 +118,29 @@ def test_per_group_entry_points_validation(lib):
     assert ga(A, 256, B, 256, S, S, C, 128, 16, 128, 192, None) == EUNSUP
 
 
+def test_fp8_entry_points_validation(lib):
+    qf = lib.q8_quant_fp8_per_group128
+    assert qf(A, 256, B, 256, S, 0, 256, None) == OK
+    assert qf(None, 256, B, 256, S, 4, 256, None) == EINVAL
+    assert qf(A, 256, B, 256, S, 4, 192, None) == EUNSUP     # K % 128
+    assert qf(A, 260, B, 256, S, 4, 256, None) == EUNSUP     # ldx % 8
+    assert qf(A, 256, B + 4, 256, S, 4, 256, None) == EUNSUP  # xq misaligned
+    qw = lib.q8_quant_weight_fp8_block128
+    assert qw(A, 256, B, 256, S, 0, 256, None) == OK
+    assert qw(A, 256, B, 256, None, 128, 256, None) == EINVAL
+    assert qw(A, 200, B, 256, S, 128, 256, None) == EINVAL   # ldw < K
+    assert qw(A, 256, B, 256, S, 64, 256, None) == EUNSUP    # N % 128
+    assert qw(A, 256, B, 256, S, 128, 192, None) == EUNSUP   # K % 128
+    assert qw(A + 2, 256, B, 256, S, 128, 256, None) == EUNSUP
+    fm = lib.q8_fp8_block_scaled_mm
+    assert fm(A, 256, B, 256, S, S, C, 128, 0, 128, 256, None) == OK
+    assert fm(A, 256, B, 256, None, S, C, 128, 16, 128, 256, None) == EINVAL
+    assert fm(A, 256, B, 256, S, None, C, 128, 16, 128, 256, None) == EINVAL
+    assert fm(A, 256, B, 256, S, S, C, 128, 16, 128, 192, None) == EUNSUP   # K % 128
+    assert fm(A, 256, B, 256, S, S, C, 128, 16, 64, 256, None) == EUNSUP    # N % 128
+    assert fm(A, 256, B, 256, S, S, C, 128, 16, 144, 256, None) == EINVAL   # ldc < N
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     x = torch.zeros((4, 256), dtype=torch.bfloat16)

@@ -1,0 +1,226 @@
+"""GPU parity of the FP8 block W8A8 path against the CPU oracle.
+
+Codes and scales of both quantizers must be bit-exact.  The GEMM runs on the
+FP8 matrix cores (v_mfma_f32_32x32x64_f8f6f4), which do not sum products in
+fp32: measured on this hardware, each group of 8 consecutive products of a
+K block is aligned to the group's largest product with 13 fractional bits
+and truncated; the group sums are then combined exactly enough not to show
+in the same measurement.  The GEMM is therefore checked against the
+oracle's exact (fp64) value with the bound of that arithmetic:
+  |y - ref| <= 2^-8 |ref|                        (bf16 rounding of the result)
+             + sum_g |s_x s_w| sum_groups sum_k min(|p_k|, 2^-12 max_group |p|)
+                                                 (truncation inside a group,
+                                                  with a factor 2 of slack on
+                                                  the grid)
+             + 1.01 (K/128 + 130) 2^-24 mag      (fp32 sums, scale product and
+                                                  one fused multiply-add per
+                                                  block)
+where mag = sum_g |s_x s_w| sum_k |a b|.  A wrong scale, block or operand
+gives errors of the size of ref itself.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w8a8_int8_gemm_token_amd as q8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def dev(t):
+    if isinstance(t, np.ndarray):
+        t = torch.from_numpy(np.ascontiguousarray(t))
+    return t.to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu()
+
+
+def bits(t_bf16_cpu):
+    return synth.bf16_bits(t_bf16_cpu)
+
+
+def u8(t_fp8):
+    return host(t_fp8).view(torch.uint8).numpy()
+
+
+_E4M3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def group8_truncation_bound(xq, wq, sx, sw):
+    """sum_g |s_x s_w| sum over groups of 8 consecutive k of
+    sum_k min(|p_k|, 2^-12 max_group |p|), p_k = a[m,k] b[n,k]."""
+    M, K = xq.shape
+    N, G = wq.shape[0], K // 128
+    A, W = _E4M3[xq], _E4M3[wq]
+    out = np.empty((M, N))
+    step = max(1, 4_000_000 // (N * K))
+    for m0 in range(0, M, step):
+        P = np.abs(A[m0:m0 + step, None, :] * W[None, :, :]).reshape(-1, N, K // 8, 8)
+        t = np.minimum(P, P.max(axis=3, keepdims=True) * 2.0 ** -12).sum(axis=3)
+        t = t.reshape(-1, N, G, 16).sum(axis=3)
+        sc = np.abs(sx[m0:m0 + step, None, :].astype(np.float64) * sw[np.arange(N) // 128][None].astype(np.float64))
+        out[m0:m0 + step] = (t * sc).sum(axis=2)
+    return out
+
+
+def check_fp8_mm(y_gpu, xq, wq, sx, sw, what, rows=None):
+    K = xq.shape[1]
+    y_ref, mag = oracle.fp8_block_mm(xq, wq, sx, sw, with_mag=True)
+    y = host(y_gpu).float().numpy().astype(np.float64)
+    if rows is not None:
+        y = y[rows]
+    err = np.abs(y - y_ref)
+    bound = (2.0 ** -8 * np.abs(y_ref) + group8_truncation_bound(xq, wq, sx, sw)
+             + 1.01 * (K / 128 + 130) * 2.0 ** -24 * mag)
+    ratio = (err / np.maximum(bound, 1e-300)).max() if err.size else 0.0
+    rel = np.linalg.norm(y - y_ref, axis=1) / np.maximum(np.linalg.norm(y_ref, axis=1), 1e-30)
+    say(f"{what}: max err/bound {ratio:.3f}, max row rel {rel.max() if rel.size else 0:.2e}")
+    assert np.all(err <= bound), what
+    assert rel.size == 0 or rel.max() <= 1e-2, what
+
+
+@pytest.mark.parametrize("M,K,pad", [(1, 128, 0), (3, 640, 8), (8, 5120, 0), (130, 1024, 16),
+                                     (33, 4096, 0)])
+def test_fp8_quant_per_group128(M, K, pad):
+    say("fp8 quant per group128", M, K, pad)
+    xf, _ = synth.custom(M, K + pad, 16, seed=M + 7 * K, outlier_cols=max(1, K // 100))
+    x = xf[:, :K].contiguous()
+    x[M // 2, :128] = 0              # an all-zero block
+    x[0, K - 128:] = -0.0            # a block of negative zeros
+    xf[:, :K] = x
+    xq_ref, s_ref = oracle.quant_fp8_per_group128(bits(x))
+    xq, s = q8.q8_quant_fp8_per_group128(dev(xf)[:, :K])
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(u8(xq), xq_ref)
+
+
+def test_fp8_quant_near_halfway_subnormal_range_and_tiny_scales():
+    """Blocks built from bf16 values whose quotient and reciprocal product
+    round to different E4M3 codes, values that land in the E4M3 subnormal
+    range, exact halfway quotients, and blocks with subnormal scales."""
+    allbf = (np.arange(0, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    rng = np.random.default_rng(3)
+    blocks = []
+    for _ in range(400):
+        a = allbf[rng.integers(0x3F00, 0x4400)]
+        s = np.float32(np.float32(a) / np.float32(448.0))
+        xs = allbf[allbf <= a]
+        q_div = torch.from_numpy((xs / s).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        q_rec = torch.from_numpy((xs * (np.float32(1.0) / s)).astype(np.float32)).to(
+            torch.float8_e4m3fn).view(torch.uint8).numpy()
+        idx = np.nonzero(q_div != q_rec)[0][:60]
+        low = xs[(xs / s >= 2.0 ** -11) & (xs / s < 2.0 ** -5)][:40]  # E4M3 subnormal range
+        blk = np.concatenate([[a], xs[idx], -xs[idx], low, -low])[:128]
+        blocks.append(np.pad(blk, (0, 128 - len(blk))).astype(np.float32))
+    # exact halfway quotients: absmax 448 gives s = 1, values at code midpoints
+    vals = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    mids = mids[torch.from_numpy(mids).to(torch.bfloat16).float().numpy() == mids]
+    for i in range(0, len(mids), 120):
+        blk = np.concatenate([[448.0], mids[i:i + 120]])
+        blocks.append(np.pad(blk, (0, 128 - len(blk))).astype(np.float32))
+    for amax in (1e-38, 2e-37, 1e-40):  # subnormal and near-subnormal scales
+        blk = np.zeros(128, np.float32)
+        blk[:7] = np.array([1, 0.5, -0.25, 0.75, 0.3, -1, 0.01], np.float32) * amax
+        blocks.append(blk)
+    nb = len(blocks) + (-len(blocks)) % 4
+    mat = np.zeros((nb, 128), np.float32)
+    mat[:len(blocks)] = np.stack(blocks)
+    x = torch.from_numpy(mat.reshape(nb // 4, 512)).to(torch.bfloat16)
+    xq_ref, s_ref = oracle.quant_fp8_per_group128(bits(x))
+    xq, s = q8.q8_quant_fp8_per_group128(dev(x))
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(u8(xq), xq_ref)
+
+
+@pytest.mark.parametrize("N,K", [(128, 128), (384, 640), (256, 5120)])
+def test_fp8_quant_weight_block128(N, K):
+    say("fp8 weight blocks", N, K)
+    _, w = synth.custom(4, K, N, seed=N + K)
+    w = w.numpy().copy()
+    w[:128, :128] *= 100.0  # blocks of different magnitudes
+    w[N - 1, K - 1] = 1.0   # a block maximum in a corner
+    wq_ref, s_ref = oracle.quant_weight_fp8_block128(w)
+    wq, s = q8.q8_quant_weight_fp8_block128(dev(w))
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(u8(wq), wq_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (8, 256, 1024), (64, 384, 640),
+                                   (65, 256, 1152), (130, 512, 384), (200, 384, 2048),
+                                   (257, 128, 256)])
+def test_fp8_block_scaled_mm_shapes(M, N, K):
+    say("fp8 block mm", M, N, K)
+    x, w = synth.custom(M, K, N, seed=M * 5 + N, outlier_cols=3)
+    xq, sx = q8.q8_quant_fp8_per_group128(dev(x))
+    wq, sw = q8.q8_quant_weight_fp8_block128(dev(w))
+    xq_h, sx_h, wq_h, sw_h = u8(xq), host(sx).numpy(), u8(wq), host(sw).numpy()
+    xq_ref, sx_ref = oracle.quant_fp8_per_group128(bits(x))
+    np.testing.assert_array_equal(xq_h, xq_ref)
+    y = q8.q8_fp8_block_scaled_mm(xq, wq, sx, sw)
+    check_fp8_mm(y, xq_h, wq_h, sx_h, sw_h, f"fp8 {M}x{N}x{K}")
+
+
+def test_fp8_block_scaled_mm_strided_and_zero_rows():
+    M, N, K = 70, 256, 768
+    x, w = synth.custom(M, K, N, seed=91, outlier_cols=2)
+    x[5] = 0
+    xq, sx = q8.q8_quant_fp8_per_group128(dev(x))
+    wq, sw = q8.q8_quant_weight_fp8_block128(dev(w))
+    a = torch.zeros((M, K + 64), dtype=torch.float8_e4m3fn, device=DEV)
+    a[:, :K] = xq
+    b = torch.zeros((N, K + 32), dtype=torch.float8_e4m3fn, device=DEV)
+    b[:, :K] = wq
+    out = torch.full((M, N + 8), 7.0, dtype=torch.bfloat16, device=DEV)
+    q8.q8_fp8_block_scaled_mm(a[:, :K], b[:, :K], sx, sw, out=out[:, :N])
+    o = host(out)
+    assert (o[:, N:] == 7.0).all()
+    assert (o[5, :N] == 0).all()
+    check_fp8_mm(out[:, :N], u8(xq), u8(wq), host(sx).numpy(), host(sw).numpy(), "fp8 strided")
+
+
+def test_fp8_full_size_sampled_rows():
+    """The FP8 workload at its full size (M=8192, N=15360, K=5120), in the
+    launch configuration the benchmark times; sampled rows against the
+    oracle, codes and scales checked whole."""
+    wl = synth.WORKLOADS["fp8_block"]
+    say("fp8 full size")
+    x = synth.activations(wl, 0)
+    w = synth.weights(wl, 0)
+    xo, wo, _ = q8.q8_smooth_fold(dev(x), dev(w))
+    del w
+    xq, sx = q8.q8_quant_fp8_per_group128(xo)
+    wq, sw = q8.q8_quant_weight_fp8_block128(wo)
+    del wo
+    xq_ref, sx_ref = oracle.quant_fp8_per_group128(bits(host(xo)))
+    np.testing.assert_array_equal(host(sx).numpy(), sx_ref)
+    np.testing.assert_array_equal(u8(xq), xq_ref)
+    y = q8.q8_fp8_block_scaled_mm(xq, wq, sx, sw)
+    rows = np.array([0, 1, 255, 256, 4095, 8190, 8191, 1234])
+    check_fp8_mm(y, xq_ref[rows], u8(wq), sx_ref[rows], host(sw).numpy(), "fp8 sampled rows",
+                 rows=rows)
+
+
+def test_fp8_repeat_calls_bitwise_identical():
+    M, N, K = 300, 512, 1024
+    x, w = synth.custom(M, K, N, seed=5, outlier_cols=3)
+    xq, sx = q8.q8_quant_fp8_per_group128(dev(x))
+    wq, sw = q8.q8_quant_weight_fp8_block128(dev(w))
+    y1 = host(q8.q8_fp8_block_scaled_mm(xq, wq, sx, sw))
+    y2 = host(q8.q8_fp8_block_scaled_mm(xq, wq, sx, sw))
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))

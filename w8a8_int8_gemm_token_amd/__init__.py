@@ -15,6 +15,12 @@ Functions mirror the C entry points:
   q8_mm_i32(a, b) -> int32 acc
   q8_quant_weight(w, group=None) -> (wq, scale)
   q8_smooth_fold(x, w, cap=16.0) -> (x', w', s)
+  q8_rmsnorm_quant(x, gamma, eps, residual=None) -> (xq, scale_tok)
+  q8_quant_per_group128(x) -> (xq, scale_grp)
+  q8_scaled_mm_group128_act(xq, wq, scale_x, scale_w) -> y
+  q8_quant_fp8_per_group128(x) -> (xq float8_e4m3fn, scale_grp)
+  q8_quant_weight_fp8_block128(w) -> (wq float8_e4m3fn, scale_blk)
+  q8_fp8_block_scaled_mm(xq, wq, scale_x, scale_w) -> y
 Each also accepts preallocated outputs (``out=`` ...) so callers control
 allocation; the library itself never allocates.
 """
@@ -29,7 +35,8 @@ __all__ = [
     "Q8Error", "lib_path", "load", "q8_quant_per_token", "q8_scaled_mm",
     "q8_scaled_mm_group128", "w8a16_mm", "q8_quant_scaled_mm", "q8_mm_i32",
     "q8_quant_weight", "q8_smooth_fold", "q8_rmsnorm_quant", "q8_quant_per_group128",
-    "q8_scaled_mm_group128_act", "EXPORTS", "MAX_K",
+    "q8_scaled_mm_group128_act", "q8_quant_fp8_per_group128", "q8_quant_weight_fp8_block128",
+    "q8_fp8_block_scaled_mm", "EXPORTS", "MAX_K",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,7 +45,8 @@ EXPORTS = (
     "q8_status_str", "q8_quant_per_token", "q8_scaled_mm",
     "q8_scaled_mm_group128", "w8a16_mm", "q8_quant_scaled_mm", "q8_mm_i32",
     "q8_quant_weight", "q8_smooth_fold", "q8_rmsnorm_quant", "q8_quant_per_group128",
-    "q8_scaled_mm_group128_act",
+    "q8_scaled_mm_group128_act", "q8_quant_fp8_per_group128", "q8_quant_weight_fp8_block128",
+    "q8_fp8_block_scaled_mm",
 )
 _STATUS = {0: "Q8_OK", 1: "Q8_EINVAL", 2: "Q8_EUNSUPPORTED", 3: "Q8_EHIP"}
 
@@ -82,6 +90,9 @@ def load():
         "q8_rmsnorm_quant": ([P, I, P, I, P, F, P, I, P, I, I, P], S),
         "q8_quant_per_group128": ([P, I, P, I, P, I, I, P], S),
         "q8_scaled_mm_group128_act": ([P, I, P, I, P, P, P, I, I, I, I, P], S),
+        "q8_quant_fp8_per_group128": ([P, I, P, I, P, I, I, P], S),
+        "q8_quant_weight_fp8_block128": ([P, I, P, I, P, I, I, P], S),
+        "q8_fp8_block_scaled_mm": ([P, I, P, I, P, P, P, I, I, I, I, P], S),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -145,9 +156,9 @@ def _gemm_out(M, N, device, out, dtype=torch.bfloat16):
     return c
 
 
-def _mk(a, b, a_dtype=torch.int8):
+def _mk(a, b, a_dtype=torch.int8, b_dtype=torch.int8):
     _dev(a, a_dtype, "a", 2)
-    _dev(b, torch.int8, "b", 2)
+    _dev(b, b_dtype, "b", 2)
     if a.shape[1] != b.shape[1]:
         raise ValueError(f"K mismatch: a {tuple(a.shape)} vs b {tuple(b.shape)}")
     return a.shape[0], b.shape[0], a.shape[1]
@@ -311,6 +322,60 @@ def q8_scaled_mm_group128_act(a, b, scale_x, scale_w, out=None):
         raise ValueError("block scales must be contiguous")
     c = _gemm_out(M, N, a.device, out)
     _check("q8_scaled_mm_group128_act", load().q8_scaled_mm_group128_act(
+        _ptr(a), _ld(a), _ptr(b), _ld(b), _ptr(scale_x), _ptr(scale_w), _ptr(c), _ld(c),
+        M, N, K, _stream(a.device)))
+    return c
+
+
+FP8 = torch.float8_e4m3fn
+
+
+def q8_quant_fp8_per_group128(x, out=None, scale_out=None):
+    """Per-token-per-128-group FP8: x bf16 [M,K] -> (xq float8_e4m3fn [M,K],
+    scale fp32 [M, K/128]), scale = absmax/448."""
+    _dev(x, torch.bfloat16, "x", 2)
+    M, K = x.shape
+    xq = out if out is not None else torch.empty((M, K), dtype=FP8, device=x.device)
+    s = scale_out if scale_out is not None else torch.empty((M, K // 128), dtype=torch.float32,
+                                                           device=x.device)
+    _dev(xq, FP8, "out", 2)
+    _dev(s, torch.float32, "scale_out", 2)
+    if not s.is_contiguous():
+        raise ValueError("scale_out must be contiguous")
+    _check("q8_quant_fp8_per_group128", load().q8_quant_fp8_per_group128(
+        _ptr(x), _ld(x), _ptr(xq), _ld(xq), _ptr(s), M, K, _stream(x.device)))
+    return xq, s
+
+
+def q8_quant_weight_fp8_block128(w, out=None, scale_out=None):
+    """FP8 [128,128] block weights: w fp32 [N,K] -> (wq float8_e4m3fn [N,K],
+    scale fp32 [N/128, K/128])."""
+    _dev(w, torch.float32, "w", 2)
+    N, K = w.shape
+    wq = out if out is not None else torch.empty((N, K), dtype=FP8, device=w.device)
+    s = scale_out if scale_out is not None else torch.empty((N // 128, K // 128), dtype=torch.float32,
+                                                           device=w.device)
+    _dev(wq, FP8, "out", 2)
+    _dev(s, torch.float32, "scale_out", 2)
+    if not s.is_contiguous():
+        raise ValueError("scale_out must be contiguous")
+    _check("q8_quant_weight_fp8_block128", load().q8_quant_weight_fp8_block128(
+        _ptr(w), _ld(w), _ptr(wq), _ld(wq), _ptr(s), N, K, _stream(w.device)))
+    return wq, s
+
+
+def q8_fp8_block_scaled_mm(a, b, scale_x, scale_w, out=None):
+    """bf16 [M,N] = sum_g scale_x[m,g] * scale_w[n/128,g] * (a_g @ b_g^T) on
+    FP8 matrix cores (fp32 block sums folded in ascending g)."""
+    M, N, K = _mk(a, b, a_dtype=FP8, b_dtype=FP8)
+    _dev(scale_x, torch.float32, "scale_x", 2)
+    _dev(scale_w, torch.float32, "scale_w", 2)
+    if tuple(scale_x.shape) != (M, K // 128) or tuple(scale_w.shape) != (N // 128, K // 128):
+        raise ValueError("block scale shapes must be [M, K/128] and [N/128, K/128]")
+    if not scale_x.is_contiguous() or not scale_w.is_contiguous():
+        raise ValueError("block scales must be contiguous")
+    c = _gemm_out(M, N, a.device, out)
+    _check("q8_fp8_block_scaled_mm", load().q8_fp8_block_scaled_mm(
         _ptr(a), _ld(a), _ptr(b), _ld(b), _ptr(scale_x), _ptr(scale_w), _ptr(c), _ld(c),
         M, N, K, _stream(a.device)))
     return c

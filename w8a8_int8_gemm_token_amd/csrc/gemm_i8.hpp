@@ -9,11 +9,18 @@
 //   EPI_GROUP_ACT: as EPI_GROUP with one activation scale per (token,
 //                128-wide K block) as well: f = fmaf((float)p_g,
 //                fl(s_x[m,g] * s_w[n,g]), f); y = bf16_rne(f)
+//   EPI_FP8_BLOCK: FP8 (E4M3) operands on v_mfma_f32_32x32x64_f8f6f4, one
+//                activation scale per (token, 128-wide K block) and one
+//                weight scale per [128,128] block: each block's fp32 partial
+//                P_g is folded as f = fmaf(P_g, fl(s_x[m,g] * s_w[n/128,g]),
+//                f) in ascending g; y = bf16_rne(f)
 //   EPI_I32:     the raw int32 acc
 // "Qwen3.8-27B -- SmoothQuant + activation-aware GPTQ, W8A8 INT8 (v3)",
 // sections "Recipe" and "Serving" (INT8 x INT8 with per-token x per-channel
 // scales, bf16 out); "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", "Quantization
-// details" (one weight scale per 128-wide K block).
+// details" (one weight scale per 128-wide K block); "Qwen3.8-27B -- FP8
+// block + AWQ", "Recipe" (FP8 [128,128] block weights, dynamic per-group
+// activations).
 //
 // Tiling: a workgroup owns a BM (tokens) x BN (channels) output tile; WM x WN
 // waves each own a (BM/WM) x (BN/WN) register tile of 32x32 MFMA blocks.  The
@@ -49,21 +56,23 @@
 // MFMAs of this stage drain.  One barrier per stage.
 #pragma once
 
+#include <type_traits>
+
 #include "q8_device.hpp"
 
 #define Q8_LDS __attribute__((address_space(3)))
 
 namespace q8 {
 
-enum { EPI_I32 = 0, EPI_CHANNEL = 1, EPI_GROUP = 2, EPI_GROUP_ACT = 3 };
+enum { EPI_I32 = 0, EPI_CHANNEL = 1, EPI_GROUP = 2, EPI_GROUP_ACT = 3, EPI_FP8_BLOCK = 4 };
 
 struct GemmArgs {
     const int8_t* x;  // activations (tokens) [M, ldx]
     int64_t ldx;
     const int8_t* w;  // weights (channels) [N, ldw]
     int64_t ldw;
-    const float* s_tok;  // [M]; EPI_GROUP_ACT: [M, K/128] per (token, block)
-    const float* s_w;    // [N] per channel, or [N, K/128] per group
+    const float* s_tok;  // [M]; EPI_GROUP_ACT, EPI_FP8_BLOCK: [M, K/128] per (token, block)
+    const float* s_w;    // [N] per channel, [N, K/128] per group, or [N/128, K/128] per block
     void* c;             // [M, ldc] bf16 bits, or int32
     int64_t ldc;
     int M, N, K;
@@ -116,18 +125,24 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     constexpr int XIW = BM / 8 / NW, WIW = BN / 8 / NW;  // 8-row loads per wave and stage
+    constexpr bool F8 = EPI == EPI_FP8_BLOCK;
     constexpr bool GRP = EPI == EPI_GROUP || EPI == EPI_GROUP_ACT;
-    constexpr bool ACT = EPI == EPI_GROUP_ACT;
+    constexpr bool FOLD = GRP || F8;                       // per-block fp32 fold
+    constexpr bool ACT = EPI == EPI_GROUP_ACT || F8;       // per-(token, block) scales
     constexpr int SGI = GRP ? BN / 64 : 0;             // 64-scale weight loads per stage
     constexpr int SXI = ACT ? (BM + 63) / 64 : 0;      // 64-scale activation loads per stage
+    constexpr int XOFF = GRP ? BN : 0;                 // activation scales in a stage's block
     constexpr int LPS = XIW + WIW + (SGI + NW - 1) / NW + (SXI + NW - 1) / NW;
-    constexpr int LSN = GRP ? BN + (ACT ? SXI * 64 : 0) : 4;  // scale floats per stage
-    constexpr int NR = TM + TN;  // fragment reads per sub-step
+    constexpr int LSN = FOLD ? XOFF + SXI * 64 : 4;    // scale floats per stage
+    constexpr int NR = (F8 ? 2 : 1) * (TM + TN);  // fragment reads (16 bytes) per sub-step
     constexpr int NM = TM * TN;  // MFMAs per sub-step
     constexpr int NM0 = NM / 2;  // MFMAs of sub-step 3 before the hand-over
     static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "tile shape");
     static_assert(XIW * 8 * NW == BM && WIW * 8 * NW == BN, "load split");
     static_assert(!GRP || BN % 64 == 0, "group scales load 64 at a time");
+    static_assert(!F8 || (WTN <= 128 && 128 % WTN == 0), "a wave's channels share one weight block");
+    using AccT = std::conditional_t<F8, v16f, v16i>;
+    using FragT = std::conditional_t<F8, v8i, v4i>;
 
     __shared__ __attribute__((aligned(1024))) int8_t lx0[BM * BK];
     __shared__ __attribute__((aligned(1024))) int8_t lx1[BM * BK];
@@ -198,57 +213,95 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
             for (int i = 0; i < (SXI + NW - 1) / NW; ++i) {
                 const int j = wid + i * NW;
                 if (j < SXI)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(sxr, (Q8_LDS void*)(bs + BN + j * 64), 4,
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(sxr, (Q8_LDS void*)(bs + XOFF + j * 64), 4,
                                                              svx, j * 64 * G * 4 + kt * 4, 0, 0);
             }
         }
     };
 
-    // ---- fragment reads: sub-step kk of 32-row block b sits at
-    // base[kk] + b*32*BK (f is the same for rows r and r + 32b)
+    // ---- fragment reads: 16-byte read i of 32-row block b sits at
+    // base[i] + b*32*BK (f is the same for rows r and r + 32b).  INT8: read
+    // i is sub-step i's fragment, chunk 2i + hi of the row.  FP8: sub-step kk
+    // takes 32 bytes per lane, chunks 4kk + 2hi and 4kk + 2hi + 1 (reads 2kk
+    // and 2kk + 1); both operands use the same chunks, so every product
+    // pairs equal k.
     int wbase[4], xbase[4];
     {
         const int rw0 = wn * WTN + (lane & 31), rx0 = wm * WTM + (lane & 31);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            wbase[kk] = rw0 * BK + (((kk * 2 + hi) ^ lds_swizzle(rw0)) << 4);
-            xbase[kk] = rx0 * BK + (((kk * 2 + hi) ^ lds_swizzle(rx0)) << 4);
+        for (int i = 0; i < 4; ++i) {
+            const int ch = F8 ? (i >> 1) * 4 + hi * 2 + (i & 1) : i * 2 + hi;
+            wbase[i] = rw0 * BK + ((ch ^ lds_swizzle(rw0)) << 4);
+            xbase[i] = rx0 * BK + ((ch ^ lds_swizzle(rx0)) << 4);
         }
     }
 
-    v16i acc[TM][TN];
-    v16f facc[GRP ? TM : 1][GRP ? TN : 1];
+    AccT acc[TM][TN];
+    v16f facc[FOLD ? TM : 1][FOLD ? TN : 1];
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b) acc[a][b] = v16i{};
-    if constexpr (GRP) {
+        for (int b = 0; b < TN; ++b) acc[a][b] = AccT{};
+    if constexpr (FOLD) {
 #pragma unroll
         for (int a = 0; a < TM; ++a)
 #pragma unroll
             for (int b = 0; b < TN; ++b) facc[a][b] = v16f{};
     }
-    v4i fw[2][TN], fx[2][TM];
+    FragT fw[2][TN], fx[2][TM];
 
     auto read = [&](int set, int kk, const int8_t* bx, const int8_t* bw) __attribute__((always_inline)) {
+        if constexpr (F8) {
 #pragma unroll
-        for (int b = 0; b < TN; ++b)
-            fw[set][b] = *reinterpret_cast<const v4i*>(bw + wbase[kk] + b * 32 * BK);
+            for (int b = 0; b < TN; ++b) {
+                const v4i lo = *reinterpret_cast<const v4i*>(bw + wbase[2 * kk] + b * 32 * BK);
+                const v4i hi8 = *reinterpret_cast<const v4i*>(bw + wbase[2 * kk + 1] + b * 32 * BK);
+                fw[set][b] = v8i{lo[0], lo[1], lo[2], lo[3], hi8[0], hi8[1], hi8[2], hi8[3]};
+            }
 #pragma unroll
-        for (int a = 0; a < TM; ++a)
-            fx[set][a] = *reinterpret_cast<const v4i*>(bx + xbase[kk] + a * 32 * BK);
+            for (int a = 0; a < TM; ++a) {
+                const v4i lo = *reinterpret_cast<const v4i*>(bx + xbase[2 * kk] + a * 32 * BK);
+                const v4i hi8 = *reinterpret_cast<const v4i*>(bx + xbase[2 * kk + 1] + a * 32 * BK);
+                fx[set][a] = v8i{lo[0], lo[1], lo[2], lo[3], hi8[0], hi8[1], hi8[2], hi8[3]};
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+                fw[set][b] = *reinterpret_cast<const v4i*>(bw + wbase[kk] + b * 32 * BK);
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+                fx[set][a] = *reinterpret_cast<const v4i*>(bx + xbase[kk] + a * 32 * BK);
+        }
     };
     auto mfma = [&](int set, int from, int to) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = from; t < to; ++t) {
             const int a = t / TN, b = t % TN;
-            acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[set][b], fx[set][a], acc[a][b], 0, 0, 0);
+            if constexpr (F8)  // A and B in E4M3 (format 0), no block exponents
+                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[set][b], fx[set][a], acc[a][b],
+                                                                            0, 0, 0, 0, 0, 0);
+            else
+                acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[set][b], fx[set][a], acc[a][b], 0, 0, 0);
         }
     };
     // EPI_GROUP: fold the stage's 128-wide block sums into the fp32
     // accumulators (the stage is group kt; groups arrive in ascending order)
-    auto fold = [&](const float* bs) __attribute__((always_inline)) {
-        if constexpr (GRP) {
+    auto fold = [&](const float* bs, int kt) __attribute__((always_inline)) {
+        if constexpr (F8) {
+            // a wave's WTN channels lie in one 128-channel weight block
+            const float sw = p.s_w[(int64_t)((n0 + wn * WTN) >> 7) * G + kt];
+            float f[TM];
+#pragma unroll
+            for (int a = 0; a < TM; ++a) f[a] = bs[wm * WTM + a * 32 + (lane & 31)] * sw;
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) facc[a][b][e] = __builtin_fmaf(acc[a][b][e], f[a], facc[a][b][e]);
+                    acc[a][b] = AccT{};
+                }
+        } else if constexpr (GRP) {
             float sx[TM];  // EPI_GROUP_ACT: block scale of this lane's token in block a
 #pragma unroll
             for (int a = 0; a < TM; ++a) sx[a] = ACT ? bs[BN + wm * WTM + a * 32 + (lane & 31)] : 1.0f;
@@ -277,42 +330,60 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     // fall outside the resource and read as zero, so the loop needs no tail.
     auto stage = [&](int kt, const int8_t* cx, const int8_t* cw, const float* cs, int8_t* nx,
                      int8_t* nw, float* ns) __attribute__((always_inline)) {
-        // sub-step 0: MFMAs on set 0; next stage's direct loads; set 1 <- kk 1
-        issue(kt + 1, nx, nw, ns);
-        read(1, 1, cx, cw);
-        mfma(0, 0, NM);
-        interleave<NM, NR, LPS>();
-        __builtin_amdgcn_sched_barrier(0);
-        // sub-step 1
-        read(0, 2, cx, cw);
-        mfma(1, 0, NM);
-        interleave<NM, NR, 0>();
-        __builtin_amdgcn_sched_barrier(0);
-        // sub-step 2
-        read(1, 3, cx, cw);
-        mfma(0, 0, NM);
-        interleave<NM, NR, 0>();
-        __builtin_amdgcn_sched_barrier(0);
-        // sub-step 3: part of the MFMAs, then the stage hand-over
-        if constexpr (GRP) {
-            // the group fold reads this stage's scales: do it before the
-            // hand-over frees the stage
+        if constexpr (F8) {
+            // two 64-deep sub-steps: MFMAs on set 0 with the next stage's
+            // direct loads and set 1 <- kk 1 behind them; then set 1, the
+            // fold of this stage's block, and the hand-over
+            issue(kt + 1, nx, nw, ns);
+            read(1, 1, cx, cw);
+            mfma(0, 0, NM);
+            interleave<NM, NR, LPS>();
+            __builtin_amdgcn_sched_barrier(0);
             mfma(1, 0, NM);
-            fold(cs);
+            fold(cs, kt);
             __builtin_amdgcn_sched_barrier(0);
             wait_vm_lgkm0<0>();
             block_barrier();
             read(0, 0, nx, nw);
             __builtin_amdgcn_sched_barrier(0);
         } else {
-            mfma(1, 0, NM0);
+            // sub-step 0: MFMAs on set 0; next stage's direct loads; set 1 <- kk 1
+            issue(kt + 1, nx, nw, ns);
+            read(1, 1, cx, cw);
+            mfma(0, 0, NM);
+            interleave<NM, NR, LPS>();
             __builtin_amdgcn_sched_barrier(0);
-            wait_vm_lgkm0<0>();
-            block_barrier();
-            read(0, 0, nx, nw);
-            mfma(1, NM0, NM);
-            interleave<NM - NM0, NR, 0>();
+            // sub-step 1
+            read(0, 2, cx, cw);
+            mfma(1, 0, NM);
+            interleave<NM, NR, 0>();
             __builtin_amdgcn_sched_barrier(0);
+            // sub-step 2
+            read(1, 3, cx, cw);
+            mfma(0, 0, NM);
+            interleave<NM, NR, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+            // sub-step 3: part of the MFMAs, then the stage hand-over
+            if constexpr (GRP) {
+                // the group fold reads this stage's scales: do it before the
+                // hand-over frees the stage
+                mfma(1, 0, NM);
+                fold(cs, kt);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vm_lgkm0<0>();
+                block_barrier();
+                read(0, 0, nx, nw);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                mfma(1, 0, NM0);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vm_lgkm0<0>();
+                block_barrier();
+                read(0, 0, nx, nw);
+                mfma(1, NM0, NM);
+                interleave<NM - NM0, NR, 0>();
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
@@ -333,7 +404,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     for (int a = 0; a < TM; ++a) {
         const int j = m0 + wm * WTM + a * 32 + (lane & 31);  // token
         if (j >= M) continue;
-        const float st = (EPI == EPI_I32 || EPI == EPI_GROUP_ACT) ? 0.0f : p.s_tok[j];
+        const float st = (EPI == EPI_CHANNEL || EPI == EPI_GROUP) ? p.s_tok[j] : 0.0f;
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
 #pragma unroll
@@ -342,10 +413,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
                 if (ch >= N) continue;
                 if constexpr (EPI == EPI_I32) {
                     v4i o;
-                    o[0] = acc[a][b][g * 4 + 0];
-                    o[1] = acc[a][b][g * 4 + 1];
-                    o[2] = acc[a][b][g * 4 + 2];
-                    o[3] = acc[a][b][g * 4 + 3];
+                    o[0] = (int)acc[a][b][g * 4 + 0];
+                    o[1] = (int)acc[a][b][g * 4 + 1];
+                    o[2] = (int)acc[a][b][g * 4 + 2];
+                    o[3] = (int)acc[a][b][g * 4 + 3];
                     *reinterpret_cast<v4i*>(static_cast<int32_t*>(p.c) + (int64_t)j * p.ldc + ch) = o;
                 } else {
                     float v[4];

@@ -12,6 +12,7 @@
 #include "norm_quant.hpp"
 #include "w8a16.hpp"
 #include "stream_gemm.hpp"
+#include "fp8.hpp"
 
 namespace {
 
@@ -73,6 +74,11 @@ hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
 hipError_t run_gemm_group_act(const GemmArgs& p, hipStream_t s) {
     if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI_GROUP_ACT, 8>(p, s);
     return launch_gemm_i8<128, 128, 2, 2, EPI_GROUP_ACT, 8>(p, s);
+}
+
+hipError_t run_gemm_fp8_block(const GemmArgs& p, hipStream_t s) {
+    if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI_FP8_BLOCK, 8>(p, s);
+    return launch_gemm_i8<128, 128, 2, 2, EPI_FP8_BLOCK, 8>(p, s);
 }
 
 hipError_t run_gemm_group(const GemmArgs& p, hipStream_t s) {
@@ -273,6 +279,49 @@ q8_status q8_scaled_mm_group128_act(const int8_t* a, int64_t lda, const int8_t* 
     GemmArgs p{a, lda, b, ldb, scale_x, scale_w, c, ldc, (int)M, (int)N, (int)K};
     if (!gemm_offsets_fit(p)) return Q8_EUNSUPPORTED;
     return hip_status(run_gemm_group_act(p, st(stream)));
+}
+
+q8_status q8_quant_fp8_per_group128(const q8_bf16* x, int64_t ldx, uint8_t* xq, int64_t ldxq,
+                                    float* scale_grp, int64_t M, int64_t K, q8_stream stream) {
+    if (M < 0 || K < 0) return Q8_EINVAL;
+    if (M == 0) return Q8_OK;
+    if (!x || !xq || !scale_grp || K == 0 || ldx < K || ldxq < K) return Q8_EINVAL;
+    if (K % 128 != 0 || M > INT32_MAX / 2 || K > INT32_MAX / 2) return Q8_EUNSUPPORTED;
+    if (ldx % 8 != 0 || ldxq % 8 != 0 || !al(x, 16) || !al(xq, 8) || !al(scale_grp, 4))
+        return Q8_EUNSUPPORTED;
+    const int64_t waves = M * ((K + 511) / 512);
+    if ((waves + 3) / 4 > INT32_MAX) return Q8_EUNSUPPORTED;
+    hipLaunchKernelGGL(quant_fp8_per_group128_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                       st(stream), x, ldx, xq, ldxq, scale_grp, (int)M, (int)K);
+    return hip_status(hipGetLastError());
+}
+
+q8_status q8_quant_weight_fp8_block128(const float* w, int64_t ldw, uint8_t* wq, int64_t ldwq,
+                                       float* scale_blk, int64_t N, int64_t K, q8_stream stream) {
+    if (N < 0 || K < 0) return Q8_EINVAL;
+    if (N == 0) return Q8_OK;
+    if (!w || !wq || !scale_blk || K == 0 || ldw < K || ldwq < K) return Q8_EINVAL;
+    if (N % 128 != 0 || K % 128 != 0) return Q8_EUNSUPPORTED;
+    if (!al(w, 4) || !al(scale_blk, 4)) return Q8_EUNSUPPORTED;
+    const int64_t blocks = (N / 128) * (K / 128);
+    if (blocks > INT32_MAX || K / 128 > INT32_MAX) return Q8_EUNSUPPORTED;
+    hipLaunchKernelGGL(quant_weight_fp8_block_kernel, dim3((unsigned)blocks), dim3(256), 0, st(stream),
+                       w, ldw, wq, ldwq, scale_blk, (int)(K / 128));
+    return hip_status(hipGetLastError());
+}
+
+q8_status q8_fp8_block_scaled_mm(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb,
+                                 const float* scale_x, const float* scale_w, q8_bf16* c,
+                                 int64_t ldc, int64_t M, int64_t N, int64_t K, q8_stream stream) {
+    q8_status r = check_gemm(a, lda, 16, b, ldb, c, ldc, 8, M, N, K);
+    if (r == Q8_OK && M > 0 && N % 128 != 0) r = Q8_EUNSUPPORTED;
+    if (r == Q8_OK && M > 0) r = check_scale(scale_x);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_w);
+    if (r != Q8_OK || M == 0) return r;
+    GemmArgs p{reinterpret_cast<const int8_t*>(a), lda, reinterpret_cast<const int8_t*>(b), ldb,
+               scale_x, scale_w, c, ldc, (int)M, (int)N, (int)K};
+    if (!gemm_offsets_fit(p)) return Q8_EUNSUPPORTED;
+    return hip_status(run_gemm_fp8_block(p, st(stream)));
 }
 
 }  // extern "C"
