@@ -62,48 +62,50 @@ __device__ __forceinline__ BlockScale8 block_scale8(float absmax) {
 }
 
 // The 8 codes of the 8 bf16 values in v, packed little-endian, bit-identical
-// to e4m3_code_of.  Fast route: t = fl(x * r), r = fl(1/s).  t differs from
-// x/s by at most |x/s| * (2^-23 + 2^-48), and the correctly rounded quotient
-// from x/s by half an ulp, so their distance is under 3 ulps of t.  E4M3
-// rounding of a normal-range t looks only at fp32 mantissa bits 19..0: when
-// those lie more than 8 ulps from the halfway pattern 0x80000, the quotient
-// rounds the same way (crossing a power of two keeps the grid point).  When
-// t < 2^-10 * (1 - 2^-20) the quotient is below the first halfway point 2^-10
-// and the code is a signed zero.  Anything else (a near-halfway t, about 1
-// element in 30,000; t in [2^-10, 2^-6)) is recomputed by division.
+// to e4m3_code_of.  Fast route: t = fl(x * r), r = fl(1/s), converted by the
+// hardware (v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even; |t| <= 448
+// (1 + 2^-22) here, so nothing saturates).  t differs from x/s by at most
+// |x/s| * (2^-23 + 2^-48), and the correctly rounded quotient from x/s by
+// half an ulp, so their distance is under 3 ulps of t.  E4M3 rounding of a
+// normal-range t looks only at fp32 mantissa bits 19..0: when those lie
+// more than 7 ulps from the halfway pattern 0x80000, the quotient rounds the
+// same way (crossing a power of two keeps the grid point).  Any other
+// element (a near-halfway t, about 1 element in 30,000, or a nonzero t
+// below 2^-6, the E4M3 subnormal range) is recomputed by division.
 __device__ __forceinline__ v2u e4m3_codes8(v4u v, const BlockScale8& q) {
-    u32 c[8];
+    float t[8];
     bool redo = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
-        const u32 u = __float_as_uint(x * q.r);
-        const u32 a = u & 0x7FFFFFFFu;
-        const bool normal = a >= E4M3_MIN_NORMAL_BITS;
-        const u32 mag = normal ? e4m3_code_normal(a) : 0u;
-        const bool near_half = normal && ((a & 0xFFFFFu) - 0x7FFF8u) < 17u;
-        const bool low = !normal && a >= 0x3A7FFFF0u;  // just below 2^-10 and up
-        redo |= near_half | low;
-        c[e] = ((u >> 24) & 0x80u) | mag;
+        t[e] = x * q.r;
+        const u32 a = __float_as_uint(t[e]) & 0x7FFFFFFFu;
+        redo |= (a - 1u) < (E4M3_MIN_NORMAL_BITS - 1u);       // 0 < |t| < 2^-6
+        redo |= ((a + 8u) & 0xFFFF0u) == 0x80000u;             // near halfway
     }
+    v2u r;
+    r[0] = (u32)__builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+    r[0] = (u32)__builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], (int)r[0], true);
+    r[1] = (u32)__builtin_amdgcn_cvt_pk_fp8_f32(t[4], t[5], 0, false);
+    r[1] = (u32)__builtin_amdgcn_cvt_pk_fp8_f32(t[6], t[7], (int)r[1], true);
     if (!q.fast || redo) {  // rare: redo by division
+        u32 c[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
             c[e] = e4m3_code_of(x, q.s);
         }
+        r[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+        r[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
     }
-    v2u r;
-    r[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    r[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
     return r;
 }
 
 // Dynamic per-token-per-group FP8 activations: one scale per (row, 128-wide
 // K block).  One wave per 512-value span of a row: lane l holds chunk l (8
-// values), lanes 16g .. 16g+15 form block g of the span, whose absmax takes
-// four lane swaps.  K % 128 == 0; 16-byte aligned x rows, 8-byte aligned xq
-// rows; s [M, K/128] dense.
+// values), lanes 16g .. 16g+15 form block g of the span (one DPP row), whose
+// absmax takes four row rotations.  K % 128 == 0; 16-byte aligned x rows,
+// 8-byte aligned xq rows; s [M, K/128] dense.
 __global__ __launch_bounds__(256) void quant_fp8_per_group128_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ xq, int64_t ldxq,
     float* __restrict__ s, int M, int K) {
@@ -116,9 +118,7 @@ __global__ __launch_bounds__(256) void quant_fp8_per_group128_kernel(
     const bool ok = c < (K >> 3);
     v4u v = v4u{};
     if (ok) v = reinterpret_cast<const v4u*>(x + (int64_t)m * ldx)[c];
-    float a = mag_to_f32(mag_max8(v2h{0, 0}, v));
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, o, 64));
+    const float a = row16_max(mag_to_f32(mag_max8(v2h{0, 0}, v)));
     const BlockScale8 q = block_scale8(a);
     if (!ok) return;
     reinterpret_cast<v2u*>(xq + (int64_t)m * ldxq)[c] = e4m3_codes8(v, q);

@@ -27,6 +27,17 @@ __device__ __forceinline__ float mag_to_f32(v2h acc) {
     return __uint_as_float(m << 16);
 }
 
+// Maximum of a non-negative float over the 16 lanes of each DPP row (lanes
+// 16g .. 16g+15): rotations by 8, 4, 2 and 1 within the row leave every lane
+// with the row's maximum, without a trip through the LDS crossbar.
+__device__ __forceinline__ float row16_max(float a) {
+    a = __builtin_fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x128, 0xF, 0xF, false)));
+    a = __builtin_fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x124, 0xF, 0xF, false)));
+    a = __builtin_fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x122, 0xF, 0xF, false)));
+    a = __builtin_fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x121, 0xF, 0xF, false)));
+    return a;
+}
+
 // The 8 codes of the 8 bf16 values in v, packed little-endian, each with a
 // full IEEE division (the reference route).
 __device__ __forceinline__ v2u codes8_div(v4u v, float s) {
@@ -97,8 +108,9 @@ __device__ __forceinline__ v2u codes8(v4u v, const RowScale& q) {
 // Per-token-per-group activations: one scale per (row, 128-wide K block),
 // every block quantized like a row of 128 values.  One wave per 512-value
 // span of a row: lane l holds chunk l (8 values), lanes 16g .. 16g+15 form
-// block g of the span, whose absmax takes four lane swaps.  K % 128 == 0;
-// 16-byte aligned x rows, 8-byte aligned xq rows; s [M, K/128] dense.
+// block g of the span (one DPP row), whose absmax takes four row rotations.
+// K % 128 == 0; 16-byte aligned x rows, 8-byte aligned xq rows; s [M, K/128]
+// dense.
 __global__ __launch_bounds__(256) void quant_per_group128_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int8_t* __restrict__ xq, int64_t ldxq,
     float* __restrict__ s, int M, int K) {
@@ -111,9 +123,7 @@ __global__ __launch_bounds__(256) void quant_per_group128_kernel(
     const bool ok = c < (K >> 3);
     v4u v = v4u{};
     if (ok) v = reinterpret_cast<const v4u*>(x + (int64_t)m * ldx)[c];
-    float a = mag_to_f32(mag_max8(v2h{0, 0}, v));
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, o, 64));
+    const float a = row16_max(mag_to_f32(mag_max8(v2h{0, 0}, v)));
     const RowScale q = row_scale(a);
     if (!ok) return;
     reinterpret_cast<v2u*>(xq + (int64_t)m * ldxq)[c] = codes8(v, q);
