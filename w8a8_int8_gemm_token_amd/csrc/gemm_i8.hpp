@@ -273,15 +273,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
                 fx[set][a] = *reinterpret_cast<const v4i*>(bx + xbase[kk] + a * 32 * BK);
         }
     };
-    auto mfma = [&](int set, int from, int to) __attribute__((always_inline)) {
+    // FP8: `fresh` starts a block's partial (C = 0) instead of adding to acc
+    auto mfma = [&](int set, int from, int to, bool fresh = false) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = from; t < to; ++t) {
             const int a = t / TN, b = t % TN;
             if constexpr (F8)  // A and B in E4M3 (format 0), no block exponents
-                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[set][b], fx[set][a], acc[a][b],
-                                                                            0, 0, 0, 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    fw[set][b], fx[set][a], fresh ? AccT{} : acc[a][b], 0, 0, 0, 0, 0, 0);
             else
-                acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[set][b], fx[set][a], acc[a][b], 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[set][b], fx[set][a], fresh ? AccT{} : acc[a][b],
+                                                                  0, 0, 0);
         }
     };
     // EPI_GROUP: fold the stage's 128-wide block sums into the fp32
@@ -299,7 +301,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
                 for (int b = 0; b < TN; ++b) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) facc[a][b][e] = __builtin_fmaf(acc[a][b][e], f[a], facc[a][b][e]);
-                    acc[a][b] = AccT{};
                 }
         } else if constexpr (GRP) {
             float sx[TM];  // EPI_GROUP_ACT: block scale of this lane's token in block a
@@ -318,8 +319,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
                                 (float)acc[a][b][g * 4 + e], ACT ? sx[a] * sc[e] : sc[e],
                                 facc[a][b][g * 4 + e]);
                 }
-#pragma unroll
-                for (int a = 0; a < TM; ++a) acc[a][b] = v16i{};
             }
         }
     };
@@ -336,7 +335,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
             // fold of this stage's block, and the hand-over
             issue(kt + 1, nx, nw, ns);
             read(1, 1, cx, cw);
-            mfma(0, 0, NM);
+            mfma(0, 0, NM, true);
             interleave<NM, NR, LPS>();
             __builtin_amdgcn_sched_barrier(0);
             mfma(1, 0, NM);
@@ -347,10 +346,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
             read(0, 0, nx, nw);
             __builtin_amdgcn_sched_barrier(0);
         } else {
-            // sub-step 0: MFMAs on set 0; next stage's direct loads; set 1 <- kk 1
+            // sub-step 0: MFMAs on set 0 (a group's first: C = 0); next
+            // stage's direct loads; set 1 <- kk 1
             issue(kt + 1, nx, nw, ns);
             read(1, 1, cx, cw);
-            mfma(0, 0, NM);
+            mfma(0, 0, NM, GRP);
             interleave<NM, NR, LPS>();
             __builtin_amdgcn_sched_barrier(0);
             // sub-step 1
