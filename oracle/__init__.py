@@ -55,6 +55,12 @@ def _load():
             "q8o_f32_to_bf16": ([F], ctypes.c_uint16),
             "q8o_bf16_to_f32": ([ctypes.c_uint16], F),
             "q8o_quant_per_token": ([P, I, I, P, P], None),
+            "q8o_quant_per_token_f16": ([P, I, I, P, P], None),
+            "q8o_f16_to_f32": ([ctypes.c_uint16], F),
+            "q8o_f32_to_f16": ([F], ctypes.c_uint16),
+            "q8o_scaled_mm_f16": ([P, P, P, P, I, I, I, P], ctypes.c_int),
+            "q8o_quant_per_group128_f16": ([P, I, I, P, P], ctypes.c_int),
+            "q8o_scaled_mm_group128_act_f16": ([P, P, P, P, I, I, I, P], ctypes.c_int),
             "q8o_e4m3_value": ([ctypes.c_uint8], ctypes.c_double),
             "q8o_e4m3_rne": ([F], ctypes.c_uint8),
             "q8o_quant_fp8_per_group128": ([P, I, I, P, P], ctypes.c_int),
@@ -328,3 +334,68 @@ def fp8_block_mm(a, b, s_x, s_w, with_mag: bool = False):
     if rc == -2:
         raise ValueError("oracle: NaN E4M3 code in an operand")
     return (y, mag) if with_mag else y
+
+
+# ---------------------------------------------------------------- fp16 --
+
+def f16_to_f32(bits: int) -> float:
+    """fp16 bits -> fp32 value (exact)."""
+    return _load().q8o_f16_to_f32(int(bits) & 0xFFFF)
+
+
+def f32_to_f16(v: float) -> int:
+    """fp32 -> fp16 bits, round to nearest even (overflow to infinity)."""
+    return int(_load().q8o_f32_to_f16(float(np.float32(v))))
+
+
+def quant_per_token_f16(x_f16: np.ndarray):
+    """Per-token quant of fp16 activations.  x: uint16 [M,K] fp16 bits ->
+    (xq int8 [M,K], s fp32 [M])."""
+    x = _c(x_f16, np.uint16)
+    M, K = x.shape
+    xq = np.empty((M, K), np.int8)
+    s = np.empty((M,), np.float32)
+    _load().q8o_quant_per_token_f16(_p(x), M, K, _p(xq), _p(s))
+    return xq, s
+
+
+def scaled_mm_f16(a, b, s_tok, s_ch) -> np.ndarray:
+    """GEMM + per-channel epilogue, fp16 out -> fp16 bits uint16 [M,N]."""
+    a = _c(a, np.int8)
+    b = _c(b, np.int8)
+    s_tok = _c(s_tok, np.float32)
+    s_ch = _c(s_ch, np.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    y = np.empty((M, N), np.uint16)
+    if _load().q8o_scaled_mm_f16(_p(a), _p(b), _p(s_tok), _p(s_ch), M, N, K, _p(y)) != 0:
+        raise OverflowError("oracle: int32 accumulator overflow")
+    return y
+
+
+def quant_per_group128_f16(x_f16):
+    """Per-token-per-128-group quant of fp16 activations -> (xq int8 [M,K],
+    s_x fp32 [M,K/128])."""
+    x = _c(x_f16, np.uint16)
+    M, K = x.shape
+    xq = np.empty((M, K), np.int8)
+    s = np.empty((M, K // 128), np.float32)
+    if _load().q8o_quant_per_group128_f16(_p(x), M, K, _p(xq), _p(s)) != 0:
+        raise ValueError("oracle: K must be a multiple of 128")
+    return xq, s
+
+
+def scaled_mm_group128_act_f16(a, b, s_x, s_w) -> np.ndarray:
+    """GEMM with per-(token, block) and per-(channel, block) scales, fp16
+    out -> fp16 bits uint16 [M,N]."""
+    a = _c(a, np.int8)
+    b = _c(b, np.int8)
+    s_x = _c(s_x, np.float32)
+    s_w = _c(s_w, np.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    assert s_x.shape == (M, K // 128) and s_w.shape == (N, K // 128)
+    y = np.empty((M, N), np.uint16)
+    if _load().q8o_scaled_mm_group128_act_f16(_p(a), _p(b), _p(s_x), _p(s_w), M, N, K, _p(y)) != 0:
+        raise ValueError("oracle: K must be a multiple of 128")
+    return y

@@ -90,6 +90,53 @@ uint16_t q8o_f32_to_bf16(float f)
 
 float q8o_bf16_to_f32(uint16_t b) { return bf16_bits_to_f32(b); }
 
+/* ---------------------------------------------------------------- fp16 -- */
+/* IEEE binary16: sign, 5 exponent bits (bias 15), 10 fraction bits.  The
+ * fp16 variant of the layer takes fp16 activations and writes fp16
+ * outputs ("Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", "Serving (vLLM, gfx908
+ * fork)": --dtype half is the model's native dtype, GEMM inputs quantized
+ * to INT8 at run time). */
+
+/* fp16 -> fp32 is exact, decoded by the definition. */
+float q8o_f16_to_f32(uint16_t h)
+{
+    const int E = (h >> 10) & 31, f = h & 1023;
+    double v;
+    if (E == 31)
+        v = f ? NAN : INFINITY;
+    else if (E == 0)
+        v = ldexp((double)f, -24);
+    else
+        v = ldexp((double)(1024 + f), E - 25);
+    return (float)((h & 0x8000) ? -v : v);
+}
+
+/* fp32 -> fp16, round to nearest, ties to even, by the definition:
+ * subnormal quantum 2^-24, magnitudes from 65520 (the midpoint above the
+ * largest finite value 65504) up overflow to infinity, NaN stays NaN. */
+uint16_t q8o_f32_to_f16(float f)
+{
+    if (isnan(f))
+        return 0x7E00;
+    const uint16_t sign = signbit(f) ? 0x8000 : 0;
+    const double a = fabs((double)f);
+    if (a >= 65520.0)
+        return sign | 0x7C00;
+    if (a < ldexp(1.0, -14))  /* subnormal range (exact scaling) */
+        return sign | (uint16_t)nearbyint(a * ldexp(1.0, 24));
+    int ex;
+    frexp(a, &ex);            /* a = fr * 2^ex, fr in [0.5, 1) */
+    int e = ex - 1;           /* 2^e <= a < 2^(e+1) */
+    double mant = nearbyint(ldexp(a, 10 - e)); /* in [1024, 2048] */
+    if (mant == 2048.0) {
+        mant = 1024.0;
+        e += 1;
+    }
+    if (e > 15)
+        return sign | 0x7C00;
+    return sign | (uint16_t)(((e + 15) << 10) | ((int)mant - 1024));
+}
+
 /* 1 if the FPU is in round-to-nearest-even mode (every routine relies on it). */
 int q8o_env_ok(void) { return fegetround() == FE_TONEAREST; }
 
@@ -125,23 +172,37 @@ static int8_t code_of(float x, float s)
     return (int8_t)r;
 }
 
-/* Per-token dynamic quantization of a bf16 activation matrix.
- * x: [M][K] bf16 bits, row-major.  xq: [M][K] int8.  s_tok: [M] fp32.
+/* Per-token dynamic quantization of a 16-bit activation matrix whose
+ * values `dec` decodes (bf16 or fp16).
+ * x: [M][K] bits, row-major.  xq: [M][K] int8.  s_tok: [M] fp32.
  * [P1 "Recipe": INT8 per-token dynamic activations; P4 "Quantization"] */
-void q8o_quant_per_token(const uint16_t *x, int64_t M, int64_t K,
-                         int8_t *xq, float *s_tok)
+static void quant_per_token_fmt(const uint16_t *x, float (*dec)(uint16_t),
+                                int64_t M, int64_t K, int8_t *xq,
+                                float *s_tok)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         float *row = (float *)malloc((size_t)K * sizeof(float));
         for (int64_t k = 0; k < K; ++k)
-            row[k] = bf16_bits_to_f32(x[m * K + k]);
+            row[k] = dec(x[m * K + k]);
         float s = absmax_scale(row, K);
         s_tok[m] = s;
         for (int64_t k = 0; k < K; ++k)
             xq[m * K + k] = code_of(row[k], s);
         free(row);
     }
+}
+
+void q8o_quant_per_token(const uint16_t *x, int64_t M, int64_t K,
+                         int8_t *xq, float *s_tok)
+{
+    quant_per_token_fmt(x, bf16_bits_to_f32, M, K, xq, s_tok);
+}
+
+void q8o_quant_per_token_f16(const uint16_t *x, int64_t M, int64_t K,
+                             int8_t *xq, float *s_tok)
+{
+    quant_per_token_fmt(x, q8o_f16_to_f32, M, K, xq, s_tok);
 }
 
 /* Offline symmetric weight quantization of an fp32 weight W [N][K].
@@ -218,10 +279,10 @@ void q8o_epilogue_channel(const int32_t *acc, const float *s_tok,
 }
 
 /* GEMM and per-channel epilogue in one call, without storing the int32
- * matrix. */
-int q8o_scaled_mm(const int8_t *a, const int8_t *b, const float *s_tok,
-                  const float *s_ch, int64_t M, int64_t N, int64_t K,
-                  uint16_t *y)
+ * matrix; `enc` rounds the fp32 result to the 16-bit output format. */
+static int scaled_mm_fmt(const int8_t *a, const int8_t *b, const float *s_tok,
+                         const float *s_ch, int64_t M, int64_t N, int64_t K,
+                         uint16_t (*enc)(float), uint16_t *y)
 {
     int bad = 0;
 #pragma omp parallel for schedule(static) reduction(| : bad)
@@ -235,10 +296,25 @@ int q8o_scaled_mm(const int8_t *a, const int8_t *b, const float *s_tok,
             float v = (float)(int32_t)t;
             v = v * s_tok[m];
             v = v * s_ch[n];
-            y[m * N + n] = q8o_f32_to_bf16(v);
+            y[m * N + n] = enc(v);
         }
     }
     return bad ? -1 : 0;
+}
+
+int q8o_scaled_mm(const int8_t *a, const int8_t *b, const float *s_tok,
+                  const float *s_ch, int64_t M, int64_t N, int64_t K,
+                  uint16_t *y)
+{
+    return scaled_mm_fmt(a, b, s_tok, s_ch, M, N, K, q8o_f32_to_bf16, y);
+}
+
+/* The same with fp16 outputs (fp16 RNE of the same fp32 value). */
+int q8o_scaled_mm_f16(const int8_t *a, const int8_t *b, const float *s_tok,
+                      const float *s_ch, int64_t M, int64_t N, int64_t K,
+                      uint16_t *y)
+{
+    return scaled_mm_fmt(a, b, s_tok, s_ch, M, N, K, q8o_f32_to_f16, y);
 }
 
 /* GEMM with group-128 weights.  For g = 0 .. K/128-1 in order:
@@ -427,8 +503,8 @@ int q8o_rmsnorm_quant(const uint16_t *x, uint16_t *res, const uint16_t *gamma,
  * Quantization: every 128-wide block of a row is quantized like a token row
  * on its own: s_x[m][g] = fl32(absmax / 127), codes RNE of fl32(x / s),
  * clamped to [-127, 127]; s_x is [M][K/128] row-major. */
-int q8o_quant_per_group128(const uint16_t *x, int64_t M, int64_t K,
-                           int8_t *xq, float *s_x)
+static int quant_per_group128_fmt(const uint16_t *x, float (*dec)(uint16_t),
+                                  int64_t M, int64_t K, int8_t *xq, float *s_x)
 {
     if (K % 128 != 0) return -1;
     const int64_t G = K / 128;
@@ -436,7 +512,7 @@ int q8o_quant_per_group128(const uint16_t *x, int64_t M, int64_t K,
     for (int64_t m = 0; m < M; ++m) {
         float v[128];
         for (int64_t g = 0; g < G; ++g) {
-            for (int k = 0; k < 128; ++k) v[k] = bf16_bits_to_f32(x[m * K + g * 128 + k]);
+            for (int k = 0; k < 128; ++k) v[k] = dec(x[m * K + g * 128 + k]);
             const float sc = absmax_scale(v, 128);
             s_x[m * G + g] = sc;
             for (int k = 0; k < 128; ++k) xq[m * K + g * 128 + k] = code_of(v[k], sc);
@@ -445,15 +521,28 @@ int q8o_quant_per_group128(const uint16_t *x, int64_t M, int64_t K,
     return 0;
 }
 
+int q8o_quant_per_group128(const uint16_t *x, int64_t M, int64_t K,
+                           int8_t *xq, float *s_x)
+{
+    return quant_per_group128_fmt(x, bf16_bits_to_f32, M, K, xq, s_x);
+}
+
+int q8o_quant_per_group128_f16(const uint16_t *x, int64_t M, int64_t K,
+                               int8_t *xq, float *s_x)
+{
+    return quant_per_group128_fmt(x, q8o_f16_to_f32, M, K, xq, s_x);
+}
+
 /* GEMM with both scales per 128-wide K block.  For g = 0 .. K/128-1 in
  * order (reading: the two scales are multiplied first, as block-scaled
  * GEMMs do, then one fused multiply-add per block):
  *   p_g = sum_{k in [128g, 128g+128)} a[m][k]*b[n][k]    (exact int32)
  *   acc = fmaf((float)p_g, fl32(s_x[m][g] * s_w[n][g]), acc)   (from 0)
  * y = bf16_rne(acc).  Returns -1 if K is not a multiple of 128. */
-int q8o_scaled_mm_group128_act(const int8_t *a, const int8_t *b,
-                               const float *s_x, const float *s_w,
-                               int64_t M, int64_t N, int64_t K, uint16_t *y)
+static int scaled_mm_group128_act_fmt(const int8_t *a, const int8_t *b,
+                                      const float *s_x, const float *s_w,
+                                      int64_t M, int64_t N, int64_t K,
+                                      uint16_t (*enc)(float), uint16_t *y)
 {
     if (K % 128 != 0) return -1;
     const int64_t G = K / 128;
@@ -468,10 +557,24 @@ int q8o_scaled_mm_group128_act(const int8_t *a, const int8_t *b,
                 const float sc = s_x[m * G + g] * s_w[n * G + g];
                 acc = fmaf((float)p, sc, acc);
             }
-            y[m * N + n] = q8o_f32_to_bf16(acc);
+            y[m * N + n] = enc(acc);
         }
     }
     return 0;
+}
+
+int q8o_scaled_mm_group128_act(const int8_t *a, const int8_t *b,
+                               const float *s_x, const float *s_w,
+                               int64_t M, int64_t N, int64_t K, uint16_t *y)
+{
+    return scaled_mm_group128_act_fmt(a, b, s_x, s_w, M, N, K, q8o_f32_to_bf16, y);
+}
+
+int q8o_scaled_mm_group128_act_f16(const int8_t *a, const int8_t *b,
+                                   const float *s_x, const float *s_w,
+                                   int64_t M, int64_t N, int64_t K, uint16_t *y)
+{
+    return scaled_mm_group128_act_fmt(a, b, s_x, s_w, M, N, K, q8o_f32_to_f16, y);
 }
 
 /* ------------------------------------------------------- FP8 block W8A8 -- */

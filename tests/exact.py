@@ -113,3 +113,10 @@ def e4m3(r: Fraction) -> Fraction:
     if abs(v) > 448:
         return Fraction(448) if v > 0 else Fraction(-448)
     return v
+
+
+def f16(r: Fraction) -> Fraction:
+    """Nearest IEEE binary16 value (11 significant bits, normal exponents
+    -14 .. 15, ties to even); beyond the largest finite value rounds to the
+    infinity stand-in of round_to_format."""
+    return round_to_format(r, 11, -14, 15)
