@@ -294,6 +294,55 @@ def fp8_block_tflops(dev, iters=10):
             "shape": [wl.M, wl.N, wl.K]}
 
 
+def f16_layer(dev, iters=10):
+    """The fp16 variant of the one-call layer (fp16 in, fp16 out): the
+    prefill shape timed with events, and M=8 decode per call in a HIP graph
+    over weight copies (as the bf16 decode line)."""
+    wl = synth.WORKLOADS["prefill"]
+    x = synth.activations(wl, 0).to(dev).half()
+    w = synth.weights(wl, 0).to(dev)
+    wq, sc = q8.q8_quant_weight(w)
+    del w
+    y = torch.empty((wl.M, wl.N), dtype=torch.float16, device=dev)
+    xq = torch.empty((wl.M, wl.K), dtype=torch.int8, device=dev)
+    st = torch.empty((wl.M,), dtype=torch.float32, device=dev)
+    f = lambda: q8.q8_quant_scaled_mm_f16(x, wq, sc, out=y, xq_out=xq, scale_tok_out=st)  # noqa: E731
+    for _ in range(2):
+        f()
+    ms = events_time(f, iters)
+    ops = 2.0 * wl.M * wl.N * wl.K
+    out = {"prefill": {"us": ms * 1e3, "TOPS": ops / (ms * 1e-3) / 1e12}}
+    del y, xq, st, wq, sc, x
+    dw = synth.WORKLOADS["decode"]
+    w = synth.weights(dw, 0).to(dev)
+    wq, sc = q8.q8_quant_weight(w)
+    del w
+    ncopy = 24
+    wqs = [wq.clone() for _ in range(ncopy)]
+    M = 8
+    x = synth.activations(dw, 0, M=M).to(dev).half()
+    y = torch.empty((M, dw.N), dtype=torch.float16, device=dev)
+    xq = torch.empty((M, dw.K), dtype=torch.int8, device=dev)
+    st = torch.empty((M,), dtype=torch.float32, device=dev)
+
+    def cycle():
+        for i in range(ncopy):
+            q8.q8_quant_scaled_mm_f16(x, wqs[i], sc, out=y, xq_out=xq, scale_tok_out=st)
+    cycle()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cycle()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = events_time(g.replay, 20) / ncopy
+    nbytes = dw.N * dw.K + 4 * dw.N + 2 * M * dw.K + 2 * M * dw.N + 4 * M + M * dw.K
+    out["decode_M8"] = {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                        "timing": "HIP graph of 24 calls, events"}
+    return out
+
+
 # The model's Linear shapes (hidden 5120, intermediate 17408): W8A8 modules
 # (q/k/v-like 15360 x 5120, gate/up 17408 x 5120, o-like 5120 x 5120) and
 # the W8A16 down projection (5120 x 17408).
@@ -353,7 +402,7 @@ SECONDARY = {"decode": lambda dev: decode_gbs(dev), "group128": lambda dev: grou
              "m_sweep": lambda dev: m_sweep(dev),
              "group128_act": lambda dev: group_act_tops(dev),
              "w8a16": lambda dev: w8a16_tflops(dev), "rmsnorm_quant": lambda dev: rmsnorm_quant_gbs(dev),
-             "fp8_block": lambda dev: fp8_block_tflops(dev)}
+             "fp8_block": lambda dev: fp8_block_tflops(dev), "f16": lambda dev: f16_layer(dev)}
 
 
 def main():
@@ -364,7 +413,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary",
-                    default="decode,group128,group128_act,w8a16,rmsnorm_quant,fp8_block,m_sweep",
+                    default="decode,group128,group128_act,w8a16,rmsnorm_quant,fp8_block,f16,m_sweep",
                     help="comma list of secondary workloads, or 'none'")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()

@@ -55,6 +55,7 @@ typedef enum {
 } q8_status;
 
 typedef uint16_t q8_bf16; /* raw bfloat16 bits */
+typedef uint16_t q8_f16;  /* raw IEEE fp16 (binary16) bits */
 typedef void *q8_stream;  /* hipStream_t; 0 selects the null stream */
 
 /* Largest K of any GEMM entry point: 128*128*K stays below 2^31, so the
@@ -286,6 +287,50 @@ q8_status q8_scaled_mm_group128_act(const int8_t *a, int64_t lda,
                                     const float *scale_x, const float *scale_w,
                                     q8_bf16 *c, int64_t ldc, int64_t M,
                                     int64_t N, int64_t K, q8_stream stream);
+
+/* ------------------------------------------------------------------------
+ * fp16 variant.  The same layer with IEEE fp16 activations and fp16
+ * outputs: "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", "Serving (vLLM, gfx908
+ * fork)" serves in half precision (the model's native dtype) with every
+ * GEMM input quantized to INT8 at run time.  Each call computes exactly
+ * what its bf16 namesake computes, with two changes: activations are fp16
+ * values (decoded exactly to fp32), and the fp32 result is rounded to fp16
+ * (round to nearest even; magnitudes from 65520 up become infinity) instead
+ * of bf16.  Arguments, layouts, alignment rules and errors are those of the
+ * bf16 call; every q8_f16 pointer takes the place of the q8_bf16 one.
+ * ---------------------------------------------------------------------- */
+
+/* As q8_quant_per_token, on fp16 activations. */
+q8_status q8_quant_per_token_f16(const q8_f16 *x, int64_t ldx, int8_t *xq,
+                                 int64_t ldxq, float *scale_tok, int64_t M,
+                                 int64_t K, q8_stream stream);
+
+/* As q8_scaled_mm, writing fp16 outputs:
+ *   c[m,n] = fp16_rne(fl32(fl32((float)acc * scale_tok[m]) * scale_ch[n])) */
+q8_status q8_scaled_mm_f16(const int8_t *a, int64_t lda, const int8_t *b,
+                           int64_t ldb, const float *scale_tok,
+                           const float *scale_ch, q8_f16 *c, int64_t ldc,
+                           int64_t M, int64_t N, int64_t K, q8_stream stream);
+
+/* As q8_quant_scaled_mm (the whole layer in one call), fp16 in and out. */
+q8_status q8_quant_scaled_mm_f16(const q8_f16 *x, int64_t ldx,
+                                 const int8_t *b, int64_t ldb,
+                                 const float *scale_ch, q8_f16 *c, int64_t ldc,
+                                 int8_t *xq, float *scale_tok, int64_t M,
+                                 int64_t N, int64_t K, q8_stream stream);
+
+/* As q8_quant_per_group128, on fp16 activations. */
+q8_status q8_quant_per_group128_f16(const q8_f16 *x, int64_t ldx, int8_t *xq,
+                                    int64_t ldxq, float *scale_grp, int64_t M,
+                                    int64_t K, q8_stream stream);
+
+/* As q8_scaled_mm_group128_act, writing fp16 outputs (c = fp16_rne(f)). */
+q8_status q8_scaled_mm_group128_act_f16(const int8_t *a, int64_t lda,
+                                        const int8_t *b, int64_t ldb,
+                                        const float *scale_x,
+                                        const float *scale_w, q8_f16 *c,
+                                        int64_t ldc, int64_t M, int64_t N,
+                                        int64_t K, q8_stream stream);
 
 /* ------------------------------------------------------------------------
  * FP8 block W8A8.  E4M3 is the OCP 8-bit float: sign, 4 exponent bits (bias

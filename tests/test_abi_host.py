@@ -141,6 +141,17 @@ def test_fp8_entry_points_validation(lib):
     assert fm(A, 256, B, 256, S, S, C, 128, 16, 144, 256, None) == EINVAL   # ldc < N
 
 
+def test_f16_entry_points_validation(lib):
+    assert lib.q8_quant_per_token_f16(A, 256, B, 256, S, 0, 256, None) == OK
+    assert lib.q8_quant_per_token_f16(None, 256, B, 256, S, 4, 256, None) == EINVAL
+    assert lib.q8_scaled_mm_f16(A, 256, B, 256, S, S, C, 128, 16, 120, 256, None) == EUNSUP
+    assert lib.q8_scaled_mm_f16(A, 256, B, 256, None, S, C, 128, 16, 128, 256, None) == EINVAL
+    assert lib.q8_quant_scaled_mm_f16(A, 256, B, 256, S, C, 128, None, S, 16, 128, 256, None) == EINVAL
+    assert lib.q8_quant_scaled_mm_f16(A, 256, B, 256, S, C, 128, B + 8, S, 16, 128, 256, None) == EUNSUP
+    assert lib.q8_quant_per_group128_f16(A, 256, B, 256, S, 4, 192, None) == EUNSUP
+    assert lib.q8_scaled_mm_group128_act_f16(A, 256, B, 256, S, None, C, 128, 16, 128, 256, None) == EINVAL
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     x = torch.zeros((4, 256), dtype=torch.bfloat16)

@@ -1,0 +1,160 @@
+"""GPU parity of the fp16 variant (fp16 activations in, fp16 outputs)
+against the CPU oracle: codes and scales bit-exact, fp16 outputs within 1
+fp16 ulp (ordered-integer distance, +0 == -0) -- the same bar as bf16,
+since the same fp32 value is rounded once to the output format."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w8a8_int8_gemm_token_amd as q8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def dev(t):
+    if isinstance(t, np.ndarray):
+        t = torch.from_numpy(np.ascontiguousarray(t))
+    return t.to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu()
+
+
+def hbits(t_f16_cpu) -> np.ndarray:
+    return t_f16_cpu.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def ulp_dist(a_bits, b_bits):
+    def ordered(u):
+        u = u.astype(np.int32)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def assert_ulp1(got_bits, ref_bits, what):
+    d = ulp_dist(got_bits, ref_bits)
+    say(f"{what}: max ulp {int(d.max()) if d.size else 0}, {int((d > 0).sum())}/{d.size} not bit-equal")
+    assert d.size == 0 or d.max() <= 1, what
+
+
+def f16_acts(name, seed, M=None, K=None):
+    return synth.activations(synth.WORKLOADS[name], seed, M=M, K=K).float().half()
+
+
+@pytest.mark.parametrize("M,K,pad", [(1, 1, 0), (3, 7, 0), (5, 100, 3), (17, 136, 0), (4, 512, 0),
+                                     (300, 2048, 0), (300, 5120, 8), (2, 8192, 0), (3, 8200, 0)])
+def test_quant_per_token_f16(M, K, pad):
+    say("quant f16", M, K, pad)
+    xf, _ = synth.custom(M, K + pad, 16, seed=M * 7 + K, outlier_cols=max(1, K // 100))
+    xf = xf.float().half()
+    x = xf[:, :K].contiguous()
+    xq_ref, s_ref = oracle.quant_per_token_f16(hbits(x))
+    xq, s = q8.q8_quant_per_token_f16(dev(xf)[:, :K])
+    np.testing.assert_array_equal(host(s).numpy(), s_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+
+
+def test_quant_f16_near_ties_subnormals_and_zero_rows():
+    """Rows of the fp16 values where x * fl(1/s) and x / s round to
+    different codes, fp16 subnormals, and an all-zero row."""
+    allh = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float32)
+    rng = np.random.default_rng(1)
+    rows = []
+    for _ in range(300):
+        a = allh[rng.integers(0x3C00, 0x7B00)]
+        s = np.float32(np.float64(a) / 127.0)
+        xs = allh[allh <= a]
+        qd = np.rint((xs.astype(np.float64) / np.float64(s)).astype(np.float32))
+        qr = np.rint((xs * (np.float32(1.0) / s)).astype(np.float32))
+        idx = np.nonzero(qd != qr)[0]
+        if len(idx):
+            rows.append(np.concatenate([[a], xs[idx], -xs[idx]]).astype(np.float32))
+    assert len(rows) >= 10
+    K = 512
+    mat = np.zeros((len(rows) + 2, K), np.float32)
+    for i, r in enumerate(rows):
+        mat[i, :len(r)] = r[:K]
+    mat[len(rows), :6] = np.array([6e-8, 1.2e-7, -3e-6, 5.9e-5, 0, -6e-8], np.float32)  # subnormal fp16
+    x = torch.from_numpy(mat).half()
+    for M in (x.shape[0], 300):  # workgroup-per-row and wave-per-row kernels
+        xx = torch.cat([x] * (1 + M // x.shape[0]))[:M]
+        xq_ref, s_ref = oracle.quant_per_token_f16(hbits(xx))
+        xq, st = q8.q8_quant_per_token_f16(dev(xx))
+        np.testing.assert_array_equal(host(st).numpy(), s_ref)
+        np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (8, 128, 1024), (16, 1040, 2048), (33, 144, 384),
+                                   (64, 256, 1024), (130, 272, 1152), (300, 2560, 1024)])
+def test_scaled_mm_f16(M, N, K):
+    say("scaled_mm f16", M, N, K)
+    x, w = synth.custom(M, K, N, seed=M + 3 * N, outlier_cols=3)
+    x = x.float().half()
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    xq_ref, st_ref = oracle.quant_per_token_f16(hbits(x))
+    y_ref = oracle.scaled_mm_f16(xq_ref, wq_ref, st_ref, sc_ref)
+    y = q8.q8_scaled_mm_f16(dev(xq_ref), dev(wq_ref), dev(st_ref), dev(sc_ref))
+    assert_ulp1(hbits(host(y)), y_ref, f"scaled_mm f16 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 8, 9, 16, 33, 64, 200])
+def test_quant_scaled_mm_f16_token_counts(M):
+    """Every route of the one-call layer: one-kernel decode (M <= 8), the
+    weight-streaming kernel, the tiled kernels."""
+    say("quant_scaled_mm f16", M)
+    N, K = 5120, 5120
+    x = f16_acts("decode", 0, M=M, K=K)
+    w = synth.weights(synth.WORKLOADS["decode"], 0, N=N, K=K)
+    wq, sc = q8.q8_quant_weight(dev(w))
+    y, xq, st = q8.q8_quant_scaled_mm_f16(dev(x), wq, sc)
+    xq_ref, st_ref = oracle.quant_per_token_f16(hbits(x))
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    np.testing.assert_array_equal(host(st).numpy(), st_ref)
+    y_ref = oracle.scaled_mm_f16(xq_ref, host(wq).numpy(), st_ref, host(sc).numpy())
+    assert_ulp1(hbits(host(y)), y_ref, f"one-call f16 M={M}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (8, 256, 1024), (65, 272, 1152), (200, 384, 2048)])
+def test_group128_act_f16(M, N, K):
+    say("group128 act f16", M, N, K)
+    x, w = synth.custom(M, K, N, seed=M * 11 + N, outlier_cols=3)
+    x = x.float().half()
+    xq_ref, sx_ref = oracle.quant_per_group128_f16(hbits(x))
+    wq_ref, sw_ref = oracle.quant_weight(w.numpy(), group=128)
+    y_ref = oracle.scaled_mm_group128_act_f16(xq_ref, wq_ref, sx_ref, sw_ref)
+    xq, sx = q8.q8_quant_per_group128_f16(dev(x))
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    np.testing.assert_array_equal(host(sx).numpy(), sx_ref)
+    y = q8.q8_scaled_mm_group128_act_f16(xq, dev(wq_ref), sx, dev(sw_ref))
+    assert_ulp1(hbits(host(y)), y_ref, f"group128 act f16 {M}x{N}x{K}")
+
+
+def test_prefill_f16_full_size_sampled_rows():
+    """The prefill shape (8192 x 15360 x 5120) through the fp16 one-call
+    layer in one launch; codes and scales whole, outputs on sampled rows."""
+    wl = synth.WORKLOADS["prefill"]
+    say("prefill f16 full size")
+    x = synth.activations(wl, 0).float().half()
+    w = synth.weights(wl, 0)
+    wq, sc = q8.q8_quant_weight(dev(w))
+    y, xq, st = q8.q8_quant_scaled_mm_f16(dev(x), wq, sc)
+    xq_ref, st_ref = oracle.quant_per_token_f16(hbits(x))
+    np.testing.assert_array_equal(host(st).numpy(), st_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    rows = np.array([0, 1, 255, 256, 4095, 8190, 8191, 777])
+    y_ref = oracle.scaled_mm_f16(xq_ref[rows], host(wq).numpy(), st_ref[rows], host(sc).numpy())
+    assert_ulp1(hbits(host(y))[rows], y_ref, "prefill f16 sampled rows")

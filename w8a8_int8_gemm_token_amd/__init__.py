@@ -21,6 +21,8 @@ Functions mirror the C entry points:
   q8_quant_fp8_per_group128(x) -> (xq float8_e4m3fn, scale_grp)
   q8_quant_weight_fp8_block128(w) -> (wq float8_e4m3fn, scale_blk)
   q8_fp8_block_scaled_mm(xq, wq, scale_x, scale_w) -> y
+  ..._f16 variants of the per-token and per-group quantizers, q8_scaled_mm,
+  q8_quant_scaled_mm and q8_scaled_mm_group128_act (fp16 in / out)
 Each also accepts preallocated outputs (``out=`` ...) so callers control
 allocation; the library itself never allocates.
 """
@@ -36,7 +38,9 @@ __all__ = [
     "q8_scaled_mm_group128", "w8a16_mm", "q8_quant_scaled_mm", "q8_mm_i32",
     "q8_quant_weight", "q8_smooth_fold", "q8_rmsnorm_quant", "q8_quant_per_group128",
     "q8_scaled_mm_group128_act", "q8_quant_fp8_per_group128", "q8_quant_weight_fp8_block128",
-    "q8_fp8_block_scaled_mm", "EXPORTS", "MAX_K",
+    "q8_fp8_block_scaled_mm", "q8_quant_per_token_f16", "q8_scaled_mm_f16",
+    "q8_quant_scaled_mm_f16", "q8_quant_per_group128_f16", "q8_scaled_mm_group128_act_f16",
+    "EXPORTS", "MAX_K",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -46,7 +50,8 @@ EXPORTS = (
     "q8_scaled_mm_group128", "w8a16_mm", "q8_quant_scaled_mm", "q8_mm_i32",
     "q8_quant_weight", "q8_smooth_fold", "q8_rmsnorm_quant", "q8_quant_per_group128",
     "q8_scaled_mm_group128_act", "q8_quant_fp8_per_group128", "q8_quant_weight_fp8_block128",
-    "q8_fp8_block_scaled_mm",
+    "q8_fp8_block_scaled_mm", "q8_quant_per_token_f16", "q8_scaled_mm_f16",
+    "q8_quant_scaled_mm_f16", "q8_quant_per_group128_f16", "q8_scaled_mm_group128_act_f16",
 )
 _STATUS = {0: "Q8_OK", 1: "Q8_EINVAL", 2: "Q8_EUNSUPPORTED", 3: "Q8_EHIP"}
 
@@ -93,6 +98,11 @@ def load():
         "q8_quant_fp8_per_group128": ([P, I, P, I, P, I, I, P], S),
         "q8_quant_weight_fp8_block128": ([P, I, P, I, P, I, I, P], S),
         "q8_fp8_block_scaled_mm": ([P, I, P, I, P, P, P, I, I, I, I, P], S),
+        "q8_quant_per_token_f16": ([P, I, P, I, P, I, I, P], S),
+        "q8_scaled_mm_f16": ([P, I, P, I, P, P, P, I, I, I, I, P], S),
+        "q8_quant_scaled_mm_f16": ([P, I, P, I, P, P, I, P, P, I, I, I, P], S),
+        "q8_quant_per_group128_f16": ([P, I, P, I, P, I, I, P], S),
+        "q8_scaled_mm_group128_act_f16": ([P, I, P, I, P, P, P, I, I, I, I, P], S),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -135,17 +145,26 @@ def _ld(t: torch.Tensor) -> int:
     return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
 
 
-def q8_quant_per_token(x: torch.Tensor, out=None, scale_out=None):
-    """Per-token symmetric INT8: x bf16 [M,K] -> (xq int8 [M,K], scale fp32 [M])."""
-    _dev(x, torch.bfloat16, "x", 2)
+def _quant_per_token(name, dtype, x, out, scale_out):
+    _dev(x, dtype, "x", 2)
     M, K = x.shape
     xq = out if out is not None else torch.empty((M, K), dtype=torch.int8, device=x.device)
     s = scale_out if scale_out is not None else torch.empty((M,), dtype=torch.float32, device=x.device)
     _dev(xq, torch.int8, "out", 2)
     _dev(s, torch.float32, "scale_out", 1)
-    _check("q8_quant_per_token", load().q8_quant_per_token(
+    _check(name, getattr(load(), name)(
         _ptr(x), _ld(x), _ptr(xq), _ld(xq), _ptr(s), M, K, _stream(x.device)))
     return xq, s
+
+
+def q8_quant_per_token(x: torch.Tensor, out=None, scale_out=None):
+    """Per-token symmetric INT8: x bf16 [M,K] -> (xq int8 [M,K], scale fp32 [M])."""
+    return _quant_per_token("q8_quant_per_token", torch.bfloat16, x, out, scale_out)
+
+
+def q8_quant_per_token_f16(x: torch.Tensor, out=None, scale_out=None):
+    """As q8_quant_per_token, on fp16 activations."""
+    return _quant_per_token("q8_quant_per_token_f16", torch.float16, x, out, scale_out)
 
 
 def _gemm_out(M, N, device, out, dtype=torch.bfloat16):
@@ -164,18 +183,27 @@ def _mk(a, b, a_dtype=torch.int8, b_dtype=torch.int8):
     return a.shape[0], b.shape[0], a.shape[1]
 
 
-def q8_scaled_mm(a, b, scale_tok, scale_ch, out=None):
-    """bf16 [M,N] = ((float)(a @ b^T) * scale_tok[m]) * scale_ch[n]."""
+def _scaled_mm(name, out_dtype, a, b, scale_tok, scale_ch, out):
     M, N, K = _mk(a, b)
     _dev(scale_tok, torch.float32, "scale_tok", 1)
     _dev(scale_ch, torch.float32, "scale_ch", 1)
     if scale_tok.numel() != M or scale_ch.numel() != N:
         raise ValueError("scale sizes do not match M / N")
-    c = _gemm_out(M, N, a.device, out)
-    _check("q8_scaled_mm", load().q8_scaled_mm(
+    c = _gemm_out(M, N, a.device, out, out_dtype)
+    _check(name, getattr(load(), name)(
         _ptr(a), _ld(a), _ptr(b), _ld(b), _ptr(scale_tok), _ptr(scale_ch),
         _ptr(c), _ld(c), M, N, K, _stream(a.device)))
     return c
+
+
+def q8_scaled_mm(a, b, scale_tok, scale_ch, out=None):
+    """bf16 [M,N] = ((float)(a @ b^T) * scale_tok[m]) * scale_ch[n]."""
+    return _scaled_mm("q8_scaled_mm", torch.bfloat16, a, b, scale_tok, scale_ch, out)
+
+
+def q8_scaled_mm_f16(a, b, scale_tok, scale_ch, out=None):
+    """As q8_scaled_mm, with fp16 outputs."""
+    return _scaled_mm("q8_scaled_mm_f16", torch.float16, a, b, scale_tok, scale_ch, out)
 
 
 def q8_scaled_mm_group128(a, b, scale_tok, scale_grp, out=None):
@@ -209,18 +237,29 @@ def w8a16_mm(x, w, scale_ch, out=None):
 def q8_quant_scaled_mm(x, b, scale_ch, out=None, xq_out=None, scale_tok_out=None):
     """The whole W8A8 layer: per-token quant of x, then the scaled INT8 GEMM.
     Returns (y bf16 [M,N], xq int8 [M,K], scale_tok fp32 [M])."""
-    M, N, K = _mk(x, b, torch.bfloat16)
+    return _quant_scaled_mm("q8_quant_scaled_mm", torch.bfloat16, x, b, scale_ch, out, xq_out,
+                            scale_tok_out)
+
+
+def q8_quant_scaled_mm_f16(x, b, scale_ch, out=None, xq_out=None, scale_tok_out=None):
+    """As q8_quant_scaled_mm, fp16 in and out."""
+    return _quant_scaled_mm("q8_quant_scaled_mm_f16", torch.float16, x, b, scale_ch, out, xq_out,
+                            scale_tok_out)
+
+
+def _quant_scaled_mm(name, dtype, x, b, scale_ch, out, xq_out, scale_tok_out):
+    M, N, K = _mk(x, b, dtype)
     _dev(scale_ch, torch.float32, "scale_ch", 1)
     if scale_ch.numel() != N:
         raise ValueError("scale_ch size does not match N")
-    c = _gemm_out(M, N, x.device, out)
+    c = _gemm_out(M, N, x.device, out, dtype)
     xq = xq_out if xq_out is not None else torch.empty((M, K), dtype=torch.int8, device=x.device)
     st = scale_tok_out if scale_tok_out is not None else torch.empty((M,), dtype=torch.float32, device=x.device)
     _dev(xq, torch.int8, "xq_out", 2)
     if not xq.is_contiguous() or tuple(xq.shape) != (M, K):
         raise ValueError("xq_out must be a contiguous [M, K] tensor")
     _dev(st, torch.float32, "scale_tok_out", 1)
-    _check("q8_quant_scaled_mm", load().q8_quant_scaled_mm(
+    _check(name, getattr(load(), name)(
         _ptr(x), _ld(x), _ptr(b), _ld(b), _ptr(scale_ch), _ptr(c), _ld(c),
         _ptr(xq), _ptr(st), M, N, K, _stream(x.device)))
     return c, xq, st
@@ -297,7 +336,16 @@ def q8_rmsnorm_quant(x, gamma, eps: float, residual=None, out=None, scale_out=No
 def q8_quant_per_group128(x, out=None, scale_out=None):
     """Per-token-per-128-group INT8: x bf16 [M,K] -> (xq int8 [M,K],
     scale fp32 [M, K/128])."""
-    _dev(x, torch.bfloat16, "x", 2)
+    return _quant_per_group128("q8_quant_per_group128", torch.bfloat16, x, out, scale_out)
+
+
+def q8_quant_per_group128_f16(x, out=None, scale_out=None):
+    """As q8_quant_per_group128, on fp16 activations."""
+    return _quant_per_group128("q8_quant_per_group128_f16", torch.float16, x, out, scale_out)
+
+
+def _quant_per_group128(name, dtype, x, out, scale_out):
+    _dev(x, dtype, "x", 2)
     M, K = x.shape
     xq = out if out is not None else torch.empty((M, K), dtype=torch.int8, device=x.device)
     s = scale_out if scale_out is not None else torch.empty((M, K // 128), dtype=torch.float32,
@@ -306,13 +354,24 @@ def q8_quant_per_group128(x, out=None, scale_out=None):
     _dev(s, torch.float32, "scale_out", 2)
     if not s.is_contiguous():
         raise ValueError("scale_out must be contiguous")
-    _check("q8_quant_per_group128", load().q8_quant_per_group128(
+    _check(name, getattr(load(), name)(
         _ptr(x), _ld(x), _ptr(xq), _ld(xq), _ptr(s), M, K, _stream(x.device)))
     return xq, s
 
 
 def q8_scaled_mm_group128_act(a, b, scale_x, scale_w, out=None):
     """bf16 [M,N]: per 128-block fmaf((float)p_g, fl(s_x[m,g]*s_w[n,g]), acc)."""
+    return _scaled_mm_group128_act("q8_scaled_mm_group128_act", torch.bfloat16, a, b, scale_x,
+                                   scale_w, out)
+
+
+def q8_scaled_mm_group128_act_f16(a, b, scale_x, scale_w, out=None):
+    """As q8_scaled_mm_group128_act, with fp16 outputs."""
+    return _scaled_mm_group128_act("q8_scaled_mm_group128_act_f16", torch.float16, a, b, scale_x,
+                                   scale_w, out)
+
+
+def _scaled_mm_group128_act(name, out_dtype, a, b, scale_x, scale_w, out):
     M, N, K = _mk(a, b)
     _dev(scale_x, torch.float32, "scale_x", 2)
     _dev(scale_w, torch.float32, "scale_w", 2)
@@ -320,8 +379,8 @@ def q8_scaled_mm_group128_act(a, b, scale_x, scale_w, out=None):
         raise ValueError("block scale shapes must be [M, K/128] and [N, K/128]")
     if not scale_x.is_contiguous() or not scale_w.is_contiguous():
         raise ValueError("block scales must be contiguous")
-    c = _gemm_out(M, N, a.device, out)
-    _check("q8_scaled_mm_group128_act", load().q8_scaled_mm_group128_act(
+    c = _gemm_out(M, N, a.device, out, out_dtype)
+    _check(name, getattr(load(), name)(
         _ptr(a), _ld(a), _ptr(b), _ld(b), _ptr(scale_x), _ptr(scale_w), _ptr(c), _ld(c),
         M, N, K, _stream(a.device)))
     return c

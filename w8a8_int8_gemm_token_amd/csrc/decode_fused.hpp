@@ -48,7 +48,7 @@ constexpr int DECODE_MAX_ROWS = 32;
 constexpr int DECODE_LDS_BYTES = 160 * 1024;
 
 struct DecodeArgs {
-    const uint16_t* x;  // [M, ldx] bf16 activations
+    const uint16_t* x;  // [M, ldx] bf16 (fp16) activations
     int64_t ldx;
     const int8_t* w;  // [N, ldw] int8 weight codes
     int64_t ldw;
@@ -78,8 +78,8 @@ __device__ __forceinline__ void wait_lgkm0() {
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // vmcnt 63, expcnt 7, lgkmcnt 0
 }
 
-// NC = K / 1024.
-template <int NC>
+// NC = K / 1024.  F16: fp16 activations and outputs instead of bf16.
+template <int NC, bool F16>
 __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
     constexpr int K = NC * 1024;
     constexpr int NQ = 2 * NC;  // 16-byte activation chunks per lane (one row per wave)
@@ -122,14 +122,14 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
             v2h mx = v2h{0, 0};
 #pragma unroll
             for (int i = 0; i < NQ; ++i) mx = mag_max8(mx, v[i]);
-            const RowScale q = row_scale(wave_max(mag_to_f32(mx)));
+            const RowScale q = row_scale(wave_max(mag_to_f32<F16>(mx)));
             if (lane == 0) {
                 row_scale_s[m] = q.s;
                 if (blockIdx.x == 0) p.s_tok[m] = q.s;
             }
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
-                const v2u cd = codes8(v[i], q);
+                const v2u cd = codes8<F16>(v[i], q);
                 const int c8 = lane + 64 * i;  // 8-byte code piece
                 const int uu = c8 >> 1;
                 *reinterpret_cast<v2u*>(ct + m * K + ((uu ^ m) << 4) + ((c8 & 1) << 3)) = cd;
@@ -195,33 +195,34 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
         y[e] = u * sc[e];
     }
     v2u o;
-    o[0] = pack_bf16x2(y[0], y[1]);
-    o[1] = pack_bf16x2(y[2], y[3]);
+    o[0] = pack16x2<F16>(y[0], y[1]);
+    o[1] = pack16x2<F16>(y[2], y[3]);
     *reinterpret_cast<v2u*>(p.c + (int64_t)tok * p.ldc + ch) = o;
 }
 
-template <int NC>
+template <int NC, bool F16>
 inline hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t stream) {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_fused_kernel<NC>),
+        reinterpret_cast<const void*>(&decode_fused_kernel<NC, F16>),
         hipFuncAttributeMaxDynamicSharedMemorySize, DECODE_LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const int grid = (p.N + p.rows - 1) / p.rows;
-    hipLaunchKernelGGL((decode_fused_kernel<NC>), dim3(grid), dim3(1024),
+    hipLaunchKernelGGL((decode_fused_kernel<NC, F16>), dim3(grid), dim3(1024),
                        decode_lds_bytes(p.K, p.rows), stream, p);
     return hipGetLastError();
 }
 
+template <bool F16>
 inline hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream) {
     switch (p.K / 1024) {
-        case 1: return launch_decode_t<1>(p, stream);
-        case 2: return launch_decode_t<2>(p, stream);
-        case 3: return launch_decode_t<3>(p, stream);
-        case 4: return launch_decode_t<4>(p, stream);
-        case 5: return launch_decode_t<5>(p, stream);
-        case 6: return launch_decode_t<6>(p, stream);
-        case 7: return launch_decode_t<7>(p, stream);
-        case 8: return launch_decode_t<8>(p, stream);
+        case 1: return launch_decode_t<1, F16>(p, stream);
+        case 2: return launch_decode_t<2, F16>(p, stream);
+        case 3: return launch_decode_t<3, F16>(p, stream);
+        case 4: return launch_decode_t<4, F16>(p, stream);
+        case 5: return launch_decode_t<5, F16>(p, stream);
+        case 6: return launch_decode_t<6, F16>(p, stream);
+        case 7: return launch_decode_t<7, F16>(p, stream);
+        case 8: return launch_decode_t<8, F16>(p, stream);
     }
     return hipErrorInvalidValue;
 }

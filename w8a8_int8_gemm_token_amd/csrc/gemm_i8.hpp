@@ -14,6 +14,8 @@
 //                weight scale per [128,128] block: each block's fp32 partial
 //                P_g is folded as f = fmaf(P_g, fl(s_x[m,g] * s_w[n/128,g]),
 //                f) in ascending g; y = bf16_rne(f)
+//   EPI_CHANNEL_F16, EPI_GROUP_ACT_F16: as EPI_CHANNEL and EPI_GROUP_ACT
+//                with fp16 (RNE) outputs
 //   EPI_I32:     the raw int32 acc
 // "Qwen3.8-27B -- SmoothQuant + activation-aware GPTQ, W8A8 INT8 (v3)",
 // sections "Recipe" and "Serving" (INT8 x INT8 with per-token x per-channel
@@ -64,7 +66,13 @@
 
 namespace q8 {
 
-enum { EPI_I32 = 0, EPI_CHANNEL = 1, EPI_GROUP = 2, EPI_GROUP_ACT = 3, EPI_FP8_BLOCK = 4 };
+enum { EPI_I32 = 0, EPI_CHANNEL = 1, EPI_GROUP = 2, EPI_GROUP_ACT = 3, EPI_FP8_BLOCK = 4,
+       EPI_CHANNEL_F16 = 5, EPI_GROUP_ACT_F16 = 6 };
+
+// The _F16 epilogues are EPI_CHANNEL and EPI_GROUP_ACT with fp16 outputs.
+constexpr int epi_base(int e) {
+    return e == EPI_CHANNEL_F16 ? EPI_CHANNEL : e == EPI_GROUP_ACT_F16 ? EPI_GROUP_ACT : e;
+}
 
 struct GemmArgs {
     const int8_t* x;  // activations (tokens) [M, ldx]
@@ -73,7 +81,7 @@ struct GemmArgs {
     int64_t ldw;
     const float* s_tok;  // [M]; EPI_GROUP_ACT, EPI_FP8_BLOCK: [M, K/128] per (token, block)
     const float* s_w;    // [N] per channel, [N, K/128] per group, or [N/128, K/128] per block
-    void* c;             // [M, ldc] bf16 bits, or int32
+    void* c;             // [M, ldc] bf16 (fp16 for the _F16 epilogues) bits, or int32
     int64_t ldc;
     int M, N, K;
 };
@@ -118,8 +126,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int GM>
+template <int BM, int BN, int WM, int WN, int EPI_, int GM>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
+    constexpr int EPI = epi_base(EPI_);
+    constexpr bool OUT_F16 = EPI_ != EPI;
     constexpr int BK = 128;
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -432,8 +442,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
                         }
                     }
                     v2u o;
-                    o[0] = pack_bf16x2(v[0], v[1]);
-                    o[1] = pack_bf16x2(v[2], v[3]);
+                    o[0] = pack16x2<OUT_F16>(v[0], v[1]);
+                    o[1] = pack16x2<OUT_F16>(v[2], v[3]);
                     *reinterpret_cast<v2u*>(static_cast<uint16_t*>(p.c) + (int64_t)j * p.ldc + ch) = o;
                 }
             }

@@ -55,13 +55,13 @@ inline q8_status check_scale(const float* s) {
 // are enough of them to fill the 256 CUs, 128 x 128 tiles in between.
 template <int EPI>
 hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
-    if constexpr (EPI == EPI_CHANNEL) {
+    if constexpr (EPI == EPI_CHANNEL || EPI == EPI_CHANNEL_F16) {
         // few tokens: stream the weights once, unless the tiled kernel already
         // has half a wave of tiles or more (M > 32 with many channels)
         const bool few = p.M <= 32 || ((p.N + 127) / 128) * ((p.M + 31) / 32) < 128;
         if (few && sg_fits(p.M, p.N, p.K, p.ldw, SG_MAX_M)) {
             const StreamArgs q{p.x, p.ldx, p.w, p.ldw, p.s_tok, p.s_w, static_cast<uint16_t*>(p.c), p.ldc,
-                               p.M, p.N, p.K, 0, 0};
+                               p.M, p.N, p.K, 0, 0, EPI == EPI_CHANNEL_F16 ? 1 : 0};
             return launch_stream<true>(q, s);
         }
     }
@@ -71,9 +71,10 @@ hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
     return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
 }
 
+template <int EPI>  // EPI_GROUP_ACT or EPI_GROUP_ACT_F16
 hipError_t run_gemm_group_act(const GemmArgs& p, hipStream_t s) {
-    if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI_GROUP_ACT, 8>(p, s);
-    return launch_gemm_i8<128, 128, 2, 2, EPI_GROUP_ACT, 8>(p, s);
+    if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
+    return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
 }
 
 hipError_t run_gemm_fp8_block(const GemmArgs& p, hipStream_t s) {
@@ -86,27 +87,100 @@ hipError_t run_gemm_group(const GemmArgs& p, hipStream_t s) {
     return launch_gemm_i8<128, 128, 2, 2, EPI_GROUP, 8>(p, s);
 }
 
+template <bool F16>
 hipError_t run_quant(const uint16_t* x, int64_t ldx, int8_t* xq, int64_t ldxq, float* s, int M,
                      int K, hipStream_t stream) {
     const dim3 grid((M + 3) / 4), block(256);
     const bool vec = K % 8 == 0 && ldx % 8 == 0 && ldxq % 8 == 0 && al(x, 16) && al(xq, 8);
+#define Q8_REG(n) hipLaunchKernelGGL((quant_per_token_reg<n, F16>), grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K)
     if (vec && M <= 256 && K <= 8 * 512 * 2)  // few rows: a workgroup per row
-        hipLaunchKernelGGL((quant_per_token_wg<512, 2>), dim3(M), dim3(512), 0, stream, x, ldx, xq, ldxq, s, K);
-    else if (vec && K <= 512)
-        hipLaunchKernelGGL(quant_per_token_reg<1>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
-    else if (vec && K <= 2048)
-        hipLaunchKernelGGL(quant_per_token_reg<4>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
-    else if (vec && K <= 3072)
-        hipLaunchKernelGGL(quant_per_token_reg<6>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
-    else if (vec && K <= 4096)
-        hipLaunchKernelGGL(quant_per_token_reg<8>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
-    else if (vec && K <= 5120)
-        hipLaunchKernelGGL(quant_per_token_reg<10>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
-    else if (vec && K <= 8192)
-        hipLaunchKernelGGL(quant_per_token_reg<16>, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
-    else
-        hipLaunchKernelGGL(quant_per_token_any, grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
+        hipLaunchKernelGGL((quant_per_token_wg<512, 2, F16>), dim3(M), dim3(512), 0, stream, x, ldx, xq, ldxq, s, K);
+    else if (vec && K <= 512) Q8_REG(1);
+    else if (vec && K <= 2048) Q8_REG(4);
+    else if (vec && K <= 3072) Q8_REG(6);
+    else if (vec && K <= 4096) Q8_REG(8);
+    else if (vec && K <= 5120) Q8_REG(10);
+    else if (vec && K <= 8192) Q8_REG(16);
+    else hipLaunchKernelGGL((quant_per_token_any<F16>), grid, block, 0, stream, x, ldx, xq, ldxq, s, M, K);
+#undef Q8_REG
     return hipGetLastError();
+}
+
+// Entry-point bodies shared by the bf16 and fp16 variants.
+template <bool F16>
+q8_status quant_per_token_impl(const uint16_t* x, int64_t ldx, int8_t* xq, int64_t ldxq,
+                               float* scale_tok, int64_t M, int64_t K, q8_stream stream) {
+    if (M < 0 || K < 0) return Q8_EINVAL;
+    if (M == 0) return Q8_OK;
+    if (!x || !xq || !scale_tok || K == 0 || ldx < K || ldxq < K) return Q8_EINVAL;
+    if (!al(x, 2) || !al(scale_tok, 4)) return Q8_EUNSUPPORTED;
+    if (M > INT32_MAX / 2 || K > INT32_MAX / 2) return Q8_EUNSUPPORTED;
+    return hip_status(run_quant<F16>(x, ldx, xq, ldxq, scale_tok, (int)M, (int)K, st(stream)));
+}
+
+template <bool F16>
+q8_status scaled_mm_impl(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
+                         const float* scale_tok, const float* scale_ch, uint16_t* c, int64_t ldc,
+                         int64_t M, int64_t N, int64_t K, q8_stream stream) {
+    q8_status r = check_gemm(a, lda, 16, b, ldb, c, ldc, 8, M, N, K);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_tok);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_ch);
+    if (r != Q8_OK || M == 0) return r;
+    GemmArgs p{a, lda, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};
+    return hip_status(run_gemm_i8<F16 ? EPI_CHANNEL_F16 : EPI_CHANNEL>(p, st(stream)));
+}
+
+template <bool F16>
+q8_status quant_scaled_mm_impl(const uint16_t* x, int64_t ldx, const int8_t* b, int64_t ldb,
+                               const float* scale_ch, uint16_t* c, int64_t ldc, int8_t* xq,
+                               float* scale_tok, int64_t M, int64_t N, int64_t K,
+                               q8_stream stream) {
+    q8_status r = check_gemm(x, ldx, 8, b, ldb, c, ldc, 8, M, N, K);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_ch);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_tok);
+    if (r == Q8_OK && M > 0 && !xq) r = Q8_EINVAL;
+    if (r == Q8_OK && M > 0 && !al(xq, 16)) r = Q8_EUNSUPPORTED;
+    if (r != Q8_OK || M == 0) return r;
+    hipStream_t s = st(stream);
+    if (decode_fits((int)M, (int)N, (int)K, ldb)) {
+        const DecodeArgs d{x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok,
+                           (int)M, (int)N, (int)K, decode_rows((int)N, (int)K)};
+        return hip_status(launch_decode<F16>(d, s));
+    }
+    hipError_t e = run_quant<F16>(x, ldx, xq, K, scale_tok, (int)M, (int)K, s);
+    if (e != hipSuccess) return Q8_EHIP;
+    GemmArgs p{xq, K, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};
+    return hip_status(run_gemm_i8<F16 ? EPI_CHANNEL_F16 : EPI_CHANNEL>(p, s));
+}
+
+template <bool F16>
+q8_status quant_per_group128_impl(const uint16_t* x, int64_t ldx, int8_t* xq, int64_t ldxq,
+                                  float* scale_grp, int64_t M, int64_t K, q8_stream stream) {
+    if (M < 0 || K < 0) return Q8_EINVAL;
+    if (M == 0) return Q8_OK;
+    if (!x || !xq || !scale_grp || K == 0 || ldx < K || ldxq < K) return Q8_EINVAL;
+    if (K % 128 != 0 || M > INT32_MAX / 2 || K > INT32_MAX / 2) return Q8_EUNSUPPORTED;
+    if (ldx % 8 != 0 || ldxq % 8 != 0 || !al(x, 16) || !al(xq, 8) || !al(scale_grp, 4))
+        return Q8_EUNSUPPORTED;
+    const int64_t waves = M * ((K + 511) / 512);
+    if ((waves + 3) / 4 > INT32_MAX) return Q8_EUNSUPPORTED;
+    hipLaunchKernelGGL((quant_per_group128_kernel<F16>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                       st(stream), x, ldx, xq, ldxq, scale_grp, (int)M, (int)K);
+    return hip_status(hipGetLastError());
+}
+
+template <bool F16>
+q8_status scaled_mm_group128_act_impl(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
+                                      const float* scale_x, const float* scale_w, uint16_t* c,
+                                      int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                      q8_stream stream) {
+    q8_status r = check_gemm(a, lda, 16, b, ldb, c, ldc, 8, M, N, K);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_x);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_w);
+    if (r != Q8_OK || M == 0) return r;
+    GemmArgs p{a, lda, b, ldb, scale_x, scale_w, c, ldc, (int)M, (int)N, (int)K};
+    if (!gemm_offsets_fit(p)) return Q8_EUNSUPPORTED;
+    return hip_status(run_gemm_group_act<F16 ? EPI_GROUP_ACT_F16 : EPI_GROUP_ACT>(p, st(stream)));
 }
 
 }  // namespace
@@ -125,23 +199,24 @@ const char* q8_status_str(q8_status s) {
 
 q8_status q8_quant_per_token(const q8_bf16* x, int64_t ldx, int8_t* xq, int64_t ldxq,
                              float* scale_tok, int64_t M, int64_t K, q8_stream stream) {
-    if (M < 0 || K < 0) return Q8_EINVAL;
-    if (M == 0) return Q8_OK;
-    if (!x || !xq || !scale_tok || K == 0 || ldx < K || ldxq < K) return Q8_EINVAL;
-    if (!al(x, 2) || !al(scale_tok, 4)) return Q8_EUNSUPPORTED;
-    if (M > INT32_MAX / 2 || K > INT32_MAX / 2) return Q8_EUNSUPPORTED;
-    return hip_status(run_quant(x, ldx, xq, ldxq, scale_tok, (int)M, (int)K, st(stream)));
+    return quant_per_token_impl<false>(x, ldx, xq, ldxq, scale_tok, M, K, stream);
+}
+
+q8_status q8_quant_per_token_f16(const q8_f16* x, int64_t ldx, int8_t* xq, int64_t ldxq,
+                                 float* scale_tok, int64_t M, int64_t K, q8_stream stream) {
+    return quant_per_token_impl<true>(x, ldx, xq, ldxq, scale_tok, M, K, stream);
 }
 
 q8_status q8_scaled_mm(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
                        const float* scale_tok, const float* scale_ch, q8_bf16* c, int64_t ldc,
                        int64_t M, int64_t N, int64_t K, q8_stream stream) {
-    q8_status r = check_gemm(a, lda, 16, b, ldb, c, ldc, 8, M, N, K);
-    if (r == Q8_OK && M > 0) r = check_scale(scale_tok);
-    if (r == Q8_OK && M > 0) r = check_scale(scale_ch);
-    if (r != Q8_OK || M == 0) return r;
-    GemmArgs p{a, lda, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};
-    return hip_status(run_gemm_i8<EPI_CHANNEL>(p, st(stream)));
+    return scaled_mm_impl<false>(a, lda, b, ldb, scale_tok, scale_ch, c, ldc, M, N, K, stream);
+}
+
+q8_status q8_scaled_mm_f16(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
+                           const float* scale_tok, const float* scale_ch, q8_f16* c, int64_t ldc,
+                           int64_t M, int64_t N, int64_t K, q8_stream stream) {
+    return scaled_mm_impl<true>(a, lda, b, ldb, scale_tok, scale_ch, c, ldc, M, N, K, stream);
 }
 
 q8_status q8_scaled_mm_group128(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
@@ -182,22 +257,14 @@ q8_status q8_quant_scaled_mm(const q8_bf16* x, int64_t ldx, const int8_t* b, int
                              const float* scale_ch, q8_bf16* c, int64_t ldc, int8_t* xq,
                              float* scale_tok, int64_t M, int64_t N, int64_t K,
                              q8_stream stream) {
-    q8_status r = check_gemm(x, ldx, 8, b, ldb, c, ldc, 8, M, N, K);
-    if (r == Q8_OK && M > 0) r = check_scale(scale_ch);
-    if (r == Q8_OK && M > 0) r = check_scale(scale_tok);
-    if (r == Q8_OK && M > 0 && !xq) r = Q8_EINVAL;
-    if (r == Q8_OK && M > 0 && !al(xq, 16)) r = Q8_EUNSUPPORTED;
-    if (r != Q8_OK || M == 0) return r;
-    hipStream_t s = st(stream);
-    if (decode_fits((int)M, (int)N, (int)K, ldb)) {
-        const DecodeArgs d{x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok,
-                           (int)M, (int)N, (int)K, decode_rows((int)N, (int)K)};
-        return hip_status(launch_decode(d, s));
-    }
-    hipError_t e = run_quant(x, ldx, xq, K, scale_tok, (int)M, (int)K, s);
-    if (e != hipSuccess) return Q8_EHIP;
-    GemmArgs p{xq, K, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};
-    return hip_status(run_gemm_i8<EPI_CHANNEL>(p, s));
+    return quant_scaled_mm_impl<false>(x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok, M, N, K, stream);
+}
+
+q8_status q8_quant_scaled_mm_f16(const q8_f16* x, int64_t ldx, const int8_t* b, int64_t ldb,
+                                 const float* scale_ch, q8_f16* c, int64_t ldc, int8_t* xq,
+                                 float* scale_tok, int64_t M, int64_t N, int64_t K,
+                                 q8_stream stream) {
+    return quant_scaled_mm_impl<true>(x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok, M, N, K, stream);
 }
 
 q8_status q8_quant_weight(const float* w, int64_t ldw, int8_t* wq, int64_t ldwq, float* scale,
@@ -255,30 +322,26 @@ q8_status q8_rmsnorm_quant(const q8_bf16* x, int64_t ldx, q8_bf16* residual, int
 
 q8_status q8_quant_per_group128(const q8_bf16* x, int64_t ldx, int8_t* xq, int64_t ldxq,
                                 float* scale_grp, int64_t M, int64_t K, q8_stream stream) {
-    if (M < 0 || K < 0) return Q8_EINVAL;
-    if (M == 0) return Q8_OK;
-    if (!x || !xq || !scale_grp || K == 0 || ldx < K || ldxq < K) return Q8_EINVAL;
-    if (K % 128 != 0 || M > INT32_MAX / 2 || K > INT32_MAX / 2) return Q8_EUNSUPPORTED;
-    if (ldx % 8 != 0 || ldxq % 8 != 0 || !al(x, 16) || !al(xq, 8) || !al(scale_grp, 4))
-        return Q8_EUNSUPPORTED;
-    const int64_t waves = M * ((K + 511) / 512);
-    if ((waves + 3) / 4 > INT32_MAX) return Q8_EUNSUPPORTED;
-    hipLaunchKernelGGL(quant_per_group128_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
-                       st(stream), x, ldx, xq, ldxq, scale_grp, (int)M, (int)K);
-    return hip_status(hipGetLastError());
+    return quant_per_group128_impl<false>(x, ldx, xq, ldxq, scale_grp, M, K, stream);
+}
+
+q8_status q8_quant_per_group128_f16(const q8_f16* x, int64_t ldx, int8_t* xq, int64_t ldxq,
+                                    float* scale_grp, int64_t M, int64_t K, q8_stream stream) {
+    return quant_per_group128_impl<true>(x, ldx, xq, ldxq, scale_grp, M, K, stream);
 }
 
 q8_status q8_scaled_mm_group128_act(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
                                     const float* scale_x, const float* scale_w, q8_bf16* c,
                                     int64_t ldc, int64_t M, int64_t N, int64_t K,
                                     q8_stream stream) {
-    q8_status r = check_gemm(a, lda, 16, b, ldb, c, ldc, 8, M, N, K);
-    if (r == Q8_OK && M > 0) r = check_scale(scale_x);
-    if (r == Q8_OK && M > 0) r = check_scale(scale_w);
-    if (r != Q8_OK || M == 0) return r;
-    GemmArgs p{a, lda, b, ldb, scale_x, scale_w, c, ldc, (int)M, (int)N, (int)K};
-    if (!gemm_offsets_fit(p)) return Q8_EUNSUPPORTED;
-    return hip_status(run_gemm_group_act(p, st(stream)));
+    return scaled_mm_group128_act_impl<false>(a, lda, b, ldb, scale_x, scale_w, c, ldc, M, N, K, stream);
+}
+
+q8_status q8_scaled_mm_group128_act_f16(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
+                                        const float* scale_x, const float* scale_w, q8_f16* c,
+                                        int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                        q8_stream stream) {
+    return scaled_mm_group128_act_impl<true>(a, lda, b, ldb, scale_x, scale_w, c, ldc, M, N, K, stream);
 }
 
 q8_status q8_quant_fp8_per_group128(const q8_bf16* x, int64_t ldx, uint8_t* xq, int64_t ldxq,

@@ -29,6 +29,30 @@ __device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
     return (u32)f32_to_bf16(lo) | ((u32)f32_to_bf16(hi) << 16);
 }
 
+// fp16 bits -> fp32 (exact) and fp32 -> fp16 bits, round to nearest even
+// (v_cvt_f16_f32 under the default rounding mode, fp16 denormals kept).
+__device__ __forceinline__ float f16_lo(u32 w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float f16_hi(u32 w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+__device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ u32 pack_f16x2(float lo, float hi) {
+    return (u32)f32_to_f16(lo) | ((u32)f32_to_f16(hi) << 16);
+}
+
+// The 16-bit activation / output formats of the layer: bf16 (F16 = false)
+// or IEEE fp16 (F16 = true).
+template <bool F16>
+__device__ __forceinline__ float h16_lo(u32 w) { if constexpr (F16) return f16_lo(w); else return bf16_lo(w); }
+template <bool F16>
+__device__ __forceinline__ float h16_hi(u32 w) { if constexpr (F16) return f16_hi(w); else return bf16_hi(w); }
+template <bool F16>
+__device__ __forceinline__ float h16_to_f32(uint16_t b) {
+    if constexpr (F16) return (float)__builtin_bit_cast(_Float16, b); else return bf16_to_f32(b);
+}
+template <bool F16>
+__device__ __forceinline__ u32 pack16x2(float lo, float hi) {
+    if constexpr (F16) return pack_f16x2(lo, hi); else return pack_bf16x2(lo, hi);
+}
+
 // Symmetric INT8 code of x for scale s: clamp(rne(x / s), -127, 127), with
 // x / s the correctly rounded fp32 quotient (IEEE division; the library is
 // built without fast-math so '/' is exact-rounded).  s == 0 gives 0.

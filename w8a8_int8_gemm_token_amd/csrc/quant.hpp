@@ -6,14 +6,18 @@
 // "Qwen3.8-27B-INT8-W8A8", section "Quantization"): per row, scale =
 // absmax/127 (one correctly rounded division), code = clamp(rne(x/scale),
 // -127, 127).  HBM-bound: one read of the bf16 row, one write of the codes.
+// The kernels take bf16 rows, or fp16 rows with F16 = true (the fp16
+// variant: "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", "Serving (vLLM, gfx908
+// fork)", where the model runs in half precision).
 #pragma once
 
 #include "q8_device.hpp"
 
 namespace q8 {
 
-// Running max of |x| over bf16 values, kept as two 16-bit magnitudes: for
-// finite bf16 the magnitude bits (sign cleared) order the same way as |x|,
+// Running max of |x| over bf16 (or fp16) values, kept as two 16-bit
+// magnitudes: for finite values the magnitude bits (sign cleared) order the
+// same way as |x|,
 // so a packed unsigned max gives the exact absmax at one VALU op per value.
 typedef unsigned short v2h __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ v2h mag_max8(v2h acc, v4u v) {
@@ -22,9 +26,10 @@ __device__ __forceinline__ v2h mag_max8(v2h acc, v4u v) {
         acc = __builtin_elementwise_max(acc, __builtin_bit_cast(v2h, v[e] & 0x7FFF7FFFu));
     return acc;
 }
+template <bool F16 = false>
 __device__ __forceinline__ float mag_to_f32(v2h acc) {
     const u32 m = acc[0] > acc[1] ? acc[0] : acc[1];
-    return __uint_as_float(m << 16);
+    return h16_to_f32<F16>((uint16_t)m);
 }
 
 // Maximum of a non-negative float over the 16 lanes of each DPP row (lanes
@@ -38,14 +43,15 @@ __device__ __forceinline__ float row16_max(float a) {
     return a;
 }
 
-// The 8 codes of the 8 bf16 values in v, packed little-endian, each with a
+// The 8 codes of the 8 bf16 (or fp16) values in v, packed little-endian, each with a
 // full IEEE division (the reference route).
+template <bool F16 = false>
 __device__ __forceinline__ v2u codes8_div(v4u v, float s) {
     v2u r;
-    r[0] = pack_i8x4(code_of(bf16_lo(v[0]), s), code_of(bf16_hi(v[0]), s),
-                    code_of(bf16_lo(v[1]), s), code_of(bf16_hi(v[1]), s));
-    r[1] = pack_i8x4(code_of(bf16_lo(v[2]), s), code_of(bf16_hi(v[2]), s),
-                    code_of(bf16_lo(v[3]), s), code_of(bf16_hi(v[3]), s));
+    r[0] = pack_i8x4(code_of(h16_lo<F16>(v[0]), s), code_of(h16_hi<F16>(v[0]), s),
+                    code_of(h16_lo<F16>(v[1]), s), code_of(h16_hi<F16>(v[1]), s));
+    r[1] = pack_i8x4(code_of(h16_lo<F16>(v[2]), s), code_of(h16_hi<F16>(v[2]), s),
+                    code_of(h16_lo<F16>(v[3]), s), code_of(h16_hi<F16>(v[3]), s));
     return r;
 }
 
@@ -74,8 +80,9 @@ __device__ __forceinline__ RowScale row_scale(float absmax) {
 // quotient fl(x/s) lies strictly within 0.5 of n and rounds to n.  Any other
 // element (a near-tie, about one in 30000) is recomputed by division on its
 // own.  |x*r| < 127.5 on the fast route, so no clamp is needed there.
+template <bool F16 = false>
 __device__ __forceinline__ v2u codes8(v4u v, const RowScale& q) {
-    if (!q.fast) return codes8_div(v, q.s);
+    if (!q.fast) return codes8_div<F16>(v, q.s);
     constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
     constexpr float TIE_LO = 0.5f - 0x1p-16f;
     u32 b[8];
@@ -83,7 +90,7 @@ __device__ __forceinline__ v2u codes8(v4u v, const RowScale& q) {
     float dmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
+        const float x = (e & 1) ? h16_hi<F16>(v[e >> 1]) : h16_lo<F16>(v[e >> 1]);
         const float m = __builtin_fmaf(x, q.r, MAGIC);
         d[e] = __builtin_fmaf(x, q.r, MAGIC - m);  // MAGIC - m = -n exactly
         dmax = __builtin_fmaxf(dmax, __builtin_fabsf(d[e]));
@@ -96,7 +103,7 @@ __device__ __forceinline__ v2u codes8(v4u v, const RowScale& q) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             if (__builtin_fabsf(d[e]) > TIE_LO) {
-                const float x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
+                const float x = (e & 1) ? h16_hi<F16>(v[e >> 1]) : h16_lo<F16>(v[e >> 1]);
                 const u32 sh = 8 * (e & 3);
                 r[e >> 2] = (r[e >> 2] & ~(0xFFu << sh)) | ((u32)(code_of(x, q.s) & 0xFF) << sh);
             }
@@ -111,6 +118,7 @@ __device__ __forceinline__ v2u codes8(v4u v, const RowScale& q) {
 // block g of the span (one DPP row), whose absmax takes four row rotations.
 // K % 128 == 0; 16-byte aligned x rows, 8-byte aligned xq rows; s [M, K/128]
 // dense.
+template <bool F16 = false>
 __global__ __launch_bounds__(256) void quant_per_group128_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int8_t* __restrict__ xq, int64_t ldxq,
     float* __restrict__ s, int M, int K) {
@@ -123,17 +131,17 @@ __global__ __launch_bounds__(256) void quant_per_group128_kernel(
     const bool ok = c < (K >> 3);
     v4u v = v4u{};
     if (ok) v = reinterpret_cast<const v4u*>(x + (int64_t)m * ldx)[c];
-    const float a = row16_max(mag_to_f32(mag_max8(v2h{0, 0}, v)));
+    const float a = row16_max(mag_to_f32<F16>(mag_max8(v2h{0, 0}, v)));
     const RowScale q = row_scale(a);
     if (!ok) return;
-    reinterpret_cast<v2u*>(xq + (int64_t)m * ldxq)[c] = codes8(v, q);
+    reinterpret_cast<v2u*>(xq + (int64_t)m * ldxq)[c] = codes8<F16>(v, q);
     if ((lane & 15) == 0) s[(int64_t)m * (K >> 7) + (c >> 4)] = q.s;
 }
 
 // One wave per row; the row stays in registers (NC 16-byte chunks per lane,
 // K <= NC * 512).  Needs K % 8 == 0, 16-byte aligned x rows and 8-byte
 // aligned xq rows.  4 rows per 256-thread workgroup.
-template <int NC>
+template <int NC, bool F16 = false>
 __global__ __launch_bounds__(256) void quant_per_token_reg(
     const uint16_t* __restrict__ x, int64_t ldx, int8_t* __restrict__ xq, int64_t ldxq,
     float* __restrict__ s_tok, int M, int K) {
@@ -152,21 +160,21 @@ __global__ __launch_bounds__(256) void quant_per_token_reg(
             mx = mag_max8(mx, v[i]);
         }
     }
-    const float a = wave_max(mag_to_f32(mx));
+    const float a = wave_max(mag_to_f32<F16>(mx));
     const RowScale q = row_scale(a);
     if (lane == 0) s_tok[m] = q.s;
     v2u* qr = reinterpret_cast<v2u*>(xq + (int64_t)m * ldxq);
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int c = lane + 64 * i;
-        if (c < nch) qr[c] = codes8(v[i], q);
+        if (c < nch) qr[c] = codes8<F16>(v[i], q);
     }
 }
 
 // One workgroup (NT threads) per row, CPT 16-byte chunks per thread held in
 // registers (K <= 8 * NT * CPT): for few rows, where spreading each row over
 // a whole workgroup is what shortens the call.
-template <int NT, int CPT>
+template <int NT, int CPT, bool F16 = false>
 __global__ __launch_bounds__(NT) void quant_per_token_wg(
     const uint16_t* __restrict__ x, int64_t ldx, int8_t* __restrict__ xq, int64_t ldxq,
     float* __restrict__ s_tok, int K) {
@@ -184,7 +192,7 @@ __global__ __launch_bounds__(NT) void quant_per_token_wg(
             mx = mag_max8(mx, v[i]);
         }
     }
-    float a = wave_max(mag_to_f32(mx));
+    float a = wave_max(mag_to_f32<F16>(mx));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
     __syncthreads();
 #pragma unroll
@@ -195,11 +203,12 @@ __global__ __launch_bounds__(NT) void quant_per_token_wg(
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
         const int c = threadIdx.x + NT * i;
-        if (c < nch) qr[c] = codes8(v[i], q);
+        if (c < nch) qr[c] = codes8<F16>(v[i], q);
     }
 }
 
 // Any K, any alignment: one wave per row, two passes over the row.
+template <bool F16 = false>
 __global__ __launch_bounds__(256) void quant_per_token_any(
     const uint16_t* __restrict__ x, int64_t ldx, int8_t* __restrict__ xq, int64_t ldxq,
     float* __restrict__ s_tok, int M, int K) {
@@ -208,12 +217,12 @@ __global__ __launch_bounds__(256) void quant_per_token_any(
     if (m >= M) return;
     const uint16_t* xr = x + (int64_t)m * ldx;
     float a = 0.0f;
-    for (int k = lane; k < K; k += 64) a = __builtin_fmaxf(a, __builtin_fabsf(bf16_to_f32(xr[k])));
+    for (int k = lane; k < K; k += 64) a = __builtin_fmaxf(a, __builtin_fabsf(h16_to_f32<F16>(xr[k])));
     a = wave_max(a);
     const float s = a / 127.0f;
     if (lane == 0) s_tok[m] = s;
     int8_t* qr = xq + (int64_t)m * ldxq;
-    for (int k = lane; k < K; k += 64) qr[k] = (int8_t)code_of(bf16_to_f32(xr[k]), s);
+    for (int k = lane; k < K; k += 64) qr[k] = (int8_t)code_of(h16_to_f32<F16>(xr[k]), s);
 }
 
 // Offline weight quantization: one workgroup per (row, span of G columns).

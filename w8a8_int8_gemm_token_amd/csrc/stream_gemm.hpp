@@ -1,6 +1,7 @@
 // stream_gemm.hpp -- GEMMs for a few tokens (M <= 64), which stream the
 // weight matrix once and are bound by HBM bandwidth:
 //   I8 (W8A8):  y[m,n] = bf16_rne(((float)sum_k xq[m,k]*w[n,k] * s_tok[m]) * s_ch[n])
+//               (or fp16_rne: the fp16 variant of the layer)
 //               exact int32 sums of the per-token codes
 //   bf16 (W8A16): y[m,n] = bf16_rne(s_ch[n] * sum_k x[m,k] * bf16(w[n,k]))
 // "Qwen3.8-27B -- SmoothQuant + activation-aware GPTQ, W8A8 INT8 (v3)",
@@ -57,11 +58,12 @@ struct StreamArgs {
     int64_t ldw;
     const float* s_tok;  // [M] (I8 only)
     const float* s_ch;   // [N]
-    uint16_t* c;         // [M, ldc] bf16
+    uint16_t* c;         // [M, ldc] bf16, or fp16 when out_f16
     int64_t ldc;
     int M, N, K;
     int rows;  // channels per workgroup (multiple of 4, <= 32)
     int nbuf;  // segment slots in the ring
+    int out_f16;  // I8 only: fp16 outputs (RNE) instead of bf16
 };
 
 // Three slots: a deeper ring issues most of a short K at once, and the
@@ -277,8 +279,13 @@ __global__ __launch_bounds__(1024) void stream_gemm_kernel(StreamArgs p) {
         }
     }
     v2u o;
-    o[0] = pack_bf16x2(y[0], y[1]);
-    o[1] = pack_bf16x2(y[2], y[3]);
+    if (p.out_f16) {
+        o[0] = pack_f16x2(y[0], y[1]);
+        o[1] = pack_f16x2(y[2], y[3]);
+    } else {
+        o[0] = pack_bf16x2(y[0], y[1]);
+        o[1] = pack_bf16x2(y[2], y[3]);
+    }
     *reinterpret_cast<v2u*>(p.c + (int64_t)em * p.ldc + ch) = o;
 }
 
