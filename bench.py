@@ -56,11 +56,11 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 # taken on: if those files change, the figure is withdrawn (null).
 GEMM_COUNTERS = {
     "sources_sha256": {
-        "gemm_i8.hpp": "ff7dc6ccb81d5223208da4e788a5e8aa420251dc67873fd7e34212f84af1f7ca",
-        "q8_device.hpp": "d4f2127e64227715d4ae11d84ffb5c1eb2a7e41146be4eadd6ffe7108b6cdd45",
+        "gemm_i8.hpp": "7fc39c836f556d5465ed227fdcc406402c68546723fa512ae5fcc19a09687e66",
+        "q8_device.hpp": "3828c206a8ddac44b2de7061ea1095197c3eeae4e5210af3b56cec58b509b088",
     },
-    "fetch_kib": 491279.6, "write_kib": 253353.6,
-    "copy_kib": 524288.0, "copy_fetch_kib": 262157.6, "copy_write_kib": 524288.0,
+    "fetch_kib": 491231.2, "write_kib": 253263.7,
+    "copy_kib": 524288.0, "copy_fetch_kib": 262157.7, "copy_write_kib": 524288.0,
 }
 
 
@@ -261,7 +261,7 @@ def group_act_tops(dev, iters=20):
             "quant_us": qms * 1e3, "quant_GB/s": qbytes / (qms * 1e-3) / 1e9}
 
 
-def fp8_block_tflops(dev, iters=10):
+def fp8_block_tflops(dev, iters=20):
     """FP8 block W8A8 at the prefill shape: per-token-per-group E4M3
     activation quant + the [128,128] block-scaled FP8 GEMM.  GEMM, quant and
     the whole step are timed separately with events."""
@@ -280,7 +280,7 @@ def fp8_block_tflops(dev, iters=10):
     def step():
         qf()
         g()
-    for _ in range(2):
+    for _ in range(5):
         step()
     gms = events_time(g, iters)
     qms = events_time(qf, iters)
@@ -294,7 +294,7 @@ def fp8_block_tflops(dev, iters=10):
             "shape": [wl.M, wl.N, wl.K]}
 
 
-def f16_layer(dev, iters=10):
+def f16_layer(dev, iters=20):
     """The fp16 variant of the one-call layer (fp16 in, fp16 out): the
     prefill shape timed with events, and M=8 decode per call in a HIP graph
     over weight copies (as the bf16 decode line)."""
@@ -307,7 +307,7 @@ def f16_layer(dev, iters=10):
     xq = torch.empty((wl.M, wl.K), dtype=torch.int8, device=dev)
     st = torch.empty((wl.M,), dtype=torch.float32, device=dev)
     f = lambda: q8.q8_quant_scaled_mm_f16(x, wq, sc, out=y, xq_out=xq, scale_tok_out=st)  # noqa: E731
-    for _ in range(2):
+    for _ in range(5):
         f()
     ms = events_time(f, iters)
     ops = 2.0 * wl.M * wl.N * wl.K
