@@ -194,7 +194,7 @@ def group_tops(dev, iters=20):
     return {"us": ms * 1e3, "TOPS": t, "frac_int8_peak": t / PEAK_INT8_TOPS}
 
 
-def w8a16_tflops(dev, iters=10):
+def w8a16_tflops(dev, iters=20):
     wl = synth.WORKLOADS["w8a16"]
     x = synth.activations(wl, 0).to(dev)
     w = synth.weights(wl, 0).to(dev)
@@ -202,7 +202,7 @@ def w8a16_tflops(dev, iters=10):
     del w
     y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
     f = lambda: q8.w8a16_mm(x, wq, sc, out=y)  # noqa: E731
-    for _ in range(2):
+    for _ in range(5):
         f()
     ms = events_time(f, iters)
     t = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12

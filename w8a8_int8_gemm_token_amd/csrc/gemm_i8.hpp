@@ -16,6 +16,9 @@
 //                f) in ascending g; y = bf16_rne(f)
 //   EPI_CHANNEL_F16, EPI_GROUP_ACT_F16: as EPI_CHANNEL and EPI_GROUP_ACT
 //                with fp16 (RNE) outputs
+//   EPI_W8A16:   bf16 activations (x, ldx in bytes) times int8 weights on
+//                v_mfma_f32_32x32x16_bf16: y = bf16_rne(s_ch[n] * acc), acc
+//                the fp32 MFMA sum of x[m,k] * bf16(w[n,k])
 //   EPI_I32:     the raw int32 acc
 // "Qwen3.8-27B -- SmoothQuant + activation-aware GPTQ, W8A8 INT8 (v3)",
 // sections "Recipe" and "Serving" (INT8 x INT8 with per-token x per-channel
@@ -67,7 +70,7 @@
 namespace q8 {
 
 enum { EPI_I32 = 0, EPI_CHANNEL = 1, EPI_GROUP = 2, EPI_GROUP_ACT = 3, EPI_FP8_BLOCK = 4,
-       EPI_CHANNEL_F16 = 5, EPI_GROUP_ACT_F16 = 6 };
+       EPI_CHANNEL_F16 = 5, EPI_GROUP_ACT_F16 = 6, EPI_W8A16 = 7 };
 
 // The _F16 epilogues are EPI_CHANNEL and EPI_GROUP_ACT with fp16 outputs.
 constexpr int epi_base(int e) {
@@ -134,7 +137,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int XIW = BM / 8 / NW, WIW = BN / 8 / NW;  // 8-row loads per wave and stage
+    constexpr bool W16 = EPI == EPI_W8A16;
+    // K elements per stage: 128 bytes of LDS row hold 128 codes or 64 bf16
+    constexpr int KS = W16 ? 64 : 128;
+    constexpr int XIW = BM / 8 / NW;                // 8-row direct loads per wave and stage
+    constexpr int WIW = W16 ? 0 : BN / 8 / NW;
+    // W8A16: the int8 weight tile (BN rows x 64 bytes) comes through registers,
+    // WLC 16-byte loads per thread, and is written to LDS as bf16
+    constexpr int WLC = W16 ? BN * 4 / (NW * 64) : 0;
     constexpr bool F8 = EPI == EPI_FP8_BLOCK;
     constexpr bool GRP = EPI == EPI_GROUP || EPI == EPI_GROUP_ACT;
     constexpr bool FOLD = GRP || F8;                       // per-block fp32 fold
@@ -142,16 +152,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     constexpr int SGI = GRP ? BN / 64 : 0;             // 64-scale weight loads per stage
     constexpr int SXI = ACT ? (BM + 63) / 64 : 0;      // 64-scale activation loads per stage
     constexpr int XOFF = GRP ? BN : 0;                 // activation scales in a stage's block
-    constexpr int LPS = XIW + WIW + (SGI + NW - 1) / NW + (SXI + NW - 1) / NW;
+    constexpr int LPS = XIW + WIW + WLC + (SGI + NW - 1) / NW + (SXI + NW - 1) / NW;
     constexpr int LSN = FOLD ? XOFF + SXI * 64 : 4;    // scale floats per stage
     constexpr int NR = (F8 ? 2 : 1) * (TM + TN);  // fragment reads (16 bytes) per sub-step
     constexpr int NM = TM * TN;  // MFMAs per sub-step
     constexpr int NM0 = NM / 2;  // MFMAs of sub-step 3 before the hand-over
     static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "tile shape");
-    static_assert(XIW * 8 * NW == BM && WIW * 8 * NW == BN, "load split");
+    static_assert(XIW * 8 * NW == BM && (W16 ? WLC * NW * 64 == BN * 4 : WIW * 8 * NW == BN), "load split");
     static_assert(!GRP || BN % 64 == 0, "group scales load 64 at a time");
     static_assert(!F8 || (WTN <= 128 && 128 % WTN == 0), "a wave's channels share one weight block");
-    using AccT = std::conditional_t<F8, v16f, v16i>;
+    using AccT = std::conditional_t<F8 || W16, v16f, v16i>;
     using FragT = std::conditional_t<F8, v8i, v4i>;
 
     __shared__ __attribute__((aligned(1024))) int8_t lx0[BM * BK];
@@ -197,8 +207,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     const __amdgpu_buffer_rsrc_t sxr = make_rsrc(p.s_tok, (uint32_t)((int64_t)M * G * 4));
     const int svx = (m0 + lane) * G * 4;  // activation block scales: token m0 + 64*i + lane
 
+    v4i wreg[W16 ? WLC : 1];
     auto issue = [&](int kt, int8_t* bx, int8_t* bw, float* bs) __attribute__((always_inline)) {
         const int koff = kt * BK;
+        if constexpr (W16) {  // first, so that a wait for them can leave the tile loads in flight
+#pragma unroll
+            for (int i = 0; i < WLC; ++i) {
+                const int c = (int)threadIdx.x + i * NW * 64, r = c >> 2, q = c & 3;
+                wreg[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      wr, (n0 + r) * (int)p.ldw + q * 16, kt * 64, 0));
+            }
+        }
 #pragma unroll
         for (int i = 0; i < XIW; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -225,6 +244,23 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
                 if (j < SXI)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(sxr, (Q8_LDS void*)(bs + XOFF + j * 64), 4,
                                                              svx, j * 64 * G * 4 + kt * 4, 0, 0);
+            }
+        }
+    };
+
+    // W8A16: the staged int8 weights of a stage -> exact bf16 (|q| <= 128) in
+    // the swizzled LDS layout: 16 codes of row r, K chunk q, become the bf16
+    // chunks 2q and 2q + 1 of that row.
+    auto wstore = [&](int8_t* bw) __attribute__((always_inline)) {
+        if constexpr (W16) {
+#pragma unroll
+            for (int i = 0; i < WLC; ++i) {
+                const int c = (int)threadIdx.x + i * NW * 64, r = c >> 2, q = c & 3;
+                const v2u a0 = i8x4_to_bf16x4((u32)wreg[i][0]), a1 = i8x4_to_bf16x4((u32)wreg[i][1]);
+                const v2u a2 = i8x4_to_bf16x4((u32)wreg[i][2]), a3 = i8x4_to_bf16x4((u32)wreg[i][3]);
+                const int f = lds_swizzle(r);
+                *reinterpret_cast<v4u*>(bw + r * BK + (((2 * q) ^ f) << 4)) = v4u{a0[0], a0[1], a1[0], a1[1]};
+                *reinterpret_cast<v4u*>(bw + r * BK + (((2 * q + 1) ^ f) << 4)) = v4u{a2[0], a2[1], a3[0], a3[1]};
             }
         }
     };
@@ -291,6 +327,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
             if constexpr (F8)  // A and B in E4M3 (format 0), no block exponents
                 acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     fw[set][b], fx[set][a], fresh ? AccT{} : acc[a][b], 0, 0, 0, 0, 0, 0);
+            else if constexpr (W16)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fw[set][b]),
+                                                                    __builtin_bit_cast(v8bf, fx[set][a]),
+                                                                    acc[a][b], 0, 0, 0);
             else
                 acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[set][b], fx[set][a], fresh ? AccT{} : acc[a][b],
                                                                   0, 0, 0);
@@ -387,6 +427,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
             } else {
                 mfma(1, 0, NM0);
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (W16) {  // this thread's weight loads landed: convert them into nw
+                    wait_vm_lgkm0<XIW>();
+                    wstore(nw);
+                }
                 wait_vm_lgkm0<0>();
                 block_barrier();
                 read(0, 0, nx, nw);
@@ -397,8 +441,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
         }
     };
 
-    const int KT = K / BK;
+    const int KT = K / KS;
     issue(0, lx0, lw0, ls0);
+    wait_vm_lgkm0<0>();
+    wstore(lw0);
     wait_vm_lgkm0<0>();
     block_barrier();
     read(0, 0, lx0, lw0);
@@ -437,6 +483,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
                             v[e] = t * p.s_w[ch + e];
                         } else if constexpr (EPI == EPI_GROUP) {
                             v[e] = facc[a][b][g * 4 + e] * st;
+                        } else if constexpr (W16) {
+                            v[e] = p.s_w[ch + e] * acc[a][b][g * 4 + e];
                         } else {
                             v[e] = facc[a][b][g * 4 + e];
                         }

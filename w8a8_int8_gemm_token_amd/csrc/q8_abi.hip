@@ -248,9 +248,17 @@ q8_status w8a16_mm(const q8_bf16* x, int64_t ldx, const int8_t* w, int64_t ldw,
         const StreamArgs q{x, ldx, w, ldw, nullptr, scale_ch, c, ldc, (int)M, (int)N, (int)K, 0, 0};
         return hip_status(launch_stream<false>(q, st(stream)));
     }
-    W8A16Args p{x, ldx, w, ldw, scale_ch, c, ldc, (int)M, (int)N, (int)K};
-    if (M <= 64) return hip_status(launch_w8a16<32, 128, 64, 1, 4, 8>(p, st(stream)));
-    return hip_status(launch_w8a16<128, 128, 64, 2, 2, 8>(p, st(stream)));
+    if (M <= 64) {
+        W8A16Args p{x, ldx, w, ldw, scale_ch, c, ldc, (int)M, (int)N, (int)K};
+        return hip_status(launch_w8a16<32, 128, 64, 1, 4, 8>(p, st(stream)));
+    }
+    // the tiled kernel's bf16 mode: activations addressed in bytes
+    GemmArgs p{reinterpret_cast<const int8_t*>(x), 2 * ldx, w, ldw, nullptr, scale_ch, c, ldc,
+               (int)M, (int)N, (int)K};
+    if (!gemm_offsets_fit(p)) return Q8_EUNSUPPORTED;
+    const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
+    if (tiles >= 256) return hip_status(launch_gemm_i8<256, 128, 4, 2, EPI_W8A16, 8>(p, st(stream)));
+    return hip_status(launch_gemm_i8<128, 128, 2, 2, EPI_W8A16, 8>(p, st(stream)));
 }
 
 q8_status q8_quant_scaled_mm(const q8_bf16* x, int64_t ldx, const int8_t* b, int64_t ldb,

@@ -68,6 +68,17 @@ __device__ __forceinline__ u32 pack_i8x4(int a, int b, int c, int d) {
            ((u32)(d & 0xFF) << 24);
 }
 
+// 4 int8 codes (one dword) -> 4 exact bf16 values (two dwords).
+__device__ __forceinline__ v2u i8x4_to_bf16x4(u32 d) {
+    const float f0 = (float)(int8_t)(d & 0xFF);
+    const float f1 = (float)(int8_t)((d >> 8) & 0xFF);
+    const float f2 = (float)(int8_t)((d >> 16) & 0xFF);
+    const float f3 = (float)(int8_t)(d >> 24);
+    // the conversions are exact, so truncating to the top 16 bits is exact
+    return v2u{(__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u),
+               (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u)};
+}
+
 // Wave-wide (64 lanes) maximum of a non-negative float.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

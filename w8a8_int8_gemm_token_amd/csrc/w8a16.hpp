@@ -6,6 +6,9 @@
 // activations); "lued/Qwen3.8-27B-INT8-W8A16-MTP", section "Why W8A16 on
 // Ampere" (weight-only kernels rebuild the weights for a 16-bit GEMM).
 //
+// This kernel serves M <= 64 when the weight-streaming kernel does not apply;
+// larger M runs the tiled INT8 GEMM's bf16 mode (EPI_W8A16 in gemm_i8.hpp).
+//
 // Design: same tile/wave structure as the INT8 GEMM.  The int8 weight tile
 // is read from HBM as int8 (half the bytes of bf16) and converted exactly to
 // bf16 once per workgroup while it is written to LDS (|q| <= 128 fits bf16's
@@ -28,17 +31,6 @@ struct W8A16Args {
     int64_t ldc;
     int M, N, K;
 };
-
-// 4 int8 codes (one dword) -> 4 exact bf16 values (two dwords).
-__device__ __forceinline__ v2u i8x4_to_bf16x4(u32 d) {
-    const float f0 = (float)(int8_t)(d & 0xFF);
-    const float f1 = (float)(int8_t)((d >> 8) & 0xFF);
-    const float f2 = (float)(int8_t)((d >> 16) & 0xFF);
-    const float f3 = (float)(int8_t)(d >> 24);
-    // the conversions are exact, so truncating to the top 16 bits is exact
-    return v2u{(__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u),
-               (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u)};
-}
 
 template <int BM, int BN, int BK, int WM, int WN, int GM>
 __global__ __launch_bounds__(WM* WN * 64) void w8a16_kernel(W8A16Args p) {
