@@ -488,6 +488,26 @@ def test_group128_shapes(M, N, K):
     assert_ulp1(bits(host(y)), y_ref, f"group128 {M}x{N}x{K}")
 
 
+def test_group_scaled_large_tiles_ragged():
+    """Enough tiles for the 256 x 128 group-scaled configuration, with a
+    ragged last tile in M and in N: both group-scaled epilogues, sampled
+    rows (including the ragged ones) against the oracle."""
+    M, N, K = 2100, 3728, 640
+    say("group-scaled large tiles", M, N, K)
+    x, w = synth.custom(M, K, N, seed=97, outlier_cols=5)
+    rows = np.array([0, 1, 255, 256, 1023, 2047, 2048, 2098, 2099, 777])
+    wq_ref, sg_ref = oracle.quant_weight(w.numpy(), group=128)
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq, sg = q8.q8_quant_weight(dev(w), group=128)
+    y = q8.q8_scaled_mm_group128(dev(xq_ref), wq, dev(st_ref), sg)
+    y_ref = oracle.scaled_mm_group128(xq_ref[rows], wq_ref, st_ref[rows], sg_ref)
+    assert_ulp1(bits(host(y))[rows], y_ref, "group128 large tiles")
+    xg_ref, sx_ref = oracle.quant_per_group128(bits(x))
+    y = q8.q8_scaled_mm_group128_act(dev(xg_ref), wq, dev(sx_ref), sg)
+    y_ref = oracle.scaled_mm_group128_act(xg_ref[rows], wq_ref, sx_ref[rows], sg_ref)
+    assert_ulp1(bits(host(y))[rows], y_ref, "group128 act large tiles")
+
+
 def test_group128_full_size_sampled_rows():
     wl = synth.WORKLOADS["group128"]
     say("group128 full size")

@@ -71,10 +71,20 @@ hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
     return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
 }
 
+// Group-scaled epilogues: 256 x 128 tiles of 8 waves (64 x 64 each, two
+// waves per SIMD: the per-block fold keeps a second set of fp32
+// accumulators) once there are enough of them to fill the CUs.
+template <int EPI>
+hipError_t run_gemm_grouped(const GemmArgs& p, hipStream_t s) {
+    if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
+    const int64_t tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
+    if (tiles >= 256) return launch_gemm_i8<256, 128, 4, 2, EPI, 8>(p, s);
+    return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
+}
+
 template <int EPI>  // EPI_GROUP_ACT or EPI_GROUP_ACT_F16
 hipError_t run_gemm_group_act(const GemmArgs& p, hipStream_t s) {
-    if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
-    return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
+    return run_gemm_grouped<EPI>(p, s);
 }
 
 hipError_t run_gemm_fp8_block(const GemmArgs& p, hipStream_t s) {
@@ -82,10 +92,7 @@ hipError_t run_gemm_fp8_block(const GemmArgs& p, hipStream_t s) {
     return launch_gemm_i8<128, 128, 2, 2, EPI_FP8_BLOCK, 8>(p, s);
 }
 
-hipError_t run_gemm_group(const GemmArgs& p, hipStream_t s) {
-    if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI_GROUP, 8>(p, s);
-    return launch_gemm_i8<128, 128, 2, 2, EPI_GROUP, 8>(p, s);
-}
+hipError_t run_gemm_group(const GemmArgs& p, hipStream_t s) { return run_gemm_grouped<EPI_GROUP>(p, s); }
 
 template <bool F16>
 hipError_t run_quant(const uint16_t* x, int64_t ldx, int8_t* xq, int64_t ldxq, float* s, int M,
