@@ -158,3 +158,22 @@ def test_prefill_f16_full_size_sampled_rows():
     rows = np.array([0, 1, 255, 256, 4095, 8190, 8191, 777])
     y_ref = oracle.scaled_mm_f16(xq_ref[rows], host(wq).numpy(), st_ref[rows], host(sc).numpy())
     assert_ulp1(hbits(host(y))[rows], y_ref, "prefill f16 sampled rows")
+
+
+def test_f16_empty_and_overflow_to_infinity():
+    """M = 0 is a no-op; an fp32 result beyond the fp16 range becomes
+    infinity, as in the oracle."""
+    x0 = torch.empty((0, 256), dtype=torch.float16, device=DEV)
+    xq0, st0 = q8.q8_quant_per_token_f16(x0)
+    assert xq0.shape == (0, 256) and st0.shape == (0,)
+    M, N, K = 4, 128, 256
+    a = synth.int8_uniform((M, K), seed=91, lo=100, hi=127)
+    b = synth.int8_uniform((N, K), seed=92, lo=100, hi=127)
+    s_tok = np.full((M,), 1.0, np.float32)
+    s_ch = np.full((N,), 0.005, np.float32)
+    s_ch[::3] = 1.0   # sums near 3.3e6: times 1.0 they overflow fp16, times 0.005 they stay finite
+    y_ref = oracle.scaled_mm_f16(a, b, s_tok, s_ch)
+    y = q8.q8_scaled_mm_f16(dev(a), dev(b), dev(s_tok), dev(s_ch))
+    yh = hbits(host(y))
+    assert (yh[:, ::3] == 0x7C00).all() and (y_ref[:, ::3] == 0x7C00).all()
+    assert_ulp1(yh, y_ref, "f16 overflow")

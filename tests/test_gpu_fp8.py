@@ -224,3 +224,20 @@ def test_fp8_repeat_calls_bitwise_identical():
     y1 = host(q8.q8_fp8_block_scaled_mm(xq, wq, sx, sw))
     y2 = host(q8.q8_fp8_block_scaled_mm(xq, wq, sx, sw))
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_fp8_empty_and_zero_inputs():
+    """M = 0 is a no-op; all-zero activations give zero scales, +0 codes and
+    zero outputs (no NaN from 0/0)."""
+    x0 = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    xq0, sx0 = q8.q8_quant_fp8_per_group128(x0)
+    assert xq0.shape == (0, 256) and sx0.shape == (0, 2)
+    w = synth.custom(4, 256, 128, seed=3)[1]
+    wq, sw = q8.q8_quant_weight_fp8_block128(dev(w))
+    y0 = q8.q8_fp8_block_scaled_mm(xq0, wq, sx0, sw)
+    assert y0.shape == (0, 128)
+    x = torch.zeros((5, 256), dtype=torch.bfloat16, device=DEV)
+    xq, sx = q8.q8_quant_fp8_per_group128(x)
+    assert (host(sx) == 0).all() and (u8(xq) == 0).all()
+    y = host(q8.q8_fp8_block_scaled_mm(xq, wq, sx, sw))
+    assert (y == 0).all()
