@@ -56,11 +56,11 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 # taken on: if those files change, the figure is withdrawn (null).
 GEMM_COUNTERS = {
     "sources_sha256": {
-        "gemm_i8.hpp": "7fc39c836f556d5465ed227fdcc406402c68546723fa512ae5fcc19a09687e66",
-        "q8_device.hpp": "3828c206a8ddac44b2de7061ea1095197c3eeae4e5210af3b56cec58b509b088",
+        "gemm_i8.hpp": "f72ebfe2d4046eff707048b383b25eafe898d8b301973a36fecde0c85c9bec02",
+        "q8_device.hpp": "9fff82523ff8b261ffd1d131815bc7b69b7b78349f593fab735c782757cf0653",
     },
-    "fetch_kib": 491231.2, "write_kib": 253263.7,
-    "copy_kib": 524288.0, "copy_fetch_kib": 262157.7, "copy_write_kib": 524288.0,
+    "fetch_kib": 491409.5, "write_kib": 253501.5,
+    "copy_kib": 524288.0, "copy_fetch_kib": 262156.4, "copy_write_kib": 524288.0,
 }
 
 
@@ -81,9 +81,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def events_time(fn, iters: int) -> float:
+def _events_once(fn, iters: int) -> float:
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def events_time(fn, iters: int, settle_ms: float = 60.0) -> float:
     """Average ms per call of fn() over iters calls, HIP events on the
-    current stream (the stream the library launches on)."""
+    current stream (the stream the library launches on).  fn first runs for
+    about settle_ms of GPU time, untimed, so that the clocks the board
+    settles at under this load are the ones measured."""
+    t1 = _events_once(fn, 1)
+    for _ in range(int(min(5000, max(1, settle_ms / max(t1, 1e-3))))):
+        fn()
     s = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -409,7 +426,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary",
