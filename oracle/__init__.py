@@ -56,6 +56,7 @@ def _load():
             "q8o_bf16_to_f32": ([ctypes.c_uint16], F),
             "q8o_quant_per_token": ([P, I, I, P, P], None),
             "q8o_quant_per_token_f16": ([P, I, I, P, P], None),
+            "q8o_w8a16_ref_f16": ([P, P, P, I, I, I, P, P], None),
             "q8o_f16_to_f32": ([ctypes.c_uint16], F),
             "q8o_f32_to_f16": ([F], ctypes.c_uint16),
             "q8o_scaled_mm_f16": ([P, P, P, P, I, I, I, P], ctypes.c_int),
@@ -399,3 +400,18 @@ def scaled_mm_group128_act_f16(a, b, s_x, s_w) -> np.ndarray:
     if _load().q8o_scaled_mm_group128_act_f16(_p(a), _p(b), _p(s_x), _p(s_w), M, N, K, _p(y)) != 0:
         raise ValueError("oracle: K must be a multiple of 128")
     return y
+
+
+def w8a16_ref_f16(x_f16, wq, s_ch, with_mag: bool = False):
+    """W8A16 reference with fp16 activations -> fp64 y_ref [M,N] (and fp64
+    magnitude sums)."""
+    x = _c(x_f16, np.uint16)
+    wq = _c(wq, np.int8)
+    s_ch = _c(s_ch, np.float32)
+    M, K = x.shape
+    N = wq.shape[0]
+    y = np.empty((M, N), np.float64)
+    mag = np.empty((M, N), np.float64) if with_mag else None
+    _load().q8o_w8a16_ref_f16(_p(x), _p(wq), _p(s_ch), M, N, K, _p(y),
+                              _p(mag) if with_mag else None)
+    return (y, mag) if with_mag else y

@@ -354,16 +354,16 @@ int q8o_scaled_mm_group128(const int8_t *a, const int8_t *b,
  * floating-point error bound of any summation order.
  * [P1 "Recipe": W8A16 group, INT8 per-channel weights with BF16 activations;
  *  P2 "Why W8A16 on Ampere": weights are rebuilt for a 16-bit GEMM] */
-void q8o_w8a16_ref(const uint16_t *x, const int8_t *q, const float *s_ch,
-                   int64_t M, int64_t N, int64_t K, double *y_ref,
-                   double *mag)
+static void w8a16_ref_fmt(const uint16_t *x, float (*dec)(uint16_t),
+                          const int8_t *q, const float *s_ch, int64_t M,
+                          int64_t N, int64_t K, double *y_ref, double *mag)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
             double t = 0.0, u = 0.0;
             for (int64_t k = 0; k < K; ++k) {
-                double xv = (double)bf16_bits_to_f32(x[m * K + k]);
+                double xv = (double)dec(x[m * K + k]);
                 double qv = (double)q[n * K + k];
                 t += xv * qv;
                 u += fabs(xv) * fabs(qv);
@@ -373,6 +373,22 @@ void q8o_w8a16_ref(const uint16_t *x, const int8_t *q, const float *s_ch,
                 mag[m * N + n] = (double)s_ch[n] * u;
         }
     }
+}
+
+void q8o_w8a16_ref(const uint16_t *x, const int8_t *q, const float *s_ch,
+                   int64_t M, int64_t N, int64_t K, double *y_ref,
+                   double *mag)
+{
+    w8a16_ref_fmt(x, bf16_bits_to_f32, q, s_ch, M, N, K, y_ref, mag);
+}
+
+/* The same with fp16 activations ("lued/Qwen3.8-27B-INT8-W8A16-MTP": FP16
+ * or BF16 activations). */
+void q8o_w8a16_ref_f16(const uint16_t *x, const int8_t *q, const float *s_ch,
+                       int64_t M, int64_t N, int64_t K, double *y_ref,
+                       double *mag)
+{
+    w8a16_ref_fmt(x, q8o_f16_to_f32, q, s_ch, M, N, K, y_ref, mag);
 }
 
 /* ------------------------------------------------------ smoothing fold -- */

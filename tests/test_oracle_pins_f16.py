@@ -146,3 +146,19 @@ def test_f16_and_bf16_epilogues_round_the_same_fp32_value():
     vb = (yb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     vh = yh.view(np.float16).astype(np.float64)
     assert np.all(np.abs(vb - vh) <= np.abs(vh) * (2.0 ** -8 + 2.0 ** -11) + 1e-30)
+
+
+def test_w8a16_ref_f16_matches_torch_fp64():
+    """The fp16-activation W8A16 reference against torch's fp64 matmul of
+    the decoded operands (numpy's fp16 decode), channel scale applied after."""
+    M, N, K = 5, 96, 384
+    g = np.random.default_rng(12)
+    x = (g.standard_normal((M, K)) * 3).astype(np.float16)
+    wq = synth.int8_uniform((N, K), seed=13, lo=-127)
+    s_ch = synth.uniform_f32((N,), 14, 1e-4, 1e-2)
+    y, mag = oracle.w8a16_ref_f16(x.view(np.uint16), wq, s_ch, with_mag=True)
+    xt = torch.from_numpy(x.astype(np.float64))
+    wt = torch.from_numpy(wq.astype(np.float64))
+    ref = (xt @ wt.T).numpy() * s_ch.astype(np.float64)[None, :]
+    assert np.all(np.abs(y - ref) <= 1e-12 * mag + 1e-300)
+    np.testing.assert_allclose(mag, (xt.abs() @ wt.abs().T).numpy() * s_ch.astype(np.float64)[None, :], rtol=1e-12)
