@@ -314,7 +314,8 @@ def fp8_block_tflops(dev, iters=20):
 def f16_layer(dev, iters=20):
     """The fp16 variant of the one-call layer (fp16 in, fp16 out): the
     prefill shape timed with events, and M=8 decode per call in a HIP graph
-    over weight copies (as the bf16 decode line)."""
+    over weight copies (as the bf16 decode line); then the weight-only GEMM
+    with fp16 activations at the W8A16 shape (fp16 MFMA peak = bf16's)."""
     wl = synth.WORKLOADS["prefill"]
     x = synth.activations(wl, 0).to(dev).half()
     w = synth.weights(wl, 0).to(dev)
@@ -357,6 +358,21 @@ def f16_layer(dev, iters=20):
     nbytes = dw.N * dw.K + 4 * dw.N + 2 * M * dw.K + 2 * M * dw.N + 4 * M + M * dw.K
     out["decode_M8"] = {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
                         "timing": "HIP graph of 24 calls, events"}
+    del wqs, wq, sc, x, y, xq, st
+    # the weight-only GEMM with fp16 activations at the W8A16 workload shape
+    ww = synth.WORKLOADS["w8a16"]
+    x = synth.activations(ww, 0).to(dev).half()
+    w = synth.weights(ww, 0).to(dev)
+    wq, sc = q8.q8_quant_weight(w)
+    del w
+    y = torch.empty((ww.M, ww.N), dtype=torch.float16, device=dev)
+    f = lambda: q8.w8a16_mm_f16(x, wq, sc, out=y)  # noqa: E731
+    for _ in range(5):
+        f()
+    ms = events_time(f, iters)
+    t = 2.0 * ww.M * ww.N * ww.K / (ms * 1e-3) / 1e12
+    out["w8a16_prefill"] = {"us": ms * 1e3, "TFLOPS": t, "frac_fp16_peak": t / PEAK_BF16_TFLOPS,
+                            "shape": [ww.M, ww.N, ww.K]}
     return out
 
 

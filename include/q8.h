@@ -332,6 +332,17 @@ q8_status q8_scaled_mm_group128_act_f16(const int8_t *a, int64_t lda,
                                         int64_t ldc, int64_t M, int64_t N,
                                         int64_t K, q8_stream stream);
 
+/* As w8a16_mm, with fp16 activations and fp16 outputs:
+ *   c[m,n] = fp16_rne( scale_ch[n] * sum_k x[m,k] * (fp16)w[n,k] )
+ * The int8 -> fp16 weight conversion is exact; products and sums run on
+ * fp16 matrix cores with fp32 accumulation.  fp16 keeps 3 more significand
+ * bits than bf16, so the result carries less rounding than w8a16_mm's on
+ * the same values; it overflows to infinity from 65520 up. */
+q8_status w8a16_mm_f16(const q8_f16 *x, int64_t ldx, const int8_t *w,
+                       int64_t ldw, const float *scale_ch, q8_f16 *c,
+                       int64_t ldc, int64_t M, int64_t N, int64_t K,
+                       q8_stream stream);
+
 /* ------------------------------------------------------------------------
  * FP8 block W8A8.  E4M3 is the OCP 8-bit float: sign, 4 exponent bits (bias
  * 7), 3 mantissa bits, largest finite value 448 (bytes 0x7F and 0xFF are

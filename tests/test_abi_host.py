@@ -150,6 +150,10 @@ def test_f16_entry_points_validation(lib):
     assert lib.q8_quant_scaled_mm_f16(A, 256, B, 256, S, C, 128, B + 8, S, 16, 128, 256, None) == EUNSUP
     assert lib.q8_quant_per_group128_f16(A, 256, B, 256, S, 4, 192, None) == EUNSUP
     assert lib.q8_scaled_mm_group128_act_f16(A, 256, B, 256, S, None, C, 128, 16, 128, 256, None) == EINVAL
+    assert lib.w8a16_mm_f16(A, 256, B, 256, S, C, 128, 0, 128, 256, None) == OK
+    assert lib.w8a16_mm_f16(A, 260, B, 256, S, C, 128, 16, 128, 256, None) == EUNSUP
+    assert lib.w8a16_mm_f16(A, 256, B, 256, None, C, 128, 16, 128, 256, None) == EINVAL
+    assert lib.w8a16_mm_f16(A, 256, B, 256, S, C, 100, 16, 128, 256, None) == EINVAL
 
 
 def test_binding_rejects_cpu_tensors():

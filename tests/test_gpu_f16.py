@@ -1,7 +1,9 @@
 """GPU parity of the fp16 variant (fp16 activations in, fp16 outputs)
 against the CPU oracle: codes and scales bit-exact, fp16 outputs within 1
 fp16 ulp (ordered-integer distance, +0 == -0) -- the same bar as bf16,
-since the same fp32 value is rounded once to the output format."""
+since the same fp32 value is rounded once to the output format.  The
+weight-only GEMM (fp16 products summed on the matrix cores) is held to an
+error bound derived from its arithmetic instead."""
 from __future__ import annotations
 
 import sys
@@ -177,3 +179,86 @@ def test_f16_empty_and_overflow_to_infinity():
     yh = hbits(host(y))
     assert (yh[:, ::3] == 0x7C00).all() and (y_ref[:, ::3] == 0x7C00).all()
     assert_ulp1(yh, y_ref, "f16 overflow")
+
+
+# ------------------------------------------- weight-only INT8, fp16 x ----
+
+def _check_w8a16_f16(y_bits, x_bits, wq, s_ch, what):
+    """|y - y_ref| <= 2^-11 |y_ref| (1 + 2^-10) + 2^-25 + K 2^-22 mag: the
+    fp16 output rounding (half an ulp, relative; half the subnormal quantum
+    near 0) and fp32 accumulation of the exact int8 x fp16 products (at most
+    one rounding of the running sum, |sum| <= mag, per product, with 4x
+    slack).  mag = s_ch[n] sum_k |x[m,k] w[n,k]|."""
+    K = x_bits.shape[1]
+    y_ref, mag = oracle.w8a16_ref_f16(x_bits, wq, s_ch, with_mag=True)
+    assert np.all(np.abs(y_ref) < 60000.0), "test data must stay in the fp16 range"
+    y = y_bits.view(np.float16).astype(np.float64)
+    err = np.abs(y - y_ref)
+    bound = 2.0 ** -11 * np.abs(y_ref) * (1 + 2.0 ** -10) + 2.0 ** -25 + K * 2.0 ** -22 * mag
+    ratio = err / bound
+    say(f"{what}: max err/bound {ratio.max() if ratio.size else 0:.3f}")
+    assert np.all(np.isfinite(y)), what
+    assert np.all(err <= bound), what
+
+
+def _w8a16_inputs(M, N, K, seed, pad=0):
+    wl = synth.WORKLOADS["w8a16"]
+    xf = synth.activations(wl, seed, M=M, K=K + pad).float()
+    xf[0] = xf[0] * 50  # a position-outlier row, as in the W8A16 workload
+    xf = xf.half()
+    w = synth.weights(wl, seed, N=N, K=K)
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    return xf, wq_ref, sc_ref
+
+
+@pytest.mark.parametrize("M,N,K,pad", [
+    (16, 128, 256, 0), (33, 144, 384, 8),          # few tokens, K not a multiple of 1024
+    (1, 16, 1024, 0), (5, 4112, 2048, 16), (16, 5120, 5120, 0), (33, 1040, 4096, 0),
+    (64, 2048, 3072, 0),                            # few tokens: weight streaming
+    (65, 272, 1152, 0), (130, 256, 1024, 8), (300, 128, 13824, 0)])  # tiled
+def test_w8a16_f16_shapes(M, N, K, pad):
+    """Each route of the weight-only GEMM with fp16 activations (small-M
+    tiles, the weight-streaming ring, the tiled kernel), strided x and y."""
+    say("w8a16 f16", M, N, K, pad)
+    xf, wq_ref, sc_ref = _w8a16_inputs(M, N, K, seed=M + N, pad=pad)
+    x = xf[:, :K].contiguous()
+    yfull = torch.full((M, N + pad), -1, dtype=torch.int16, device=DEV).view(torch.float16)
+    y = q8.w8a16_mm_f16(dev(xf)[:, :K], dev(wq_ref), dev(sc_ref), out=yfull[:, :N])
+    _check_w8a16_f16(hbits(host(y)), hbits(x), wq_ref, sc_ref, f"w8a16 f16 {M}x{N}x{K}")
+    if pad:
+        assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
+
+
+def test_w8a16_f16_full_size_sampled_rows():
+    """The W8A16 workload's full shape in one launch (the 256 x 128 tiles),
+    outputs checked on sampled rows."""
+    wl = synth.WORKLOADS["w8a16"]
+    say("w8a16 f16 full size")
+    x = synth.activations(wl, 0).float().half()
+    w = synth.weights(wl, 0)
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    wq, sc = q8.q8_quant_weight(dev(w))
+    y = q8.w8a16_mm_f16(dev(x), wq, sc)
+    rows = np.array([0, 1, 40, 81, 82, 83, 127, 128, 4096, 8190, 8191])
+    _check_w8a16_f16(hbits(host(y))[rows], np.ascontiguousarray(hbits(x)[rows]), wq_ref, sc_ref,
+                     "w8a16 f16 sampled rows")
+
+
+@pytest.mark.parametrize("M", [0, 4, 100])
+def test_w8a16_f16_empty_and_overflow_to_infinity(M):
+    """M = 0 is a no-op; sums beyond the fp16 range become infinity (small
+    M: the streaming ring; M = 100: the tiled kernel)."""
+    N, K = 128, 1024
+    x = torch.full((M, K), 1024.0, dtype=torch.float16)
+    wq = np.full((N, K), 127, np.int8)
+    s_ch = np.full((N,), 2.0 ** -12, np.float32)
+    s_ch[::3] = 1.0  # 1024 * 127 * 1024 = 127 * 2^20: times 1 it overflows, times 2^-12 it is 32512
+    y = q8.w8a16_mm_f16(dev(x), dev(wq), dev(s_ch))
+    assert y.shape == (M, N)
+    if M == 0:
+        return
+    yh = hbits(host(y))
+    assert (yh[:, ::3] == 0x7C00).all()
+    finite = np.ones(N, bool)
+    finite[::3] = False
+    assert (yh[:, finite].view(np.float16).astype(np.float64) == 32512.0).all()

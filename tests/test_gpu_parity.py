@@ -527,13 +527,22 @@ def test_group128_full_size_sampled_rows():
 # --------------------------------------------------------------- W8A16 --
 
 def _check_w8a16(y_bits, x_bits, wq, s_ch, what):
+    """Each row within 2e-2 relative (2-norm), and elementwise
+    |y - y_ref| <= 2^-8 |y_ref| (1 + 2^-7) + 2^-134 + K 2^-22 mag: the bf16
+    output rounding (half an ulp is at most 2^-8 of the value; half the
+    subnormal quantum near 0) and fp32 accumulation of the exact int8 x bf16
+    products (at most one rounding of the running sum, |sum| <= mag, per
+    product, with 4x slack).  mag = s_ch[n] sum_k |x[m,k] w[n,k]|.  The
+    elementwise bound is below 2e-2 |y_ref| + K 2^-22 mag, so it is the
+    stricter of the two readings of "2e-2 relative"."""
     K = x_bits.shape[1]
     y_ref, mag = oracle.w8a16_ref(x_bits, wq, s_ch, with_mag=True)
     y = (y_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     err = np.abs(y - y_ref)
-    bound = 2e-2 * np.abs(y_ref) + K * 2.0 ** -22 * mag + 2.0 ** -8 * np.abs(y_ref)
+    bound = 2.0 ** -8 * np.abs(y_ref) * (1 + 2.0 ** -7) + 2.0 ** -134 + K * 2.0 ** -22 * mag
     rel = np.linalg.norm(y - y_ref, axis=1) / np.maximum(np.linalg.norm(y_ref, axis=1), 1e-30)
-    say(f"{what}: max row rel {rel.max():.2e}, max err/bound {(err / np.maximum(bound, 1e-300)).max():.3f}")
+    say(f"{what}: max row rel {rel.max():.2e}, max err/bound {(err / bound).max():.3f}")
+    assert np.all(np.isfinite(y)), what
     assert rel.max() <= 2e-2, what
     assert np.all(err <= bound), what
 

@@ -22,7 +22,7 @@ Functions mirror the C entry points:
   q8_quant_weight_fp8_block128(w) -> (wq float8_e4m3fn, scale_blk)
   q8_fp8_block_scaled_mm(xq, wq, scale_x, scale_w) -> y
   ..._f16 variants of the per-token and per-group quantizers, q8_scaled_mm,
-  q8_quant_scaled_mm and q8_scaled_mm_group128_act (fp16 in / out)
+  q8_quant_scaled_mm, q8_scaled_mm_group128_act and w8a16_mm (fp16 in / out)
 Each also accepts preallocated outputs (``out=`` ...) so callers control
 allocation; the library itself never allocates.
 """
@@ -40,7 +40,7 @@ __all__ = [
     "q8_scaled_mm_group128_act", "q8_quant_fp8_per_group128", "q8_quant_weight_fp8_block128",
     "q8_fp8_block_scaled_mm", "q8_quant_per_token_f16", "q8_scaled_mm_f16",
     "q8_quant_scaled_mm_f16", "q8_quant_per_group128_f16", "q8_scaled_mm_group128_act_f16",
-    "EXPORTS", "MAX_K",
+    "w8a16_mm_f16", "EXPORTS", "MAX_K",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,6 +52,7 @@ EXPORTS = (
     "q8_scaled_mm_group128_act", "q8_quant_fp8_per_group128", "q8_quant_weight_fp8_block128",
     "q8_fp8_block_scaled_mm", "q8_quant_per_token_f16", "q8_scaled_mm_f16",
     "q8_quant_scaled_mm_f16", "q8_quant_per_group128_f16", "q8_scaled_mm_group128_act_f16",
+    "w8a16_mm_f16",
 )
 _STATUS = {0: "Q8_OK", 1: "Q8_EINVAL", 2: "Q8_EUNSUPPORTED", 3: "Q8_EHIP"}
 
@@ -103,6 +104,7 @@ def load():
         "q8_quant_scaled_mm_f16": ([P, I, P, I, P, P, I, P, P, I, I, I, P], S),
         "q8_quant_per_group128_f16": ([P, I, P, I, P, I, I, P], S),
         "q8_scaled_mm_group128_act_f16": ([P, I, P, I, P, P, P, I, I, I, I, P], S),
+        "w8a16_mm_f16": ([P, I, P, I, P, P, I, I, I, I, P], S),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -221,17 +223,26 @@ def q8_scaled_mm_group128(a, b, scale_tok, scale_grp, out=None):
     return c
 
 
-def w8a16_mm(x, w, scale_ch, out=None):
-    """bf16 [M,N] = scale_ch[n] * (x @ bf16(w)^T), fp32 accumulation."""
-    M, N, K = _mk(x, w, torch.bfloat16)
+def _w8a16_mm(name, dtype, x, w, scale_ch, out):
+    M, N, K = _mk(x, w, dtype)
     _dev(scale_ch, torch.float32, "scale_ch", 1)
     if scale_ch.numel() != N:
         raise ValueError("scale_ch size does not match N")
-    c = _gemm_out(M, N, x.device, out)
-    _check("w8a16_mm", load().w8a16_mm(
+    c = _gemm_out(M, N, x.device, out, dtype)
+    _check(name, getattr(load(), name)(
         _ptr(x), _ld(x), _ptr(w), _ld(w), _ptr(scale_ch), _ptr(c), _ld(c),
         M, N, K, _stream(x.device)))
     return c
+
+
+def w8a16_mm(x, w, scale_ch, out=None):
+    """bf16 [M,N] = scale_ch[n] * (x @ bf16(w)^T), fp32 accumulation."""
+    return _w8a16_mm("w8a16_mm", torch.bfloat16, x, w, scale_ch, out)
+
+
+def w8a16_mm_f16(x, w, scale_ch, out=None):
+    """fp16 [M,N] = scale_ch[n] * (x @ fp16(w)^T), fp16 x, fp32 accumulation."""
+    return _w8a16_mm("w8a16_mm_f16", torch.float16, x, w, scale_ch, out)
 
 
 def q8_quant_scaled_mm(x, b, scale_ch, out=None, xq_out=None, scale_tok_out=None):

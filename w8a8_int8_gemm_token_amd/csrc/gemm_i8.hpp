@@ -16,6 +16,8 @@
 //                f) in ascending g; y = bf16_rne(f)
 //   EPI_CHANNEL_F16, EPI_GROUP_ACT_F16: as EPI_CHANNEL and EPI_GROUP_ACT
 //                with fp16 (RNE) outputs
+//   EPI_W8A16_F16: EPI_W8A16 with fp16 activations (v_mfma_f32_32x32x16_f16)
+//                and fp16 outputs
 //   EPI_W8A16:   bf16 activations (x, ldx in bytes) times int8 weights on
 //                v_mfma_f32_32x32x16_bf16: y = bf16_rne(s_ch[n] * acc), acc
 //                the fp32 MFMA sum of x[m,k] * bf16(w[n,k])
@@ -70,11 +72,14 @@
 namespace q8 {
 
 enum { EPI_I32 = 0, EPI_CHANNEL = 1, EPI_GROUP = 2, EPI_GROUP_ACT = 3, EPI_FP8_BLOCK = 4,
-       EPI_CHANNEL_F16 = 5, EPI_GROUP_ACT_F16 = 6, EPI_W8A16 = 7 };
+       EPI_CHANNEL_F16 = 5, EPI_GROUP_ACT_F16 = 6, EPI_W8A16 = 7, EPI_W8A16_F16 = 8 };
 
-// The _F16 epilogues are EPI_CHANNEL and EPI_GROUP_ACT with fp16 outputs.
+// The _F16 epilogues are EPI_CHANNEL, EPI_GROUP_ACT and EPI_W8A16 with fp16
+// outputs (EPI_W8A16_F16: fp16 activations as well).
 constexpr int epi_base(int e) {
-    return e == EPI_CHANNEL_F16 ? EPI_CHANNEL : e == EPI_GROUP_ACT_F16 ? EPI_GROUP_ACT : e;
+    return e == EPI_CHANNEL_F16 ? EPI_CHANNEL
+           : e == EPI_GROUP_ACT_F16 ? EPI_GROUP_ACT
+           : e == EPI_W8A16_F16 ? EPI_W8A16 : e;
 }
 
 struct GemmArgs {
@@ -256,8 +261,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < WLC; ++i) {
                 const int c = (int)threadIdx.x + i * NW * 64, r = c >> 2, q = c & 3;
-                const v2u a0 = i8x4_to_bf16x4((u32)wreg[i][0]), a1 = i8x4_to_bf16x4((u32)wreg[i][1]);
-                const v2u a2 = i8x4_to_bf16x4((u32)wreg[i][2]), a3 = i8x4_to_bf16x4((u32)wreg[i][3]);
+                const v2u a0 = i8x4_to_h16x4<OUT_F16>((u32)wreg[i][0]);
+                const v2u a1 = i8x4_to_h16x4<OUT_F16>((u32)wreg[i][1]);
+                const v2u a2 = i8x4_to_h16x4<OUT_F16>((u32)wreg[i][2]);
+                const v2u a3 = i8x4_to_h16x4<OUT_F16>((u32)wreg[i][3]);
                 const int f = lds_swizzle(r);
                 *reinterpret_cast<v4u*>(bw + r * BK + (((2 * q) ^ f) << 4)) = v4u{a0[0], a0[1], a1[0], a1[1]};
                 *reinterpret_cast<v4u*>(bw + r * BK + (((2 * q + 1) ^ f) << 4)) = v4u{a2[0], a2[1], a3[0], a3[1]};
@@ -327,6 +334,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
             if constexpr (F8)  // A and B in E4M3 (format 0), no block exponents
                 acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     fw[set][b], fx[set][a], fresh ? AccT{} : acc[a][b], 0, 0, 0, 0, 0, 0);
+            else if constexpr (W16 && OUT_F16)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fw[set][b]),
+                                                                   __builtin_bit_cast(v8h, fx[set][a]),
+                                                                   acc[a][b], 0, 0, 0);
             else if constexpr (W16)
                 acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fw[set][b]),
                                                                     __builtin_bit_cast(v8bf, fx[set][a]),

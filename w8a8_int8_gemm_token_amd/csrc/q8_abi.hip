@@ -245,27 +245,47 @@ q8_status q8_mm_i32(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb, 
     return hip_status(run_gemm_i8<EPI_I32>(p, st(stream)));
 }
 
-q8_status w8a16_mm(const q8_bf16* x, int64_t ldx, const int8_t* w, int64_t ldw,
-                   const float* scale_ch, q8_bf16* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                   q8_stream stream) {
+}  // extern "C"
+
+namespace {
+// Weight-only INT8 GEMM: bf16 or (F16) fp16 activations and outputs.
+template <bool F16>
+q8_status w8a16_impl(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ldw, const float* scale_ch,
+                     uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, q8_stream stream) {
     q8_status r = check_gemm(x, ldx, 8, w, ldw, c, ldc, 8, M, N, K);
     if (r == Q8_OK && M > 0) r = check_scale(scale_ch);
     if (r != Q8_OK || M == 0) return r;
     if (sg_fits((int)M, (int)N, (int)K, ldw, SG_MAX_M)) {  // few tokens: stream the weights once
-        const StreamArgs q{x, ldx, w, ldw, nullptr, scale_ch, c, ldc, (int)M, (int)N, (int)K, 0, 0};
-        return hip_status(launch_stream<false>(q, st(stream)));
+        const StreamArgs q{x, ldx, w, ldw, nullptr, scale_ch, c, ldc, (int)M, (int)N, (int)K, 0, 0, 0};
+        return hip_status(launch_stream<false, F16>(q, st(stream)));
     }
     if (M <= 64) {
         W8A16Args p{x, ldx, w, ldw, scale_ch, c, ldc, (int)M, (int)N, (int)K};
-        return hip_status(launch_w8a16<32, 128, 64, 1, 4, 8>(p, st(stream)));
+        return hip_status(launch_w8a16<32, 128, 64, 1, 4, 8, F16>(p, st(stream)));
     }
-    // the tiled kernel's bf16 mode: activations addressed in bytes
+    // the tiled kernel's 16-bit mode: activations addressed in bytes
+    constexpr int E = F16 ? EPI_W8A16_F16 : EPI_W8A16;
     GemmArgs p{reinterpret_cast<const int8_t*>(x), 2 * ldx, w, ldw, nullptr, scale_ch, c, ldc,
                (int)M, (int)N, (int)K};
     if (!gemm_offsets_fit(p)) return Q8_EUNSUPPORTED;
     const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
-    if (tiles >= 256) return hip_status(launch_gemm_i8<256, 128, 4, 2, EPI_W8A16, 8>(p, st(stream)));
-    return hip_status(launch_gemm_i8<128, 128, 2, 2, EPI_W8A16, 8>(p, st(stream)));
+    if (tiles >= 256) return hip_status(launch_gemm_i8<256, 128, 4, 2, E, 8>(p, st(stream)));
+    return hip_status(launch_gemm_i8<128, 128, 2, 2, E, 8>(p, st(stream)));
+}
+}  // namespace
+
+extern "C" {
+
+q8_status w8a16_mm(const q8_bf16* x, int64_t ldx, const int8_t* w, int64_t ldw,
+                   const float* scale_ch, q8_bf16* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                   q8_stream stream) {
+    return w8a16_impl<false>(x, ldx, w, ldw, scale_ch, c, ldc, M, N, K, stream);
+}
+
+q8_status w8a16_mm_f16(const q8_f16* x, int64_t ldx, const int8_t* w, int64_t ldw,
+                       const float* scale_ch, q8_f16* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                       q8_stream stream) {
+    return w8a16_impl<true>(x, ldx, w, ldw, scale_ch, c, ldc, M, N, K, stream);
 }
 
 q8_status q8_quant_scaled_mm(const q8_bf16* x, int64_t ldx, const int8_t* b, int64_t ldb,

@@ -79,6 +79,19 @@ __device__ __forceinline__ v2u i8x4_to_bf16x4(u32 d) {
                (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u)};
 }
 
+// 4 int8 codes (one dword) -> 4 exact fp16 values (two dwords): |q| <= 128
+// fits the 11-bit fp16 significand.
+__device__ __forceinline__ v2u i8x4_to_f16x4(u32 d) {
+    return v2u{pack_f16x2((float)(int8_t)(d & 0xFF), (float)(int8_t)((d >> 8) & 0xFF)),
+               pack_f16x2((float)(int8_t)((d >> 16) & 0xFF), (float)(int8_t)(d >> 24))};
+}
+template <bool F16>
+__device__ __forceinline__ v2u i8x4_to_h16x4(u32 d) {
+    if constexpr (F16) return i8x4_to_f16x4(d); else return i8x4_to_bf16x4(d);
+}
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
 // Wave-wide (64 lanes) maximum of a non-negative float.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

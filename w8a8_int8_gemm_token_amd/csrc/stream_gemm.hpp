@@ -52,7 +52,7 @@ constexpr int SG_NBUF = 3;
 typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 
 struct StreamArgs {
-    const void* x;  // [M, ldx]: int8 codes (I8) or bf16
+    const void* x;  // [M, ldx]: int8 codes (I8), bf16, or fp16 (W8A16 with out_f16)
     int64_t ldx;
     const int8_t* w;  // [N, ldw] int8
     int64_t ldw;
@@ -63,7 +63,7 @@ struct StreamArgs {
     int M, N, K;
     int rows;  // channels per workgroup (multiple of 4, <= 32)
     int nbuf;  // segment slots in the ring
-    int out_f16;  // I8 only: fp16 outputs (RNE) instead of bf16
+    int out_f16;  // fp16 outputs (RNE) instead of bf16 (and, W8A16, fp16 activations)
 };
 
 // Three slots: a deeper ring issues most of a short K at once, and the
@@ -116,12 +116,17 @@ __device__ __forceinline__ void sg_wait_vm(int n) {
     }
 }
 
+__device__ __forceinline__ v8h i8x8_to_f16x8(v2u raw) {
+    const v2u lo = i8x4_to_f16x4(raw[0]), hi = i8x4_to_f16x4(raw[1]);
+    return __builtin_bit_cast(v8h, v4u{lo[0], lo[1], hi[0], hi[1]});
+}
 __device__ __forceinline__ v8bf16 i8x8_to_bf16x8(v2u raw) {
     const v2u lo = i8x4_to_bf16x4(raw[0]), hi = i8x4_to_bf16x4(raw[1]);
     return __builtin_bit_cast(v8bf16, v4u{lo[0], lo[1], hi[0], hi[1]});
 }
 
-template <bool I8, int MG>
+// F16 (W8A16 only): fp16 activations, v_mfma_f32_16x16x32_f16.
+template <bool I8, int MG, bool F16 = false>
 __global__ __launch_bounds__(1024) void stream_gemm_kernel(StreamArgs p) {
     // K blocks per MFMA: 64 (int8) or 32 (bf16); per segment and wave
     constexpr int KB = I8 ? 64 : 32;
@@ -206,6 +211,18 @@ __global__ __launch_bounds__(1024) void stream_gemm_kernel(StreamArgs p) {
                         const v4i bg = __builtin_bit_cast(v4i, b[j][g]);
                         acc[0][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bg, acc[0][g], 0, 0, 0);
                         acc[1][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bg, acc[1][g], 0, 0, 0);
+                    }
+                } else if constexpr (F16) {
+                    const int h = (o >> 3) & 1;
+                    const v8h a0 = i8x8_to_f16x8(
+                        *reinterpret_cast<const v2u*>(slot + r0 * SG_SEG + ((u ^ (r0 & 15)) << 4) + (h << 3)));
+                    const v8h a1 = i8x8_to_f16x8(
+                        *reinterpret_cast<const v2u*>(slot + r1 * SG_SEG + ((u ^ (r1 & 15)) << 4) + (h << 3)));
+#pragma unroll
+                    for (int g = 0; g < MG; ++g) {
+                        const v8h bg = __builtin_bit_cast(v8h, b[j][g]);
+                        acc[0][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bg, acc[0][g], 0, 0, 0);
+                        acc[1][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bg, acc[1][g], 0, 0, 0);
                     }
                 } else {
                     const int h = (o >> 3) & 1;
@@ -310,26 +327,29 @@ inline bool sg_fits(int M, int N, int K, int64_t ldw, int max_m) {
     return (int64_t)sg_rows(N) * ldw < ((int64_t)1 << 31);
 }
 
-template <bool I8, int MG>
+template <bool I8, int MG, bool F16>
 inline hipError_t launch_stream_t(const StreamArgs& p, hipStream_t stream) {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&stream_gemm_kernel<I8, MG>),
+        reinterpret_cast<const void*>(&stream_gemm_kernel<I8, MG, F16>),
         hipFuncAttributeMaxDynamicSharedMemorySize, SG_RING_BYTES);
     if (attr != hipSuccess) return attr;
     const int grid = (p.N + p.rows - 1) / p.rows;
-    hipLaunchKernelGGL((stream_gemm_kernel<I8, MG>), dim3(grid), dim3(1024),
+    hipLaunchKernelGGL((stream_gemm_kernel<I8, MG, F16>), dim3(grid), dim3(1024),
                        sg_lds_bytes(p.rows, p.nbuf, MG), stream, p);
     return hipGetLastError();
 }
 
-// Fills rows and nbuf from N, then launches for the token count.
-template <bool I8>
+// Fills rows and nbuf from N, then launches for the token count.  F16 (W8A16
+// only): fp16 activations and outputs.
+template <bool I8, bool F16 = false>
 inline hipError_t launch_stream(StreamArgs p, hipStream_t stream) {
+    static_assert(!(I8 && F16), "fp16 activations are a W8A16 mode");
     p.rows = sg_rows(p.N);
     p.nbuf = sg_nbuf(p.rows);
-    if (p.M <= 16) return launch_stream_t<I8, 1>(p, stream);
-    if (p.M <= 32) return launch_stream_t<I8, 2>(p, stream);
-    return launch_stream_t<I8, 4>(p, stream);
+    if (F16) p.out_f16 = 1;
+    if (p.M <= 16) return launch_stream_t<I8, 1, F16>(p, stream);
+    if (p.M <= 32) return launch_stream_t<I8, 2, F16>(p, stream);
+    return launch_stream_t<I8, 4, F16>(p, stream);
 }
 
 }  // namespace q8

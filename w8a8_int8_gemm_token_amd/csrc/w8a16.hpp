@@ -8,6 +8,8 @@
 //
 // This kernel serves M <= 64 when the weight-streaming kernel does not apply;
 // larger M runs the tiled INT8 GEMM's bf16 mode (EPI_W8A16 in gemm_i8.hpp).
+// F16: fp16 activations and outputs instead (v_mfma_f32_32x32x16_f16; the
+// int8 weights are exact in fp16 as well).
 //
 // Design: same tile/wave structure as the INT8 GEMM.  The int8 weight tile
 // is read from HBM as int8 (half the bytes of bf16) and converted exactly to
@@ -22,17 +24,17 @@
 namespace q8 {
 
 struct W8A16Args {
-    const uint16_t* x;  // [M, ldx] bf16
+    const uint16_t* x;  // [M, ldx] bf16 (fp16 when F16)
     int64_t ldx;
     const int8_t* w;  // [N, ldw] int8
     int64_t ldw;
     const float* s_ch;  // [N]
-    uint16_t* c;        // [M, ldc] bf16
+    uint16_t* c;        // [M, ldc] bf16 (fp16 when F16)
     int64_t ldc;
     int M, N, K;
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int GM>
+template <int BM, int BN, int BK, int WM, int WN, int GM, bool F16>
 __global__ __launch_bounds__(WM* WN * 64) void w8a16_kernel(W8A16Args p) {
     constexpr int NT = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -97,8 +99,8 @@ __global__ __launch_bounds__(WM* WN * 64) void w8a16_kernel(W8A16Args p) {
         for (int i = 0; i < XCH; ++i) *reinterpret_cast<v4i*>(&lx[buf][xo[i]]) = rx[i];
 #pragma unroll
         for (int i = 0; i < WCH; ++i) {
-            const v2u a = i8x4_to_bf16x4(rw[i][0]), b = i8x4_to_bf16x4(rw[i][1]);
-            const v2u c = i8x4_to_bf16x4(rw[i][2]), d = i8x4_to_bf16x4(rw[i][3]);
+            const v2u a = i8x4_to_h16x4<F16>(rw[i][0]), b = i8x4_to_h16x4<F16>(rw[i][1]);
+            const v2u c = i8x4_to_h16x4<F16>(rw[i][2]), d = i8x4_to_h16x4<F16>(rw[i][3]);
             *reinterpret_cast<v4u*>(&lw[buf][wo[i]]) = v4u{a[0], a[1], b[0], b[1]};
             *reinterpret_cast<v4u*>(&lw[buf][wo[i] + 16]) = v4u{c[0], c[1], d[0], d[1]};
         }
@@ -120,8 +122,14 @@ __global__ __launch_bounds__(WM* WN * 64) void w8a16_kernel(W8A16Args p) {
 #pragma unroll
             for (int a = 0; a < TM; ++a)
 #pragma unroll
-                for (int b = 0; b < TN; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[b], fx[a], acc[a][b], 0, 0, 0);
+                for (int b = 0; b < TN; ++b) {
+                    if constexpr (F16)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fw[b]),
+                                                                           __builtin_bit_cast(v8h, fx[a]),
+                                                                           acc[a][b], 0, 0, 0);
+                    else
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[b], fx[a], acc[a][b], 0, 0, 0);
+                }
         }
     };
 
@@ -151,16 +159,16 @@ __global__ __launch_bounds__(WM* WN * 64) void w8a16_kernel(W8A16Args p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = p.s_ch[ch + e] * acc[a][b][g * 4 + e];
                 *reinterpret_cast<v2u*>(p.c + (int64_t)j * p.ldc + ch) =
-                    v2u{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    v2u{pack16x2<F16>(v[0], v[1]), pack16x2<F16>(v[2], v[3])};
             }
         }
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int GM>
+template <int BM, int BN, int BK, int WM, int WN, int GM, bool F16>
 inline hipError_t launch_w8a16(const W8A16Args& p, hipStream_t stream) {
     const int nbm = (p.M + BM - 1) / BM, nbn = (p.N + BN - 1) / BN;
-    hipLaunchKernelGGL((w8a16_kernel<BM, BN, BK, WM, WN, GM>), dim3(nbm * nbn), dim3(WM * WN * 64),
+    hipLaunchKernelGGL((w8a16_kernel<BM, BN, BK, WM, WN, GM, F16>), dim3(nbm * nbn), dim3(WM * WN * 64),
                        0, stream, p);
     return hipGetLastError();
 }
