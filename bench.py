@@ -495,7 +495,7 @@ def main():
                 "unit": "TFLOP/s", "frac": achieved / PEAK_INT8_TOPS,
                 "traffic": None if traffic is None else sum(traffic),
                 "traffic_read_write": traffic, "algorithmic_bytes": algo_bytes,
-                "kernel": "gemm_i8_kernel (per-channel epilogue)",
+                "kernel": "gemm_big_kernel (per-channel epilogue, 256 x 384 tiles)",
                 "kernel_us": gemm_ms * 1e3}
     secondary = {"quant_kernel": {"us": quant_ms * 1e3,
                                   "GB/s": quant_bytes / (quant_ms * 1e-3) / 1e9}}

@@ -289,6 +289,46 @@ def test_mm_i32_strided_operands():
     assert not got[:, N:].any(), "wrote outside the output view"
 
 
+# Large problems run the per-channel and int32 GEMMs on 256 x 384 tiles when
+# that needs fewer whole waves of tiles (4100 x 4000: 272 tiles of 256 x 256
+# against 187 of 256 x 384; 8192 x 5120: 640 against 448), with ragged tiles
+# on both edges here.  The sampled rows sit on each side of tile boundaries
+# and in the partial last row of tiles; every column is checked.
+BIG_ROWS = np.array([0, 1, 31, 32, 127, 128, 255, 256, 2047, 2048, 4095, 4096, 4097, 4099, 8191])
+
+
+@pytest.mark.parametrize("M,N,K,pad", [(4100, 4000, 256, 0), (4100, 4000, 384, 48), (8192, 5120, 1024, 0)])
+def test_big_tiles_mm_i32_sampled_rows(M, N, K, pad):
+    say("big tiles mm_i32", M, N, K, pad)
+    a = synth.int8_uniform((M, K + pad), seed=M + K)
+    b = synth.int8_uniform((N, K + pad), seed=N + 3 * K)
+    rows = BIG_ROWS[BIG_ROWS < M]
+    outbuf = torch.full((M, N + pad), -7, dtype=torch.int32, device=DEV)
+    q8.q8_mm_i32(dev(a)[:, :K], dev(b)[:, :K], out=outbuf[:, :N])
+    got = host(outbuf).numpy()
+    ref = oracle.mm_i32(np.ascontiguousarray(a[rows, :K]), np.ascontiguousarray(b[:, :K]))
+    np.testing.assert_array_equal(got[rows, :N], ref)
+    if pad:
+        assert (got[:, N:] == -7).all(), "wrote outside the output view"
+
+
+@pytest.mark.parametrize("M,N,K", [(4100, 4000, 256), (8192, 5120, 1024)])
+def test_big_tiles_scaled_mm_sampled_rows(M, N, K):
+    say("big tiles scaled_mm", M, N, K)
+    a = synth.int8_uniform((M, K), seed=M + 5 * K, lo=-127)
+    b = synth.int8_uniform((N, K), seed=N + 7 * K, lo=-127)
+    st = synth.uniform_f32((M,), seed=M, lo=1e-4, hi=2e-2)
+    sc = synth.uniform_f32((N,), seed=N, lo=1e-4, hi=2e-2)
+    rows = BIG_ROWS[BIG_ROWS < M]
+    y = q8.q8_scaled_mm(dev(a), dev(b), dev(st), dev(sc))
+    ref = oracle.scaled_mm(np.ascontiguousarray(a[rows]), b, st[rows], sc)
+    assert_ulp1(bits(host(y))[rows], ref, f"big tiles scaled_mm {M}x{N}x{K}")
+    yh = q8.q8_scaled_mm_f16(dev(a), dev(b), dev(st), dev(sc))
+    ref_h = oracle.scaled_mm_f16(np.ascontiguousarray(a[rows]), b, st[rows], sc)
+    got_h = host(yh).contiguous().view(torch.int16).numpy().view(np.uint16)[rows]
+    assert_ulp1(got_h, ref_h, f"big tiles scaled_mm_f16 {M}x{N}x{K}")
+
+
 # ------------------------------------------------------------ W8A8 layer -
 
 def _layer_inputs(name, seed, M=None):

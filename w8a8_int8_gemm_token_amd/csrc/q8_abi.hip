@@ -11,6 +11,7 @@
 #include "decode_fused.hpp"
 #include "norm_quant.hpp"
 #include "w8a16.hpp"
+#include "gemm_big.hpp"
 #include "stream_gemm.hpp"
 #include "fp8.hpp"
 
@@ -66,9 +67,15 @@ hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
         }
     }
     if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
-    const int64_t big_tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
-    if (big_tiles >= 256) return launch_gemm_i8<256, 256, 2, 4, EPI, 8>(p, s);
-    return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
+    const int64_t nbm = (p.M + 255) / 256;
+    const int64_t t256 = nbm * ((p.N + 255) / 256), t384 = nbm * ((p.N + 383) / 384);
+    if (t256 < 256) return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
+    // Whole waves of 256 tiles (a partly filled last wave costs a whole
+    // one); a wave of 256 x 384 tiles takes about 1.4 times as long as one
+    // of 256 x 256 (measured at the prefill shape: 111.5 us against 78-83).
+    const int64_t w256 = (t256 + 255) / 256, w384 = (t384 + 255) / 256;
+    if (140 * w384 < 100 * w256 && gemm_big_offsets_fit(p)) return launch_gemm_big<EPI>(p, s);
+    return launch_gemm_i8<256, 256, 2, 4, EPI, 8>(p, s);
 }
 
 // Group-scaled epilogues: 256 x 128 tiles of 8 waves (64 x 64 each, two
