@@ -50,17 +50,19 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 
 
 # HBM bytes of the prefill GEMM from hardware counters (rocprofv3 --pmc
-# FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, mean of 7 dispatches of
-# gemm_i8_kernel<256,256,2,4,1,8>), scaled by what the same counters read for
-# a plain 512 MiB device copy.  Valid only for the kernel sources they were
-# taken on: if those files change, the figure is withdrawn (null).
+# FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, mean over the dispatches of
+# gemm_big_kernel<EPI_CHANNEL> in a short bench run), scaled by what the same
+# counters read for a plain 512 MiB device copy.  Valid only for the kernel
+# sources they were taken on: if those files change, the figure is withdrawn
+# (null).
 GEMM_COUNTERS = {
     "sources_sha256": {
-        "gemm_i8.hpp": "f72ebfe2d4046eff707048b383b25eafe898d8b301973a36fecde0c85c9bec02",
-        "q8_device.hpp": "9fff82523ff8b261ffd1d131815bc7b69b7b78349f593fab735c782757cf0653",
+        "gemm_big.hpp": "86785bac67fcdcaaf077878f83390f6fc1805d1d3c6b704b21311aa69f3681a1",
+        "gemm_i8.hpp": "cd18b8b57aa890022611210e3ae06f99127a3762c9173ed154adcd2b6d701081",
+        "q8_device.hpp": "93921317d9ee2061ee8f6a130188921aef7ffc81f9e84a6867f9e2ea825e1a33",
     },
-    "fetch_kib": 491409.5, "write_kib": 253501.5,
-    "copy_kib": 524288.0, "copy_fetch_kib": 262156.4, "copy_write_kib": 524288.0,
+    "fetch_kib": 367721.7, "write_kib": 261641.9,
+    "copy_kib": 524288.0, "copy_fetch_kib": 262155.5, "copy_write_kib": 524288.0,
 }
 
 
