@@ -237,6 +237,28 @@ def copy_calibration(dev, nbytes=512 << 20, reps=3):
             "GB/s": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
+def quant_after(quant, before, iters: int) -> float:
+    """Median time (ms) of quant() measured with events on the launch stream
+    when each call follows a call of before() (whose traffic evicts quant's
+    input from the caches, as in the step)."""
+    s = torch.cuda.current_stream()
+    for _ in range(3):
+        before()
+        quant()
+    s.synchronize()
+    ev = []
+    for _ in range(iters):
+        before()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        quant()
+        e1.record(s)
+        ev.append((e0, e1))
+    s.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    return ts[len(ts) // 2]
+
+
 def rmsnorm_quant_gbs(dev, iters=20):
     """Residual add + RMSNorm + per-token quant at the prefill shape: bytes
     = x read + residual read and write + codes + scales (+ gamma), over the
@@ -499,8 +521,13 @@ def main():
                 "traffic_read_write": traffic, "algorithmic_bytes": algo_bytes,
                 "kernel": "gemm_big_kernel (per-channel epilogue, 256 x 384 tiles)",
                 "kernel_us": gemm_ms * 1e3}
+    quant_step_ms = quant_after(quant, gemm, args.steps)
     secondary = {"quant_kernel": {"us": quant_ms * 1e3,
-                                  "GB/s": quant_bytes / (quant_ms * 1e-3) / 1e9}}
+                                  "GB/s": quant_bytes / (quant_ms * 1e-3) / 1e9,
+                                  "timing": "back to back, X left in the last-level cache",
+                                  "in_step_us": quant_step_ms * 1e3,
+                                  "in_step_GB/s": quant_bytes / (quant_step_ms * 1e-3) / 1e9,
+                                  "in_step_timing": "each call right after a GEMM, as in the step: X read from HBM"}}
     names = [] if args.no_secondary or args.secondary == "none" else args.secondary.split(",")
     for name in names:
         if name not in SECONDARY:

@@ -156,7 +156,11 @@ __global__ __launch_bounds__(256) void quant_per_token_reg(
     for (int i = 0; i < NC; ++i) {
         const int c = lane + 64 * i;
         if (c < nch) {
-            v[i] = xr[c];
+            // Streaming (non-temporal) load: the row is read once.  With X in
+            // HBM (as after a large GEMM) this quantizer takes 33 us instead
+            // of 43 at 8192 x 5120; with X still in the last-level cache it
+            // takes 31 instead of 27, since these loads do not keep it there.
+            v[i] = __builtin_nontemporal_load(&xr[c]);
             mx = mag_max8(mx, v[i]);
         }
     }
