@@ -244,6 +244,18 @@ def test_w8a16_f16_full_size_sampled_rows():
                      "w8a16 f16 sampled rows")
 
 
+def test_w8a16_f16_big_tiles_sampled_rows():
+    """The 256 x 320 tiles (4100 x 4000: 544 tiles of 256 x 128 against 221),
+    ragged on both edges; sampled rows, every column."""
+    M, N, K = 4100, 4000, 256
+    say("w8a16 f16 big tiles", M, N, K)
+    xf, wq_ref, sc_ref = _w8a16_inputs(M, N, K, seed=5)
+    y = q8.w8a16_mm_f16(dev(xf), dev(wq_ref), dev(sc_ref))
+    rows = np.array([0, 1, 31, 32, 255, 256, 2047, 4095, 4096, 4099])
+    _check_w8a16_f16(hbits(host(y))[rows], np.ascontiguousarray(hbits(xf)[rows]), wq_ref, sc_ref,
+                     "w8a16 f16 big tiles")
+
+
 @pytest.mark.parametrize("M", [0, 4, 100])
 def test_w8a16_f16_empty_and_overflow_to_infinity(M):
     """M = 0 is a no-op; sums beyond the fp16 range become infinity (small

@@ -626,6 +626,22 @@ def test_w8a16_few_tokens_weight_stream(M, N, K, pad):
         assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
 
 
+@pytest.mark.parametrize("M,N,K", [(4100, 4000, 256), (8192, 5120, 1024)])
+def test_w8a16_big_tiles_sampled_rows(M, N, K):
+    """Large problems run on 256 x 320 tiles when that needs fewer whole
+    waves (4100 x 4000: 544 tiles of 256 x 128 against 221 of 256 x 320),
+    here with ragged tiles on both edges; sampled rows, every column."""
+    say("w8a16 big tiles", M, N, K)
+    wl = synth.WORKLOADS["w8a16"]
+    x = synth.activations(wl, 2, M=M, K=K)
+    w = synth.weights(wl, 2, N=N, K=K)
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y = q8.w8a16_mm(dev(x), dev(torch.from_numpy(wq_ref)), dev(torch.from_numpy(sc_ref)))
+    rows = BIG_ROWS[BIG_ROWS < M]
+    _check_w8a16(bits(host(y))[rows], np.ascontiguousarray(bits(x)[rows]), wq_ref, sc_ref,
+                 f"w8a16 big tiles {M}x{N}x{K}")
+
+
 def test_w8a16_full_size_sampled_rows():
     wl = synth.WORKLOADS["w8a16"]
     say("w8a16 full size")

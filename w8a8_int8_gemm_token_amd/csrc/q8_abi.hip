@@ -12,6 +12,7 @@
 #include "norm_quant.hpp"
 #include "w8a16.hpp"
 #include "gemm_big.hpp"
+#include "gemm_w16.hpp"
 #include "stream_gemm.hpp"
 #include "fp8.hpp"
 
@@ -275,9 +276,15 @@ q8_status w8a16_impl(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ld
     GemmArgs p{reinterpret_cast<const int8_t*>(x), 2 * ldx, w, ldw, nullptr, scale_ch, c, ldc,
                (int)M, (int)N, (int)K};
     if (!gemm_offsets_fit(p)) return Q8_EUNSUPPORTED;
-    const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
-    if (tiles >= 256) return hip_status(launch_gemm_i8<256, 128, 4, 2, E, 8>(p, st(stream)));
-    return hip_status(launch_gemm_i8<128, 128, 2, 2, E, 8>(p, st(stream)));
+    const int64_t nbm = (M + 255) / 256;
+    const int64_t t128 = nbm * ((N + 127) / 128), t320 = nbm * ((N + 319) / 320);
+    if (t128 < 256) return hip_status(launch_gemm_i8<128, 128, 2, 2, E, 8>(p, st(stream)));
+    // Whole waves of 256 tiles; a wave of 256 x 320 tiles takes about 2.2
+    // times as long as one of 256 x 128 (measured at 8192 x 5120 x 13824:
+    // 447 us against 211).
+    const int64_t w128 = (t128 + 255) / 256, w320 = (t320 + 255) / 256;
+    if (220 * w320 < 100 * w128 && gemm_w16_offsets_fit(p)) return hip_status(launch_gemm_w16<F16>(p, st(stream)));
+    return hip_status(launch_gemm_i8<256, 128, 4, 2, E, 8>(p, st(stream)));
 }
 }  // namespace
 
