@@ -151,8 +151,10 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
         for (int i = d * per; i < b1; ++i) {
             const int r = i / NC, u = i - r * NC;
             const int voff = r * (int)p.ldw + u * 1024 + ((lane ^ (r & 15)) << 4);
+            // cache policy 2 = non-temporal: every weight byte is read once
+            // per call (measured 0.4-0.6 us faster per call at N = K = 5120)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (Q8_LDS void*)(wt + r * K + u * 1024), 16,
-                                                     voff, 0, 0, 0);
+                                                     voff, 0, 0, 2);
         }
         wait_vm_lgkm0<0>();  // this wave's part of the tile landed
     }

@@ -252,8 +252,9 @@ __global__ __launch_bounds__(1024) void stream_gemm_kernel(StreamArgs p) {
             for (int j = 0; j < cnt; ++j) {
                 const int r = d + 8 * j;
                 const int voff = r * (int)p.ldw + sg * SG_SEG + ((lane ^ (r & 15)) << 4);
+                // non-temporal (cache policy 2): the weights are read once
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (Q8_LDS void*)(slot + r * SG_SEG), 16, voff,
-                                                         0, 0, 0);
+                                                         0, 0, 2);
             }
         };
         const int first = min(nbuf, nseg);
