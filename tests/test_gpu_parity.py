@@ -626,20 +626,27 @@ def test_w8a16_few_tokens_weight_stream(M, N, K, pad):
         assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
 
 
-@pytest.mark.parametrize("M,N,K", [(4100, 4000, 256), (8192, 5120, 1024)])
-def test_w8a16_big_tiles_sampled_rows(M, N, K):
+@pytest.mark.parametrize("M,N,K,pad", [(4100, 4000, 256, 0), (8192, 5120, 1024, 0), (4100, 4000, 384, 64)])
+def test_w8a16_big_tiles_sampled_rows(M, N, K, pad):
     """Large problems run on 256 x 320 tiles when that needs fewer whole
     waves (4100 x 4000: 544 tiles of 256 x 128 against 221 of 256 x 320),
-    here with ragged tiles on both edges; sampled rows, every column."""
-    say("w8a16 big tiles", M, N, K)
+    here with ragged tiles on both edges and, with pad, strided x, w and y;
+    sampled rows, every column."""
+    say("w8a16 big tiles", M, N, K, pad)
     wl = synth.WORKLOADS["w8a16"]
-    x = synth.activations(wl, 2, M=M, K=K)
+    xf = synth.activations(wl, 2, M=M, K=K + pad)
+    x = xf[:, :K].contiguous()
     w = synth.weights(wl, 2, N=N, K=K)
     wq_ref, sc_ref = oracle.quant_weight(w.numpy())
-    y = q8.w8a16_mm(dev(x), dev(torch.from_numpy(wq_ref)), dev(torch.from_numpy(sc_ref)))
+    wq_full = torch.zeros((N, K + pad), dtype=torch.int8, device=DEV)
+    wq_full[:, :K] = dev(torch.from_numpy(wq_ref))
+    yfull = torch.full((M, N + pad), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    y = q8.w8a16_mm(dev(xf)[:, :K], wq_full[:, :K], dev(torch.from_numpy(sc_ref)), out=yfull[:, :N])
     rows = BIG_ROWS[BIG_ROWS < M]
-    _check_w8a16(bits(host(y))[rows], np.ascontiguousarray(bits(x)[rows]), wq_ref, sc_ref,
+    _check_w8a16(bits(host(y).contiguous())[rows], np.ascontiguousarray(bits(x)[rows]), wq_ref, sc_ref,
                  f"w8a16 big tiles {M}x{N}x{K}")
+    if pad:
+        assert (host(yfull)[:, N:].view(torch.int16) == -1).all(), "wrote outside the output view"
 
 
 def test_w8a16_full_size_sampled_rows():
