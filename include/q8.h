@@ -156,10 +156,12 @@ q8_status w8a16_mm(const q8_bf16 *x, int64_t ldx, const int8_t *w,
  * q8_quant_scaled_mm -- the whole W8A8 layer in one call: per-token
  * quantization of x (as q8_quant_per_token) followed by q8_scaled_mm.
  * The quantized activations and their scales are written to the caller's
- * xq / scale_tok buffers (they are outputs, and the GEMM's inputs).  Two
- * kernels run back to back on `stream`: the row quantizer, then the GEMM
- * (for M <= 16 and K a multiple of 1024 up to 10240, a weight-streaming
- * kernel that reads each weight byte once; otherwise the tiled GEMM).
+ * xq / scale_tok buffers (they are outputs, and the GEMM's inputs).  For
+ * M <= 8 and K a multiple of 1024 up to 8192 one kernel does both (every
+ * workgroup quantizes the rows for itself while its weights stream in).
+ * Otherwise two kernels run back to back on `stream`: the row quantizer,
+ * then the GEMM of q8_scaled_mm (for few tokens a weight-streaming kernel
+ * that reads each weight byte once, else the tiled GEMM).
  *   x [M, ldx] bf16; b [N, ldb] int8; scale_ch [N]; c [M, ldc] bf16;
  *   xq [M, K] int8 (dense, ld = K), scale_tok [M] fp32.
  * Rules: as q8_scaled_mm, plus ldx >= K a multiple of 8, x 16-byte aligned.

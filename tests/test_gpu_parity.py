@@ -419,6 +419,42 @@ def test_decode_one_call_shapes(M, N, K, pad):
         assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
 
 
+@pytest.mark.parametrize("M,N,K,pad", [
+    (1, 16, 128, 0),        # one partial segment, one K block per active wave
+    (8, 1040, 1152, 16),    # 1024 + 128, strided operands
+    (17, 4112, 4480, 0),    # two token groups, last workgroup ragged
+    (33, 2048, 13824, 16),  # four token groups, 13.5 segments
+    (64, 5120, 2176, 0),
+])
+def test_scaled_mm_few_tokens_partial_segment(M, N, K, pad):
+    """Few tokens with K a multiple of 128 but not of 1024: the
+    weight-streaming kernel's last K segment is partial (loads past K read
+    nothing, its K blocks past K are skipped). q8_scaled_mm and the one-call
+    layer against the oracle, strided x, w and y."""
+    say("scaled_mm partial segment", M, N, K, pad)
+    xf, wf = synth.custom(M, K + pad, N, seed=3 * M + K, outlier_cols=K // 64)
+    x = xf[:, :K].contiguous()
+    w = wf[:, :K].contiguous()
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y_ref = oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref)
+    wq_full = torch.zeros((N, K + pad), dtype=torch.int8, device=DEV)
+    wq_full[:, :K] = dev(torch.from_numpy(wq_ref))
+    wq = wq_full[:, :K]
+    sc = dev(torch.from_numpy(sc_ref))
+    xq_full = torch.zeros((M, K + pad), dtype=torch.int8, device=DEV)
+    xq_full[:, :K] = dev(torch.from_numpy(xq_ref))
+    yfull = torch.full((M, N + pad), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    y = q8.q8_scaled_mm(xq_full[:, :K], wq, dev(torch.from_numpy(st_ref)), sc, out=yfull[:, :N])
+    assert_ulp1(bits(host(y).contiguous()), y_ref, f"scaled_mm {M}x{N}x{K}")
+    if pad:
+        assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
+    y2, xq2, st2 = q8.q8_quant_scaled_mm(dev(xf)[:, :K], wq, sc)
+    np.testing.assert_array_equal(host(xq2).numpy(), xq_ref)
+    np.testing.assert_array_equal(host(st2).numpy(), st_ref)
+    assert_ulp1(bits(host(y2)), y_ref, f"quant_scaled_mm {M}x{N}x{K}")
+
+
 def test_scaled_mm_ragged_and_zero_rows():
     M, N, K = 131, 208, 384
     x, w = synth.custom(M, K, N, seed=5, outlier_cols=4)
@@ -604,12 +640,15 @@ def test_w8a16_shapes(M, N, K):
                                        (8, 5120, 17408, 0), (16, 5120, 5120, 32),
                                        (3, 17408, 5120, 0), (16, 8192, 1024, 0),
                                        (17, 5120, 3072, 16), (33, 1040, 4096, 0),
-                                       (64, 5120, 17408, 0)])
+                                       (64, 5120, 17408, 0),
+                                       # K not a multiple of 1024: a partial last segment
+                                       (1, 16, 128, 0), (8, 5120, 13824, 0), (33, 1040, 1152, 16),
+                                       (64, 4112, 4480, 0), (17, 2048, 13824, 16)])
 def test_w8a16_few_tokens_weight_stream(M, N, K, pad):
-    """M <= 64 with K a multiple of 1024: the weight-streaming kernel (ring
-    of K segments in LDS; 1, 2 or 4 groups of 16 tokens), including the down
-    projection's 5120 x 17408 and several workgroups per CU for large N;
-    strided x, w and y."""
+    """M <= 64: the weight-streaming kernel (ring of 1024-deep K segments in
+    LDS; 1, 2 or 4 groups of 16 tokens), including the down projection's
+    5120 x 17408, several workgroups per CU for large N, and K with a partial
+    last segment (the W8A16 workload's 13824); strided x, w and y."""
     say("w8a16 stream", M, N, K, pad)
     wl = synth.WORKLOADS["w8a16"]
     xf = synth.activations(wl, 1, M=M, K=K + pad)

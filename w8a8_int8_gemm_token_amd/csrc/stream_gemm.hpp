@@ -32,6 +32,10 @@
 // the last valid one; their outputs are never stored.
 // Segment slot layout: [R][1024] bytes, 16-byte unit u of row r stored at
 // unit u ^ (r & 15), so the fragment reads of 16 rows are conflict-free.
+// K is a multiple of 128; when it is not one of 1024 the last segment is
+// partial: its loads past K read nothing (out-of-range offsets return zero)
+// and the multiplying waves skip its K blocks past K, activation loads
+// included.
 #pragma once
 
 #include <type_traits>
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(1024) void stream_gemm_kernel(StreamArgs p) {
     __shared__ int ready[SG_MAX_SEG];  // loading waves done with segment s (8 = landed)
     __shared__ int freed[SG_MAX_SEG];  // multiplying waves done with segment s (8 = free)
 
-    const int M = p.M, K = p.K, nseg = K / SG_SEG, nbuf = p.nbuf;
+    const int M = p.M, K = p.K, nseg = (K + SG_SEG - 1) / SG_SEG, nbuf = p.nbuf;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int R = p.rows;
@@ -184,18 +188,26 @@ __global__ __launch_bounds__(1024) void stream_gemm_kernel(StreamArgs p) {
             return *reinterpret_cast<const v4u*>(xb[g] + (int64_t)(sg * SG_SEG + KB * (BPW * wid + j)) *
                                                              (I8 ? 1 : 2));
         };
+        // K block j of segment sg lies below K (wave-uniform; a block is
+        // wholly inside or outside since K % 128 == 0 and KB <= 64)
+        auto live = [&](int sg, int j) __attribute__((always_inline)) {
+            return sg * SG_SEG + KB * (BPW * wid + j) < K;
+        };
         for (int sg = 0; sg < nseg; ++sg) {
             v4u b[PRE ? BPW : 1][MG];
             if constexpr (PRE) {
 #pragma unroll
                 for (int j = 0; j < BPW; ++j)
+                    if (live(sg, j)) {
 #pragma unroll
-                    for (int g = 0; g < MG; ++g) b[j][g] = bload(sg, j, g);
+                        for (int g = 0; g < MG; ++g) b[j][g] = bload(sg, j, g);
+                    }
             }
             sg_wait_ge(&ready[sg], 8);
             const int8_t* slot = lds + (sg % nbuf) * slot_bytes;
 #pragma unroll
             for (int jj = 0; jj < BPW; ++jj) {
+                if (!live(sg, jj)) break;  // the rest of a partial last segment
                 const int j = PRE ? jj : 0;
                 if constexpr (!PRE) {
 #pragma unroll
@@ -251,7 +263,9 @@ __global__ __launch_bounds__(1024) void stream_gemm_kernel(StreamArgs p) {
             int8_t* slot = lds + (sg % nbuf) * slot_bytes;
             for (int j = 0; j < cnt; ++j) {
                 const int r = d + 8 * j;
-                const int voff = r * (int)p.ldw + sg * SG_SEG + ((lane ^ (r & 15)) << 4);
+                const int ku = sg * SG_SEG + ((lane ^ (r & 15)) << 4);  // K byte of this lane's unit
+                // past K: an offset beyond the resource, which reads as zero
+                const int voff = ku < K ? r * (int)p.ldw + ku : 0x7FFFFFF0;
                 // non-temporal (cache policy 2): the weights are read once
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (Q8_LDS void*)(slot + r * SG_SEG), 16, voff,
                                                          0, 0, 2);
@@ -322,9 +336,9 @@ inline int sg_rows(int N) {
     return best;
 }
 
-// M <= max_m, K a multiple of 1024, 32-bit buffer offsets for the tile.
+// M <= max_m, K a multiple of 128, 32-bit buffer offsets for the tile.
 inline bool sg_fits(int M, int N, int K, int64_t ldw, int max_m) {
-    if (M < 1 || M > max_m || K % SG_SEG != 0 || K / SG_SEG > SG_MAX_SEG) return false;
+    if (M < 1 || M > max_m || K % 128 != 0 || (K + SG_SEG - 1) / SG_SEG > SG_MAX_SEG) return false;
     return (int64_t)sg_rows(N) * ldw < ((int64_t)1 << 31);
 }
 
