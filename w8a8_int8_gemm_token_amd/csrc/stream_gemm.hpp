@@ -33,9 +33,9 @@
 // Segment slot layout: [R][1024] bytes, 16-byte unit u of row r stored at
 // unit u ^ (r & 15), so the fragment reads of 16 rows are conflict-free.
 // K is a multiple of 128; when it is not one of 1024 the last segment is
-// partial: its loads past K read nothing (out-of-range offsets return zero)
-// and the multiplying waves skip its K blocks past K, activation loads
-// included.
+// partial: its weight loads past K read nothing (an out-of-range offset
+// returns zero), and the multiplying waves' K blocks past K pair those zeros
+// with the last valid block's activations, adding exact zeros.
 #pragma once
 
 #include <type_traits>
@@ -130,8 +130,14 @@ __device__ __forceinline__ v8bf16 i8x8_to_bf16x8(v2u raw) {
 }
 
 // F16 (W8A16 only): fp16 activations, v_mfma_f32_16x16x32_f16.
+// Up to 32 tokens (I8) or 16 (bf16) a workgroup fits in 64 registers per
+// lane, so two workgroups share a CU when the tile is small (large N); the
+// second launch-bounds argument (waves per SIMD) keeps it there.
+template <bool I8, int MG>
+constexpr int sg_waves_per_simd() { return (I8 ? MG <= 2 : MG == 1) ? 8 : 4; }
+
 template <bool I8, int MG, bool F16 = false>
-__global__ __launch_bounds__(1024) void stream_gemm_kernel(StreamArgs p) {
+__global__ __launch_bounds__(1024, (sg_waves_per_simd<I8, MG>())) void stream_gemm_kernel(StreamArgs p) {
     // K blocks per MFMA: 64 (int8) or 32 (bf16); per segment and wave
     constexpr int KB = I8 ? 64 : 32;
     constexpr int BPW = SG_SEG / KB / 8;
@@ -184,34 +190,34 @@ __global__ __launch_bounds__(1024) void stream_gemm_kernel(StreamArgs p) {
         // activation fragments (16 bytes per lane: 16 codes or 8 bf16) are
         // loaded before the wait on the segment when they fit in registers
         constexpr bool PRE = BPW * MG <= 8;
-        auto bload = [&](int sg, int j, int g) __attribute__((always_inline)) {
-            return *reinterpret_cast<const v4u*>(xb[g] + (int64_t)(sg * SG_SEG + KB * (BPW * wid + j)) *
-                                                             (I8 ? 1 : 2));
-        };
-        // K block j of segment sg lies below K (wave-uniform; a block is
-        // wholly inside or outside since K % 128 == 0 and KB <= 64)
-        auto live = [&](int sg, int j) __attribute__((always_inline)) {
-            return sg * SG_SEG + KB * (BPW * wid + j) < K;
+        // A wave's K range in a segment is 128 wide and 128-aligned, so with
+        // K % 128 == 0 it lies wholly below or past K.  Past K (in a partial
+        // last segment) the wave re-reads the last valid range's
+        // activations: finite values (non-finite inputs are out of
+        // contract) that meet the zeros the loading waves left in the slot
+        // there, so those products add exact zeros (an fp32 sum that starts
+        // at +0 never becomes -0, so even the sign of zero is unchanged).
+        static_assert(KB * BPW == 128, "one 128-deep K range per wave and segment");
+        auto bload = [&](int kb, int j, int g) __attribute__((always_inline)) {
+            return *reinterpret_cast<const v4u*>(xb[g] + (int64_t)(kb + KB * j) * (I8 ? 1 : 2));
         };
         for (int sg = 0; sg < nseg; ++sg) {
+            const int kb = min(sg * SG_SEG + KB * BPW * wid, K - KB * BPW);
             v4u b[PRE ? BPW : 1][MG];
             if constexpr (PRE) {
 #pragma unroll
                 for (int j = 0; j < BPW; ++j)
-                    if (live(sg, j)) {
 #pragma unroll
-                        for (int g = 0; g < MG; ++g) b[j][g] = bload(sg, j, g);
-                    }
+                    for (int g = 0; g < MG; ++g) b[j][g] = bload(kb, j, g);
             }
             sg_wait_ge(&ready[sg], 8);
             const int8_t* slot = lds + (sg % nbuf) * slot_bytes;
 #pragma unroll
             for (int jj = 0; jj < BPW; ++jj) {
-                if (!live(sg, jj)) break;  // the rest of a partial last segment
                 const int j = PRE ? jj : 0;
                 if constexpr (!PRE) {
 #pragma unroll
-                    for (int g = 0; g < MG; ++g) b[0][g] = bload(sg, jj, g);
+                    for (int g = 0; g < MG; ++g) b[0][g] = bload(kb, jj, g);
                 }
                 const int o = KB * (BPW * wid + jj) + (I8 ? 16 : 8) * kg;  // byte of K in the row
                 const int u = o >> 4;
@@ -264,8 +270,9 @@ __global__ __launch_bounds__(1024) void stream_gemm_kernel(StreamArgs p) {
             for (int j = 0; j < cnt; ++j) {
                 const int r = d + 8 * j;
                 const int ku = sg * SG_SEG + ((lane ^ (r & 15)) << 4);  // K byte of this lane's unit
-                // past K: an offset beyond the resource, which reads as zero
-                const int voff = ku < K ? r * (int)p.ldw + ku : 0x7FFFFFF0;
+                // past K: offset 2^31, beyond any resource here (sg_fits keeps
+                // rows * ldw below 2^31), which reads as zero
+                const int voff = ku < K ? r * (int)p.ldw + ku : INT32_MIN;
                 // non-temporal (cache policy 2): the weights are read once
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (Q8_LDS void*)(slot + r * SG_SEG), 16, voff,
                                                          0, 0, 2);
