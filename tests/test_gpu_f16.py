@@ -101,7 +101,8 @@ def test_quant_f16_near_ties_subnormals_and_zero_rows():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (8, 128, 1024), (16, 1040, 2048), (33, 144, 384),
-                                   (64, 256, 1024), (130, 272, 1152), (300, 2560, 1024)])
+                                   (64, 256, 1024), (100, 1040, 1024),  # 100: two streaming passes
+                                   (130, 272, 1152), (300, 2560, 1024)])
 def test_scaled_mm_f16(M, N, K):
     say("scaled_mm f16", M, N, K)
     x, w = synth.custom(M, K, N, seed=M + 3 * N, outlier_cols=3)
@@ -215,7 +216,8 @@ def _w8a16_inputs(M, N, K, seed, pad=0):
     (16, 128, 256, 0), (33, 144, 384, 8),          # few tokens, K not a multiple of 1024
     (1, 16, 1024, 0), (5, 4112, 2048, 16), (16, 5120, 5120, 0), (33, 1040, 4096, 0),
     (64, 2048, 3072, 0),                            # few tokens: weight streaming
-    (65, 272, 1152, 0), (130, 256, 1024, 8), (300, 128, 13824, 0)])  # tiled
+    (65, 272, 1152, 0), (120, 1040, 2048, 8),       # 65-128 tokens: two streaming passes
+    (130, 256, 1024, 8), (300, 128, 13824, 0)])     # tiled
 def test_w8a16_f16_shapes(M, N, K, pad):
     """Each route of the weight-only GEMM with fp16 activations (small-M
     tiles, the weight-streaming ring, the tiled kernel), strided x and y."""

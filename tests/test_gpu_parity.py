@@ -455,6 +455,43 @@ def test_scaled_mm_few_tokens_partial_segment(M, N, K, pad):
     assert_ulp1(bits(host(y2)), y_ref, f"quant_scaled_mm {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,pad", [
+    (65, 1040, 1024, 16),   # 64 + 1 tokens
+    (100, 5120, 1152, 0),   # the second pass has 36 tokens and a partial K segment
+    (128, 2048, 4096, 16),
+])
+def test_scaled_mm_two_streaming_passes(M, N, K, pad):
+    """65-128 tokens with under 64 channel tiles run the weight-streaming
+    kernel twice (tokens 0-63, then the rest). q8_scaled_mm and the one-call
+    layer against the oracle, with a zero row in each pass and strided x, w
+    and y."""
+    say("scaled_mm two passes", M, N, K, pad)
+    xf, wf = synth.custom(M, K + pad, N, seed=7 * M + N, outlier_cols=K // 64)
+    x = xf[:, :K].contiguous()
+    x[3] = 0
+    x[M - 2] = 0
+    xf[:, :K] = x
+    w = wf[:, :K].contiguous()
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y_ref = oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref)
+    wq_full = torch.zeros((N, K + pad), dtype=torch.int8, device=DEV)
+    wq_full[:, :K] = dev(torch.from_numpy(wq_ref))
+    wq = wq_full[:, :K]
+    sc = dev(torch.from_numpy(sc_ref))
+    xq_full = torch.zeros((M, K + pad), dtype=torch.int8, device=DEV)
+    xq_full[:, :K] = dev(torch.from_numpy(xq_ref))
+    yfull = torch.full((M, N + pad), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    y = q8.q8_scaled_mm(xq_full[:, :K], wq, dev(torch.from_numpy(st_ref)), sc, out=yfull[:, :N])
+    assert_ulp1(bits(host(y).contiguous()), y_ref, f"scaled_mm {M}x{N}x{K}")
+    if pad:
+        assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
+    y2, xq2, st2 = q8.q8_quant_scaled_mm(dev(xf)[:, :K], wq, sc)
+    np.testing.assert_array_equal(host(xq2).numpy(), xq_ref)
+    np.testing.assert_array_equal(host(st2).numpy(), st_ref)
+    assert_ulp1(bits(host(y2)), y_ref, f"quant_scaled_mm {M}x{N}x{K}")
+
+
 def test_scaled_mm_ragged_and_zero_rows():
     M, N, K = 131, 208, 384
     x, w = synth.custom(M, K, N, seed=5, outlier_cols=4)
@@ -643,12 +680,16 @@ def test_w8a16_shapes(M, N, K):
                                        (64, 5120, 17408, 0),
                                        # K not a multiple of 1024: a partial last segment
                                        (1, 16, 128, 0), (8, 5120, 13824, 0), (33, 1040, 1152, 16),
-                                       (64, 4112, 4480, 0), (17, 2048, 13824, 16)])
+                                       (64, 4112, 4480, 0), (17, 2048, 13824, 16),
+                                       # 65-128 tokens, few channel tiles: two streaming passes
+                                       (65, 1040, 2048, 16), (97, 5120, 3072, 0), (128, 4112, 1152, 0)])
 def test_w8a16_few_tokens_weight_stream(M, N, K, pad):
-    """M <= 64: the weight-streaming kernel (ring of 1024-deep K segments in
-    LDS; 1, 2 or 4 groups of 16 tokens), including the down projection's
-    5120 x 17408, several workgroups per CU for large N, and K with a partial
-    last segment (the W8A16 workload's 13824); strided x, w and y."""
+    """The weight-streaming kernel (ring of 1024-deep K segments in LDS; 1,
+    2 or 4 groups of 16 tokens): M <= 64 in one pass, and 65-128 tokens with
+    under 64 channel tiles in two (64, then the rest); including the down
+    projection's 5120 x 17408, several workgroups per CU for large N, and K
+    with a partial last segment (the W8A16 workload's 13824); strided x, w
+    and y."""
     say("w8a16 stream", M, N, K, pad)
     wl = synth.WORKLOADS["w8a16"]
     xf = synth.activations(wl, 1, M=M, K=K + pad)
