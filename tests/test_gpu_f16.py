@@ -102,7 +102,8 @@ def test_quant_f16_near_ties_subnormals_and_zero_rows():
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (8, 128, 1024), (16, 1040, 2048), (33, 144, 384),
                                    (64, 256, 1024), (100, 1040, 1024),  # 100: two streaming passes
-                                   (130, 272, 1152), (300, 2560, 1024)])
+                                   (130, 272, 1152), (300, 2560, 1024),
+                                   (200, 9216, 256), (450, 8192, 128)])  # 64 x 128, 128 x 128 tiles
 def test_scaled_mm_f16(M, N, K):
     say("scaled_mm f16", M, N, K)
     x, w = synth.custom(M, K, N, seed=M + 3 * N, outlier_cols=3)

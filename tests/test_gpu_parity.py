@@ -254,7 +254,9 @@ def test_smooth_fold_cap_and_in_place():
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (16, 128, 256), (31, 144, 384),
                                    (64, 256, 128), (65, 128, 256), (130, 272, 640),
-                                   (257, 400, 1024), (300, 512, 512)])
+                                   (257, 400, 1024), (300, 512, 512),
+                                   (200, 9216, 256),    # 64 x 128 tiles (504 of 32 x 128)
+                                   (450, 8192, 128)])   # 128 x 128 tiles
 def test_mm_i32(M, N, K):
     say("mm_i32", M, N, K)
     a = synth.int8_uniform((M, K), seed=M + K)
@@ -490,6 +492,20 @@ def test_scaled_mm_two_streaming_passes(M, N, K, pad):
     np.testing.assert_array_equal(host(xq2).numpy(), xq_ref)
     np.testing.assert_array_equal(host(st2).numpy(), st_ref)
     assert_ulp1(bits(host(y2)), y_ref, f"quant_scaled_mm {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(97, 9216, 384), (200, 9216, 256), (450, 8192, 128)])
+def test_scaled_mm_mid_token_tiles(M, N, K):
+    """65-512 tokens where 256 x 256 tiles are too few: 32 x 128, 64 x 128
+    and 128 x 128 tiles by workgroup count (ragged M), against the oracle."""
+    say("scaled_mm mid tiles", M, N, K)
+    x, w = synth.custom(M, K, N, seed=M + N + K, outlier_cols=4)
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y_ref = oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref)
+    y = q8.q8_scaled_mm(dev(torch.from_numpy(xq_ref)), dev(torch.from_numpy(wq_ref)),
+                        dev(torch.from_numpy(st_ref)), dev(torch.from_numpy(sc_ref)))
+    assert_ulp1(bits(host(y)), y_ref, f"mid tiles {M}x{N}x{K}")
 
 
 def test_scaled_mm_ragged_and_zero_rows():

@@ -85,7 +85,17 @@ hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
     if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
     const int64_t nbm = (p.M + 255) / 256;
     const int64_t t256 = nbm * ((p.N + 255) / 256), t384 = nbm * ((p.N + 383) / 384);
-    if (t256 < 256) return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
+    if (t256 < 256) {
+        // Too few 256 x 256 tiles to fill the chip: the tile with the fewest
+        // bytes per product among those that still give at most 420
+        // workgroups (measured over 65-384 tokens at N = 5120, 15360 and
+        // 17408: 32 x 128 tiles won below that count, 64 x 128 next, and
+        // 128 x 128 beyond; 10-20% apart).
+        const int64_t nt = (p.N + 127) / 128;
+        if ((p.M + 31) / 32 * nt <= 420) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
+        if ((p.M + 63) / 64 * nt <= 420) return launch_gemm_i8<64, 128, 2, 2, EPI, 8>(p, s);
+        return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
+    }
     // Whole waves of 256 tiles (a partly filled last wave costs a whole
     // one); a wave of 256 x 384 tiles takes about 1.4 times as long as one
     // of 256 x 256 (measured at the prefill shape: 111.5 us against 78-83).
