@@ -217,7 +217,8 @@ def _w8a16_inputs(M, N, K, seed, pad=0):
     (16, 128, 256, 0), (33, 144, 384, 8),          # few tokens, K not a multiple of 1024
     (1, 16, 1024, 0), (5, 4112, 2048, 16), (16, 5120, 5120, 0), (33, 1040, 4096, 0),
     (64, 2048, 3072, 0),                            # few tokens: weight streaming
-    (65, 272, 1152, 0), (120, 1040, 2048, 8),       # 65-128 tokens: two streaming passes
+    (65, 272, 1152, 0), (100, 1040, 2048, 8),       # 65-112 tokens: two streaming passes
+    (192, 5120, 1024, 0), (300, 5120, 512, 8),      # 32 x 128 and 64 x 128 tiles
     (130, 256, 1024, 8), (300, 128, 13824, 0)])     # tiled
 def test_w8a16_f16_shapes(M, N, K, pad):
     """Each route of the weight-only GEMM with fp16 activations (small-M

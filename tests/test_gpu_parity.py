@@ -697,12 +697,15 @@ def test_w8a16_shapes(M, N, K):
                                        # K not a multiple of 1024: a partial last segment
                                        (1, 16, 128, 0), (8, 5120, 13824, 0), (33, 1040, 1152, 16),
                                        (64, 4112, 4480, 0), (17, 2048, 13824, 16),
-                                       # 65-128 tokens, few channel tiles: two streaming passes
-                                       (65, 1040, 2048, 16), (97, 5120, 3072, 0), (128, 4112, 1152, 0)])
+                                       # 65-112 tokens, few channel tiles: two streaming passes
+                                       (65, 1040, 2048, 16), (97, 5120, 3072, 0), (112, 4112, 1152, 0),
+                                       # more tokens, few channel tiles: 32 x 128 and 64 x 128 tiles
+                                       (192, 5120, 1024, 0), (300, 5120, 512, 16), (130, 9216, 256, 0)])
 def test_w8a16_few_tokens_weight_stream(M, N, K, pad):
     """The weight-streaming kernel (ring of 1024-deep K segments in LDS; 1,
-    2 or 4 groups of 16 tokens): M <= 64 in one pass, and 65-128 tokens with
-    under 64 channel tiles in two (64, then the rest); including the down
+    2 or 4 groups of 16 tokens): M <= 64 in one pass, and 65-112 tokens with
+    under 64 channel tiles in two (64, then the rest), then the tiles that
+    follow them (32 x 128, 64 x 128); including the down
     projection's 5120 x 17408, several workgroups per CU for large N, and K
     with a partial last segment (the W8A16 workload's 13824); strided x, w
     and y."""

@@ -292,10 +292,11 @@ q8_status w8a16_impl(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ld
         const StreamArgs q{x, ldx, w, ldw, nullptr, scale_ch, c, ldc, (int)M, (int)N, (int)K, 0, 0, 0};
         return hip_status(launch_stream<false, F16>(q, st(stream)));
     }
-    // 65-128 tokens and under 64 channel tiles of 128: two streaming passes
+    // 65-112 tokens and under 64 channel tiles of 128: two streaming passes
     // (64 tokens, then the rest) instead of a tiled grid that leaves most
-    // CUs idle (5120 x 17408: about 110-170 against 200 us)
-    if (M > SG_MAX_M && M <= 2 * SG_MAX_M && (N + 127) / 128 < 64 &&
+    // CUs idle (5120 x 17408: 113-129 against 165-200 us; from about 120
+    // tokens the 32 x 128 tiles below are faster)
+    if (M > SG_MAX_M && M <= 112 && (N + 127) / 128 < 64 &&
         sg_fits(SG_MAX_M, (int)N, (int)K, ldw, SG_MAX_M)) {
         for (int h = 0; h < 2; ++h) {
             const int64_t m0 = h * SG_MAX_M;
@@ -317,7 +318,16 @@ q8_status w8a16_impl(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ld
     if (!gemm_offsets_fit(p)) return Q8_EUNSUPPORTED;
     const int64_t nbm = (M + 255) / 256;
     const int64_t t128 = nbm * ((N + 127) / 128), t320 = nbm * ((N + 319) / 320);
-    if (t128 < 256) return hip_status(launch_gemm_i8<128, 128, 2, 2, E, 8>(p, st(stream)));
+    if (t128 < 256) {
+        // Too few 256 x 128 tiles to fill the chip: 32 x 128 tiles while they
+        // give at most 256 workgroups, else 64 x 128, else 128 x 128
+        // (measured over 65-1024 tokens at 5120 x 17408, 5120 x 13824 and
+        // 15360 x 5120: 10-16% faster than 128 x 128 where they apply).
+        const int64_t nt = (N + 127) / 128;
+        if ((M + 31) / 32 * nt <= 256) return hip_status(launch_gemm_i8<32, 128, 1, 4, E, 8>(p, st(stream)));
+        if ((M + 63) / 64 * nt <= 256) return hip_status(launch_gemm_i8<64, 128, 2, 2, E, 8>(p, st(stream)));
+        return hip_status(launch_gemm_i8<128, 128, 2, 2, E, 8>(p, st(stream)));
+    }
     // Whole waves of 256 tiles; a wave of 256 x 320 tiles takes about 2.2
     // times as long as one of 256 x 128 (measured at 8192 x 5120 x 13824:
     // 447 us against 211).
