@@ -405,7 +405,7 @@ def f16_layer(dev, iters=20):
 # the W8A16 down projection (5120 x 17408).
 SWEEP_SHAPES = (("qkv", "w8a8", 15360, 5120), ("gate_up", "w8a8", 17408, 5120),
                 ("o_proj", "w8a8", 5120, 5120), ("down_proj", "w8a16", 5120, 17408))
-SWEEP_M = (1, 2, 4, 8, 16, 32, 64)
+SWEEP_M = (1, 2, 4, 8, 16, 32, 64, 96, 128, 256)
 
 
 def m_sweep(dev, reps=10):
