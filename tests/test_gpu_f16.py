@@ -132,7 +132,8 @@ def test_quant_scaled_mm_f16_token_counts(M):
     assert_ulp1(hbits(host(y)), y_ref, f"one-call f16 M={M}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (8, 256, 1024), (65, 272, 1152), (200, 384, 2048)])
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (8, 256, 1024), (65, 272, 1152), (200, 384, 2048),
+                                   (300, 5120, 256), (600, 5120, 256)])  # 64 x 128, 128 x 128 tiles
 def test_group128_act_f16(M, N, K):
     say("group128 act f16", M, N, K)
     x, w = synth.custom(M, K, N, seed=M * 11 + N, outlier_cols=3)

@@ -569,7 +569,9 @@ def test_quant_per_group128(M, K, pad):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (8, 256, 1024), (64, 144, 640),
-                                   (65, 272, 1152), (200, 384, 2048), (257, 128, 256)])
+                                   (65, 272, 1152), (200, 384, 2048), (257, 128, 256),
+                                   # tiles by workgroup count: 64 x 128, 128 x 128, 256 x 128
+                                   (300, 5120, 256), (600, 5120, 256), (1100, 5120, 128)])
 def test_scaled_mm_group128_act_shapes(M, N, K):
     say("group128 act", M, N, K)
     x, w = synth.custom(M, K, N, seed=M * 3 + N, outlier_cols=3)
@@ -604,7 +606,10 @@ def test_group128_act_full_size_sampled_rows():
 # ------------------------------------------------------------ group 128 --
 
 @pytest.mark.parametrize("M,N,K", [(16, 128, 256), (33, 144, 384), (130, 256, 1024),
-                                   (257, 128, 128)])
+                                   (257, 128, 128),
+                                   # tiles by workgroup count: 32, 64, 128 and 256 tokens
+                                   (100, 1040, 512), (300, 5120, 256), (600, 5120, 256),
+                                   (1100, 5120, 128)])
 def test_group128_shapes(M, N, K):
     say("group128", M, N, K)
     x, w = synth.custom(M, K, N, seed=M + N, outlier_cols=3)

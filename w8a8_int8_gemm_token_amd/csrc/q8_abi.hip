@@ -106,13 +106,20 @@ hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
 
 // Group-scaled epilogues: 256 x 128 tiles of 8 waves (64 x 64 each, two
 // waves per SIMD: the per-block fold keeps a second set of fp32
-// accumulators) once there are enough of them to fill the CUs.
+// accumulators) once smaller tiles would give more than one workgroup per
+// CU.
 template <int EPI>
 hipError_t run_gemm_grouped(const GemmArgs& p, hipStream_t s) {
     if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
-    const int64_t tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
-    if (tiles >= 256) return launch_gemm_i8<256, 128, 4, 2, EPI, 8>(p, s);
-    return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
+    // The first of 32, 64 and 128 tokens per tile that gives at most 256
+    // workgroups (one per CU), else 256 (measured over 65-1024 tokens at
+    // N = 5120 and 15360: within 3% of the fastest of the four, and 20-37%
+    // faster than the 128 x 128 tiles used throughout before).
+    const int64_t nt = (p.N + 127) / 128;
+    if ((p.M + 31) / 32 * nt <= 256) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
+    if ((p.M + 63) / 64 * nt <= 256) return launch_gemm_i8<64, 128, 2, 2, EPI, 8>(p, s);
+    if ((p.M + 127) / 128 * nt <= 256) return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
+    return launch_gemm_i8<256, 128, 4, 2, EPI, 8>(p, s);
 }
 
 template <int EPI>  // EPI_GROUP_ACT or EPI_GROUP_ACT_F16
