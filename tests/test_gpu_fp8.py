@@ -163,7 +163,9 @@ def test_fp8_quant_weight_block128(N, K):
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (8, 256, 1024), (64, 384, 640),
                                    (65, 256, 1152), (130, 512, 384), (200, 384, 2048),
-                                   (257, 128, 256)])
+                                   (257, 128, 256),
+                                   # tiles by workgroup count: 64 x 128, then 128 x 128
+                                   (300, 5120, 256), (600, 5120, 256)])
 def test_fp8_block_scaled_mm_shapes(M, N, K):
     say("fp8 block mm", M, N, K)
     x, w = synth.custom(M, K, N, seed=M * 5 + N, outlier_cols=3)
