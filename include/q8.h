@@ -225,12 +225,19 @@ q8_status q8_smooth_fold(const q8_bf16 *x, int64_t ldx, const float *w,
  * divisor is folded into gamma offline.  Per row m (K a multiple of 8):
  *   h = bf16_rne(x + residual), residual := h   (residual != NULL)
  *   h = x                                       (residual == NULL)
- *   ss = sum of h[k]^2 in fp32: 64 partial sums, partial l adding the
- *        8-element chunks l, l+64, ... in ascending k, then combined by a
- *        xor butterfly (p_l + p_{l^o}, o = 32, 16, ..., 1); ss = p_0
+ *   ss = sum of h[k]^2 (each square exact), added in fp32: its value is
+ *        the exact sum S of the squares up to the error of the summation,
+ *        |ss - S| <= n_d * 2^-24 * (1 + n_d * 2^-24) * S with
+ *        n_d = 8 * ceil(K / 512) + 6 (64 running partial sums of at most
+ *        8 * ceil(K/512) squares each, combined pairwise in 6 levels)
  *   rstd = 1 / sqrtf(ss / K + eps)              (correctly rounded)
  *   y[k] = bf16_rne((h[k] * rstd) * gamma[k])   (fp32 products)
  *   xq, scale_tok = q8_quant_per_token of the bf16 row y
+ * The plain definition takes ss as S rounded once to fp32; the codes and
+ * scale of a row are those of that definition at the kernel's own ss, which
+ * lies within the bound above (a different ss can move y across a bf16
+ * rounding boundary, so rows may differ from the definition's at the
+ * correctly rounded S while matching it at a nearby fp32 ss).
  * Cited: "...W8A8 INT8 (v3)", "Recipe" (smoothing folded into the preceding
  * norm); "Qwen3.8-27B -- FP8 block + AWQ", "Recipe" (the same fold);
  * "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", "Serving (vLLM, gfx908 fork)"

@@ -76,7 +76,9 @@ def _load():
             "q8o_smooth_scales": ([P, I, I, F, P], ctypes.c_int),
             "q8o_smooth_fold_x": ([P, P, I, I, P], None),
             "q8o_smooth_fold_w": ([P, P, I, I, P], None),
-            "q8o_rmsnorm_quant": ([P, P, P, F, I, I, P, P, P], ctypes.c_int),
+            "q8o_rmsnorm_quant": ([P, P, P, F, I, I, P, P, P, P], ctypes.c_int),
+            "q8o_rmsnorm_quant_at_ss": ([P, P, F, I, I, P, P, P, P], ctypes.c_int),
+            "q8o_sum_squares_bf16": ([P, I, I, P], None),
             "q8o_quant_per_group128": ([P, I, I, P, P], ctypes.c_int),
             "q8o_scaled_mm_group128_act": ([P, P, P, P, I, I, I, P], ctypes.c_int),
         }
@@ -234,10 +236,11 @@ def smooth_fold_w(w_f32, s) -> np.ndarray:
     return out
 
 
-def rmsnorm_quant(x_bf16, gamma_bf16, eps: float, res_bf16=None):
+def rmsnorm_quant(x_bf16, gamma_bf16, eps: float, res_bf16=None, return_ss: bool = False):
     """Residual add (optional) + RMSNorm + per-token INT8 quant.
     Returns (xq int8 [M,K], scale fp32 [M], y bf16 bits [M,K], res_out bf16
-    bits [M,K] or None)."""
+    bits [M,K] or None), and with return_ss the fp32 sums of squares [M]
+    (the exact sum of each row's squares, rounded once) as a fifth item."""
     x = _c(x_bf16, np.uint16)
     g = _c(gamma_bf16, np.uint16)
     M, K = x.shape
@@ -247,11 +250,40 @@ def rmsnorm_quant(x_bf16, gamma_bf16, eps: float, res_bf16=None):
     xq = np.empty((M, K), np.int8)
     s = np.empty((M,), np.float32)
     y = np.empty((M, K), np.uint16)
+    ss = np.empty((M,), np.float32)
     rc = _load().q8o_rmsnorm_quant(_p(x), None if res is None else _p(res), _p(g), float(eps),
-                                   M, K, _p(xq), _p(s), _p(y))
+                                   M, K, _p(xq), _p(s), _p(y), _p(ss))
     if rc != 0:
         raise ValueError(f"oracle rmsnorm_quant failed ({rc}): K must be a multiple of 8")
-    return xq, s, y, res
+    return (xq, s, y, res, ss) if return_ss else (xq, s, y, res)
+
+
+def sum_squares_bf16(h_bf16) -> np.ndarray:
+    """Per row of bf16 bits [M,K]: the exact sum of the squares, rounded once
+    to fp32 (round to nearest even)."""
+    h = _c(h_bf16, np.uint16)
+    M, K = h.shape
+    ss = np.empty((M,), np.float32)
+    _load().q8o_sum_squares_bf16(_p(h), M, K, _p(ss))
+    return ss
+
+
+def rmsnorm_quant_at_ss(h_bf16, gamma_bf16, eps: float, ss):
+    """The normalization + quantization of rows h (bf16 bits [M,K], after the
+    residual add) for given fp32 sums of squares ss [M]:
+    returns (xq int8 [M,K], scale fp32 [M], y bf16 bits [M,K])."""
+    h = _c(h_bf16, np.uint16)
+    g = _c(gamma_bf16, np.uint16)
+    ssa = _c(np.asarray(ss, dtype=np.float32), np.float32)
+    M, K = h.shape
+    if g.shape != (K,) or ssa.shape != (M,):
+        raise ValueError("gamma must have K entries and ss M entries")
+    xq = np.empty((M, K), np.int8)
+    s = np.empty((M,), np.float32)
+    y = np.empty((M, K), np.uint16)
+    if _load().q8o_rmsnorm_quant_at_ss(_p(h), _p(g), float(eps), M, K, _p(ssa), _p(xq), _p(s), _p(y)) != 0:
+        raise MemoryError("oracle rmsnorm_quant_at_ss: allocation failed")
+    return xq, s, y
 
 
 def quant_per_group128(x_bf16):

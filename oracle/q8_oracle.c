@@ -446,68 +446,150 @@ void q8o_smooth_fold_w(const float *w, const float *s, int64_t N, int64_t K,
  * of its output [P1 "Recipe": smoothing folded into the preceding norm; P3
  * "Recipe": the same fold; P5 "Serving (vLLM, gfx908 fork)": residual add,
  * RMSNorm and INT8 quantization fused into one output step].
- * Readings (the pages give no RMSNorm numerics):
+ * Readings (the pages give no RMSNorm numerics; this is the plain RMSNorm):
  *  - with a residual stream: h = bf16_rne(fl32(x) + fl32(res)), and res := h;
  *    without one: h = x;
- *  - ss = sum of h^2 in fp32 in this order: 64 partial sums, partial l
- *    adding h[k]^2 for the 8-element chunks c = l, l + 64, l + 128, ... in
- *    ascending k; then for o = 32, 16, 8, 4, 2, 1 every partial l becomes
- *    p[l] + p[l ^ o]; ss = p[0].  (Any order is a valid RMSNorm; fixing one
- *    makes the codes checkable bit for bit.)  K must be a multiple of 8;
+ *  - ss = the exact sum of h[k]^2 over the row, rounded once to fp32 (round
+ *    to nearest even).  Each square of a bf16 value is exact, so ss is the
+ *    sum of squares as a real number, with one rounding;
  *  - rstd = 1 / sqrtf(ss / K + eps) (correctly rounded division and root);
  *  - y[k] = bf16_rne(fl32(fl32(h[k] * rstd) * gamma[k]));
  *  - then the per-token quantization above, applied to the bf16 row y.
- * y_out (optional) receives y.  Returns -1 if K is not a multiple of 8. */
-int q8o_rmsnorm_quant(const uint16_t *x, uint16_t *res, const uint16_t *gamma,
-                      float eps, int64_t M, int64_t K, int8_t *xq, float *s,
-                      uint16_t *y_out)
+ * A summation in fp32 in any other order gives a value near ss; what a
+ * kernel's order may change is stated where the kernel is declared, and the
+ * tests accept the codes of every fp32 ss within that bound
+ * (q8o_rmsnorm_quant_at_ss computes them). */
+
+/* Exact sum of the squares of n bf16 values, rounded once to fp32.
+ * A nonzero bf16 magnitude is m * 2^e with an integer m < 2^8 (m = 128 + the
+ * 7 stored bits for a normal value with biased exponent E, e = E - 134; the
+ * stored bits alone with e = -133 for a subnormal), so its square is the
+ * integer m^2 < 2^16 times 2^(2e), 2e >= -266.  The squares are added as
+ * integers into a fixed-point register whose bit i stands for 2^(i - 266):
+ * 2e + 266 >= 0, and the largest square, below 2^256, plus 2^13 more of them
+ * stays below 2^270, so 9 limbs of 64 bits (576 bits) hold every sum exactly.
+ * The register is then rounded to the fp32 grid: 24 significant bits, or the
+ * subnormal quantum 2^-149, ties to even. */
+#define SSQ_LIMBS 9
+#define SSQ_BIAS 266
+
+static int ssq_bit(const uint64_t *acc, int i)
 {
-    if (K % 8 != 0) return -1;
+    return (int)((acc[i >> 6] >> (i & 63)) & 1u);
+}
+
+static float sum_squares_bf16_rn(const uint16_t *h, int64_t n)
+{
+    uint64_t acc[SSQ_LIMBS];
+    memset(acc, 0, sizeof acc);
+    for (int64_t k = 0; k < n; ++k) {
+        const uint32_t b = h[k] & 0x7FFFu;
+        if (b == 0) continue;
+        const uint32_t E = b >> 7, f = b & 0x7Fu;
+        const uint64_t m = E ? 128u + f : f;
+        const int e = E ? (int)E - 134 : -133;
+        const uint64_t sq = m * m;
+        const int pos = 2 * e + SSQ_BIAS;
+        int limb = pos >> 6;
+        const int sh = pos & 63;
+        uint64_t lo = sq << sh, hi = sh ? sq >> (64 - sh) : 0;
+        /* add (hi:lo) at limb, then carry upwards */
+        uint64_t old = acc[limb];
+        acc[limb] = old + lo;
+        uint64_t carry = acc[limb] < old;
+        for (++limb; limb < SSQ_LIMBS && (hi | carry); ++limb) {
+            old = acc[limb];
+            const uint64_t add = hi + carry;  /* hi < 2^16: no overflow */
+            acc[limb] = old + add;
+            carry = acc[limb] < old;
+            hi = 0;
+        }
+    }
+    int top = -1;
+    for (int i = SSQ_LIMBS * 64 - 1; i >= 0; --i)
+        if (ssq_bit(acc, i)) { top = i; break; }
+    if (top < 0) return 0.0f;
+    /* value = acc * 2^-266; its leading bit has exponent top - 266 */
+    int qe = top - SSQ_BIAS - 23;          /* exponent of the last kept bit */
+    if (qe < -149) qe = -149;
+    const int qp = qe + SSQ_BIAS;          /* its position in the register */
+    uint64_t keep = 0;
+    for (int i = top; i >= qp; --i) keep = (keep << 1) | (uint64_t)ssq_bit(acc, i);
+    int half = 0, sticky = 0;
+    if (qp >= 1) {
+        half = ssq_bit(acc, qp - 1);
+        for (int i = qp - 2; i >= 0 && !sticky; --i) sticky = ssq_bit(acc, i);
+    }
+    if (half && (sticky || (keep & 1u))) keep += 1;
+    const double v = ldexp((double)keep, qe);  /* exact: keep <= 2^24 */
+    return v >= 0x1p128 ? INFINITY : (float)v;
+}
+
+/* ss of each of M rows of K bf16 values (the exact sum, rounded once). */
+void q8o_sum_squares_bf16(const uint16_t *h, int64_t M, int64_t K, float *ss)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) ss[m] = sum_squares_bf16_rn(h + m * K, K);
+}
+
+/* The normalization and the quantization of M rows h [M][K] (bf16, the row
+ * after the residual add) for given sums of squares ss [M]:
+ *   rstd = 1 / sqrtf(ss / K + eps); y = bf16_rne((h * rstd) * gamma);
+ *   xq, s = the per-token quantization of y.  y_out (optional) receives y. */
+int q8o_rmsnorm_quant_at_ss(const uint16_t *h, const uint16_t *gamma,
+                            float eps, int64_t M, int64_t K, const float *ss,
+                            int8_t *xq, float *s, uint16_t *y_out)
+{
     int bad = 0;
 #pragma omp parallel for schedule(static) reduction(| : bad)
     for (int64_t m = 0; m < M; ++m) {
-        uint16_t *h = (uint16_t *)malloc((size_t)K * sizeof(uint16_t));
-        uint16_t *y = (uint16_t *)malloc((size_t)K * sizeof(uint16_t));
         float *yf = (float *)malloc((size_t)K * sizeof(float));
-        if (!h || !y || !yf) { bad = 1; free(h); free(y); free(yf); continue; }
-        for (int64_t k = 0; k < K; ++k) {
-            if (res) {
-                const float sum = bf16_bits_to_f32(x[m * K + k]) + bf16_bits_to_f32(res[m * K + k]);
-                h[k] = q8o_f32_to_bf16(sum);
-                res[m * K + k] = h[k];
-            } else {
-                h[k] = x[m * K + k];
-            }
-        }
-        float p[64];
-        for (int l = 0; l < 64; ++l) {
-            p[l] = 0.0f;
-            for (int64_t c = l; c < K / 8; c += 64)
-                for (int e = 0; e < 8; ++e) {
-                    const float v = bf16_bits_to_f32(h[c * 8 + e]);
-                    const float sq = v * v;
-                    p[l] = p[l] + sq;
-                }
-        }
-        for (int o = 32; o >= 1; o >>= 1) {
-            float q[64];
-            for (int l = 0; l < 64; ++l) q[l] = p[l] + p[l ^ o];
-            memcpy(p, q, sizeof(p));
-        }
-        const float var = p[0] / (float)K;
+        if (!yf) { bad = 1; continue; }
+        const float var = ss[m] / (float)K;
         const float rstd = 1.0f / sqrtf(var + eps);
         for (int64_t k = 0; k < K; ++k) {
-            const float t = bf16_bits_to_f32(h[k]) * rstd;
-            y[k] = q8o_f32_to_bf16(t * bf16_bits_to_f32(gamma[k]));
-            yf[k] = bf16_bits_to_f32(y[k]);
+            const float t = bf16_bits_to_f32(h[m * K + k]) * rstd;
+            const uint16_t yb = q8o_f32_to_bf16(t * bf16_bits_to_f32(gamma[k]));
+            yf[k] = bf16_bits_to_f32(yb);
+            if (y_out) y_out[m * K + k] = yb;
         }
         const float sc = absmax_scale(yf, K);
         s[m] = sc;
         for (int64_t k = 0; k < K; ++k) xq[m * K + k] = code_of(yf[k], sc);
-        if (y_out) memcpy(y_out + m * K, y, (size_t)K * sizeof(uint16_t));
-        free(h); free(y); free(yf);
+        free(yf);
     }
     return bad ? -2 : 0;
+}
+
+/* The whole step: residual add (res may be NULL; it is overwritten with h),
+ * exact sum of squares, normalization and quantization.  ss_out and y_out
+ * are optional.  Returns -1 if K is not a multiple of 8 (the vector layout
+ * of the step's entry point). */
+int q8o_rmsnorm_quant(const uint16_t *x, uint16_t *res, const uint16_t *gamma,
+                      float eps, int64_t M, int64_t K, int8_t *xq, float *s,
+                      uint16_t *y_out, float *ss_out)
+{
+    if (K % 8 != 0) return -1;
+    uint16_t *h = (uint16_t *)malloc((size_t)(M * K > 0 ? M * K : 1) * sizeof(uint16_t));
+    float *ss = (float *)malloc((size_t)(M > 0 ? M : 1) * sizeof(float));
+    if (!h || !ss) { free(h); free(ss); return -2; }
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            if (res) {
+                const float sum = bf16_bits_to_f32(x[m * K + k]) + bf16_bits_to_f32(res[m * K + k]);
+                h[m * K + k] = q8o_f32_to_bf16(sum);
+                res[m * K + k] = h[m * K + k];
+            } else {
+                h[m * K + k] = x[m * K + k];
+            }
+        }
+    q8o_sum_squares_bf16(h, M, K, ss);
+    const int rc = q8o_rmsnorm_quant_at_ss(h, gamma, eps, M, K, ss, xq, s, y_out);
+    if (ss_out) memcpy(ss_out, ss, (size_t)M * sizeof(float));
+    free(h);
+    free(ss);
+    return rc;
 }
 
 /* --------------------- per-token-per-group activations, group-128 weights --

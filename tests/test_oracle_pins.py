@@ -403,6 +403,62 @@ def test_smooth_fold_general_within_rounding():
     assert np.all(np.abs(ratio / s.astype(np.float64)[None, :] - 1) <= 2.0 ** -24)
 
 
+def _bf16_of_f32(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 (torch's RNE cast), returned as fp32 values."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def test_smooth_fold_x_divides_rather_than_multiplying_by_reciprocal():
+    """X' = bf16(fl32(x / s)): one correctly rounded division, not x times
+    fl32(1/s).  Pairs (x, s) with a general fp32 s where the two routes give
+    different bf16 values are found by a float32 search (numpy's float32 '/'
+    and '*' are IEEE), confirmed with exact rationals, and the oracle must
+    give the quotient's rounding."""
+    g = np.random.default_rng(5)
+    n = 4_000_000
+    s = (1 + 15 * g.random(n)).astype(np.float32)
+    x = _bf16_of_f32((g.random(n) * 2 - 1) * 8)
+    q_div = _bf16_of_f32(x / s)
+    q_rcp = _bf16_of_f32(x * (np.float32(1) / s))
+    hit = np.nonzero(q_div != q_rcp)[0]
+    assert len(hit) >= 5
+    xs, ss = x[hit], s[hit]
+    for xv, sv in zip(xs, ss):
+        fx, fs = Fraction(float(xv)), Fraction(float(sv))
+        stated = bf16(fp32(fx / fs))
+        other = bf16(fp32(fx * fp32(1 / fs)))
+        assert stated != other
+    # one column per pair: the oracle folds x_j by its s_j
+    xb = _bits([xs.tolist()])
+    out = oracle.smooth_fold_x(xb, ss.astype(np.float32))
+    for j, (xv, sv) in enumerate(zip(xs, ss)):
+        assert bf16_bits_value(int(out[0, j])) == bf16(fp32(Fraction(float(xv)) / Fraction(float(sv))))
+
+
+def test_smooth_fold_routes_agree_on_the_folds_own_scales():
+    """Within the fold step itself the scale is s = min(16, sqrtf(a)) for a
+    bf16 column maximum a, and every |x| <= a.  On that domain the division
+    and the reciprocal product give the same bf16 value for every pair:
+    exhaustively over every such s with every bf16 significand of x (the
+    rounding of a normal quotient depends on the significands only), and
+    over every bf16 x small enough for the quotient to be subnormal in fp32.
+    So the fold's bf16 outputs cannot tell the two routes apart, and the
+    explicit-scale pin above is what fixes the oracle's division."""
+    allb = np.arange(1, 0x7F80, dtype=np.uint32)
+    vals = (allb << 16).view(np.float32)
+    a = vals[vals <= 256]
+    s = np.unique(np.minimum(np.float32(16), np.sqrt(a).astype(np.float32)))
+    r = np.float32(1) / s
+    xm = (1 + np.arange(128) / 128).astype(np.float32)
+    for xe in (-1, 0, 1):
+        X = (xm * np.float32(2.0 ** xe))[:, None]
+        assert np.array_equal(_bf16_of_f32(X / s[None, :]), _bf16_of_f32(X * r[None, :]))
+    tiny = vals[vals <= np.float32(2.0 ** -119)]
+    for i in range(0, len(tiny), 128):
+        X = tiny[i:i + 128][:, None]
+        assert np.array_equal(_bf16_of_f32(X / s[None, :]), _bf16_of_f32(X * r[None, :]))
+
+
 # --------------------------------------------- end to end vs unquantized -
 
 @pytest.mark.parametrize("name", ["tiny", "decode"])
@@ -586,6 +642,90 @@ def test_rmsnorm_product_order_targeted():
         _, _, y, _ = oracle.rmsnorm_quant(_bits([row]), _bits(gam), e32)
         assert bf16_bits_value(int(y[0, 100])) == stated
         assert bf16_bits_value(int(y[0, 0])) == bf16(fp32(fp32(rstd) * Fraction(3, 4)))
+
+
+def _exact_ss_fp32(row_bits) -> Fraction:
+    """The exact sum of the squares of a row of bf16 bits, rounded once to
+    fp32, in rational arithmetic."""
+    tot = Fraction(0)
+    for u in row_bits:
+        v = bf16_bits_value(int(u))
+        tot += v * v
+    return fp32(tot)
+
+
+def test_rmsnorm_sum_of_squares_is_exact_then_rounded_once():
+    """ss is the exact sum of the row's squares rounded once to fp32: checked
+    against rational arithmetic on random rows (moderate, wide-range and
+    subnormal values, K up to 8192), and on two constructed rows that an
+    fp32 running sum and an fp64 running sum each get wrong."""
+    g = np.random.default_rng(21)
+    rows = [g.standard_normal(5120) * 3,
+            g.standard_normal(8192) * 2.0 ** g.integers(-60, 40, 8192),
+            g.standard_normal(1024) * 2.0 ** -128,  # subnormal bf16 values
+            np.concatenate([[2.0 ** 63], g.standard_normal(511)])]
+    for r in rows:
+        b = _bits([r.astype(np.float32).tolist()])
+        ss = oracle.sum_squares_bf16(b)
+        assert Fraction(float(ss[0])) == _exact_ss_fp32(b[0])
+    # 2^20 + 17 * 2^-8: the small squares are each below half an fp32 ulp of
+    # 2^20 (2^-4), so a running fp32 sum keeps 2^20, but together they pass
+    # the midpoint and the exact sum rounds up to 2^20 + 2^-3
+    row = [1024.0] + [2.0 ** -4] * 17 + [0.0] * 14
+    ss = oracle.sum_squares_bf16(_bits([row]))[0]
+    assert ss == np.float32(2.0 ** 20 + 2.0 ** -3)
+    run = np.float32(0)
+    for v in row:
+        run = np.float32(run + np.float32(v) * np.float32(v))
+    assert run == np.float32(2.0 ** 20)
+    # 2^60 + 2^36 + 2^-40: the first two make an exact fp32 tie, the third
+    # breaks it upwards; an fp64 running sum loses 2^-40 and rounds the tie
+    # to even (2^60), the exact sum rounds to 2^60 + 2^37
+    row = [2.0 ** 30, 2.0 ** 18, 2.0 ** -20] + [0.0] * 5
+    ss = oracle.sum_squares_bf16(_bits([row]))[0]
+    assert ss == np.float32(2.0 ** 60 + 2.0 ** 37)
+    d64 = 0.0
+    for v in row:
+        d64 += v * v
+    assert np.float32(d64) == np.float32(2.0 ** 60)
+    # the full step uses the same ss
+    ss_step = oracle.rmsnorm_quant(_bits([row]), _bits([[1.0] * 8])[0], 1e-6, return_ss=True)[4]
+    assert ss_step[0] == np.float32(2.0 ** 60 + 2.0 ** 37)
+
+
+def test_rmsnorm_at_ss_reproduces_the_step():
+    """The normalization at a given ss (used by the validity check) equals
+    the full step when given the step's own ss."""
+    x, gam = _norm_inputs(12, 2048, 31, scale=2.0)
+    r, _ = _norm_inputs(12, 2048, 32)
+    xq, s, y, h, ss = oracle.rmsnorm_quant(x, gam, 1e-5, res_bf16=r, return_ss=True)
+    xq2, s2, y2 = oracle.rmsnorm_quant_at_ss(h, gam, 1e-5, ss)
+    for a, b in ((xq, xq2), (s, s2), (y, y2)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_norm_check_accepts_bounded_sums_and_rejects_a_dropped_term():
+    """The validity check used on the GPU accepts the outputs at fp32 sums of
+    squares a few ulps from the exact one (any summation order within the
+    stated bound), and rejects outputs computed from a sum that misses one
+    square (an error far outside the bound)."""
+    from tests.norm_check import check_rows
+    M, K = 64, 5120
+    h, gam = _norm_inputs(M, K, 41, scale=1.5)
+    ss = oracle.sum_squares_bf16(h)
+    off = np.array([0, 1, -1, 3, -4, 7] * (M // 6 + 1))[:M]
+    cand = (ss.view(np.int32) + off.astype(np.int32)).view(np.float32)
+    xq, s, _ = oracle.rmsnorm_quant_at_ss(h, gam, 1e-6, cand)
+    n_exact, n_nb, _ = check_rows(h, gam, 1e-6, xq, s)
+    assert n_exact + n_nb == M and n_nb > 0
+    drop = h.copy()
+    drop[:, 5] = 0  # one square missing from every row's sum
+    ss_d = oracle.sum_squares_bf16(drop)
+    xq_d, s_d, _ = oracle.rmsnorm_quant_at_ss(h, gam, 1e-6, ss_d)
+    changed = np.any(xq_d != oracle.rmsnorm_quant_at_ss(h, gam, 1e-6, ss)[0], axis=1)
+    assert changed.sum() > M // 2
+    with pytest.raises(AssertionError):
+        check_rows(h, gam, 1e-6, xq_d, s_d)
 
 
 # -------------------- per-token-per-group activations, group-128 weights --

@@ -13,9 +13,11 @@
 //
 // Arithmetic, per row (K a multiple of 8):
 //   h = bf16_rne(x + res) and res := h   (or h = x without a residual)
-//   ss: 64 partial sums, lane l adding h[k]^2 (fp32 products and sums) over
-//       its 8-element chunks l, l + 64, ... in ascending k; then a xor
-//       butterfly over the lanes (ss_l + ss_{l^o}, o = 32 .. 1)
+//   ss: the sum of the squares h[k]^2 (each exact in fp32), added in fp32:
+//       64 running partial sums, lane l over its 8-element chunks l,
+//       l + 64, ..., then a xor butterfly over the lanes.  The summation
+//       tree has depth n_d = 8 * ceil(K / 512) + 6, so ss is within
+//       n_d * 2^-24 (1 + n_d * 2^-24) of the exact sum, relative
 //   rstd = 1 / sqrtf(ss / K + eps)        (correctly rounded)
 //   y = bf16_rne((h * rstd) * gamma)
 //   codes and scale of y exactly as the per-token quantizer.
