@@ -1,25 +1,35 @@
 """Benchmark of the W8A8 INT8 linear layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--secondary decode,group128,group128_act,w8a16,rmsnorm_quant,
-                                 m_sweep | none]
+                    [--secondary decode,tiny,group128,group128_act,w8a16,
+                                 rmsnorm_quant,fp8_block,f16,m_sweep | none]
                     [--calibrate-copy]
 
 A step is one pass of the W8A8 hot path over the prefill workload
 (X bf16 [8192, 5120] after the smoothing fold, W int8 [15360, 5120] with
 per-channel scales): per-token quantization of X (row absmax -> scale ->
 codes) followed by the INT8 x INT8 -> INT32 GEMM with the per-token x
-per-channel epilogue to bf16, both through the library's one-call entry
-point.  Inputs (synthetic, seeded) are resident in HBM before timing; the
+per-channel epilogue to bf16 -- the two kernels the one-call entry point
+q8_quant_scaled_mm launches at this size, called here as q8_quant_per_token
+then q8_scaled_mm so that HIP events can mark the GEMM inside every timed
+step.  Inputs (synthetic, seeded) are resident in HBM before timing; the
 weight quantization and the fold are offline preparation, outside the timed
-region.  Prints one JSON line:
-  value    = 2*M*N*K*steps / elapsed  (TOPS, whole quant+GEMM step)
-  roofline = the GEMM kernel alone, timed with events on the launch stream,
-             against the INT8 dense MFMA peak (5.0 POP/s)
-  cpu_baseline = the CPU oracle on a bounded sample of the same workload
-  secondary    = decode (M=1, M=8) GB/s of the one-call layer with the weight
-             copies rotated past the 256 MB last-level cache, and the other
-             workloads
+region.  Before the W warm-up steps the GEMM runs alone for about 60 ms
+(the "gemm_alone" figure), which also brings the board from idle to the
+clock it holds under this load.  Prints one JSON line:
+  value    = 2*M*N*K*steps / elapsed  (TOPS, whole quant+GEMM step, host
+             clock around the K timed steps)
+  roofline = the GEMM kernel: its mean duration over the K timed steps from
+             the events around it (on the stream it is launched on), against
+             the INT8 dense MFMA peak (5.0 POP/s), with the ceiling an MFMA-only
+             loop on changing operands reaches on the same board
+  cpu_baseline = the CPU oracle on a bounded sample of the same workload,
+             and on each of the other four workloads (per_config)
+  secondary    = decode (M=1, M=8) per call in a HIP graph with the weight
+             copies rotated past the 256 MB last-level cache, against 8 TB/s
+             and against a plain read of the same bytes in the same protocol;
+             the tiny workload's latency; the measured ceilings; and the
+             other workloads (p10/p50/p90 of per-call event times)
 --calibrate-copy adds a plain device-to-device copy of 512 MiB (torch's copy
 kernel), so that a hardware-counter run of this script also measures the
 bytes the counters report for a transfer of known size.
@@ -114,6 +124,144 @@ def events_time(fn, iters: int, settle_ms: float = 60.0) -> float:
     return e0.elapsed_time(e1) / iters
 
 
+def call_stats(fn, iters: int, settle_ms: float = 60.0) -> dict:
+    """Per-call times of fn() (ms), each call between its own pair of HIP
+    events on the current stream, after about settle_ms of untimed calls:
+    mean, p10, p50, p90."""
+    t1 = _events_once(fn, 1)
+    for _ in range(int(min(5000, max(1, settle_ms / max(t1, 1e-3))))):
+        fn()
+    s = torch.cuda.current_stream()
+    ev = []
+    for _ in range(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        fn()
+        e1.record(s)
+        ev.append((e0, e1))
+    s.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"mean": float(t.mean()), "p10": float(np.percentile(t, 10)),
+            "p50": float(np.percentile(t, 50)), "p90": float(np.percentile(t, 90))}
+
+
+def _us(st: dict) -> dict:
+    return {k: round(v * 1e3, 3) for k, v in st.items()}
+
+
+_ceil = None
+
+
+def ceil_lib():
+    """The benchmark's measurement kernels (libq8_ceilings.so)."""
+    global _ceil
+    if _ceil is None:
+        import ctypes
+        path = os.path.join(ROOT, "w8a8_int8_gemm_token_amd", "libq8_ceilings.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} not built (python -m w8a8_int8_gemm_token_amd.build)")
+        lib = ctypes.CDLL(path)
+        P, I, C = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.q8c_mfma_i8_loop.argtypes = [C, C, C, P, P]
+        lib.q8c_mfma_i8_loop.restype = C
+        lib.q8c_stream_read.argtypes = [P, I, C, P, P]
+        lib.q8c_stream_read.restype = C
+        _ceil = lib
+    return _ceil
+
+
+def _stream_ptr():
+    import ctypes
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def mfma_ceiling(dev, random: bool, iters: int = 16384, reps: int = 10) -> dict:
+    """int8 MFMA rate of a loop of v_mfma_i32_32x32x32_i8 from registers
+    (no memory traffic): 768 workgroups of 4 waves (3 waves per SIMD, all
+    resident), each wave 4 * iters MFMAs; operands changing every MFMA
+    (random) or all zero."""
+    import ctypes
+    lib = ceil_lib()
+    blocks = 768
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+
+    def f():
+        rc = lib.q8c_mfma_i8_loop(blocks, iters, int(random), ctypes.c_void_p(out.data_ptr()), _stream_ptr())
+        if rc != 0:
+            raise RuntimeError(f"q8c_mfma_i8_loop failed ({rc})")
+    ms = events_time(f, reps)
+    ops = blocks * 4 * 4 * iters * 65536.0
+    return {"TOPS": ops / (ms * 1e-3) / 1e12, "ms": ms, "operands": "random" if random else "zero"}
+
+
+def read_ceiling_graph(dev, nbytes: int, ncopy: int = 24, reps: int = 20) -> dict:
+    """A plain read of nbytes per call, cycling through ncopy buffers (past
+    the 256 MB last-level cache), captured in a HIP graph and timed per call
+    with events: the decode line's protocol with the layer replaced by a
+    bare read.  The fastest of a few grid sizes is kept."""
+    import ctypes
+    lib = ceil_lib()
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(i % 251) for i in range(ncopy)]
+    best = None
+    for blocks in (512, 1024, 2048, 4096):
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+
+        def cycle():
+            for b in bufs:
+                rc = lib.q8c_stream_read(ctypes.c_void_p(b.data_ptr()), nbytes, blocks,
+                                         ctypes.c_void_p(out.data_ptr()), _stream_ptr())
+                if rc != 0:
+                    raise RuntimeError(f"q8c_stream_read failed ({rc})")
+        cycle()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cycle()
+        g.replay()
+        torch.cuda.synchronize()
+        ms = events_time(g.replay, reps) / ncopy
+        if best is None or ms < best[0]:
+            best = (ms, blocks)
+        del g
+    ms, blocks = best
+    return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes, "blocks": blocks,
+            "timing": f"HIP graph of {ncopy} calls on distinct buffers, events"}
+
+
+def read_ceiling_big(dev, nbytes: int = 512 << 20, reps: int = 10) -> dict:
+    """A plain read of one 512 MiB buffer (twice the last-level cache),
+    events per call."""
+    import ctypes
+    lib = ceil_lib()
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
+    blocks = 4096
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+
+    def f():
+        rc = lib.q8c_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, blocks,
+                                 ctypes.c_void_p(out.data_ptr()), _stream_ptr())
+        if rc != 0:
+            raise RuntimeError(f"q8c_stream_read failed ({rc})")
+    ms = events_time(f, reps)
+    return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes}
+
+
+_CEILINGS = {}
+
+
+def ceilings(dev) -> dict:
+    """The board's measured ceilings: int8 MFMA on changing and on zero
+    operands, and plain reads (the decode protocol's 26,398,752 bytes per
+    call over 24 buffers, and one 512 MiB buffer)."""
+    if not _CEILINGS:
+        _CEILINGS["mfma_int8_random"] = mfma_ceiling(dev, True)
+        _CEILINGS["mfma_int8_zero"] = mfma_ceiling(dev, False)
+        _CEILINGS["read_decode_bytes_graph"] = read_ceiling_graph(dev, 26_398_752)
+        _CEILINGS["read_512MiB"] = read_ceiling_big(dev)
+        torch.cuda.empty_cache()
+    return dict(_CEILINGS)
+
+
 def prefill_setup(dev):
     wl = synth.WORKLOADS["prefill"]
     x = synth.activations(wl, 0).to(dev)
@@ -126,10 +274,41 @@ def prefill_setup(dev):
     return wl, xo, wq, sc
 
 
-def cpu_baseline(target_s: float = 15.0):
-    """The oracle (as it stands) on a bounded sample of the prefill workload:
-    quantize a block of token rows and run the scaled INT8 GEMM for them
-    against all 15360 channels.  Scaled to TOPS like the GPU figure."""
+def cpu_model() -> str | None:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _timed(fn) -> float:
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
+
+
+def _rows_for(run, total_rows: int, target_s: float) -> tuple[int, float]:
+    """Grow a row block until its time is steady, then size it to about
+    target_s of oracle work; returns (rows, seconds of the sized run)."""
+    rows = 16
+    t = run(rows)
+    while t < 0.5 and rows < total_rows:
+        rows = min(total_rows, rows * 4)
+        t = run(rows)
+    rows = int(max(16, min(total_rows, rows * target_s / t)))
+    return rows, run(rows)
+
+
+def cpu_baseline(target_s: float = 10.0):
+    """The oracle (as it stands) on the host cores: on a bounded sample of
+    the prefill workload (a block of token rows quantized and multiplied
+    against all 15360 channels, sized to about target_s), and on the other
+    four workloads (tiny and decode whole, median of 5; W8A16 and group-128
+    on a row block of about 5 s).  Scaled to the unit of the GPU figures."""
     import oracle
     wl = synth.WORKLOADS["prefill"]
     x = synth.bf16_bits(synth.activations(wl, 0))
@@ -137,34 +316,69 @@ def cpu_baseline(target_s: float = 15.0):
     s = oracle.smooth_scales(x)
     xo = oracle.smooth_fold_x(x, s)
     wq, sc = oracle.quant_weight(oracle.smooth_fold_w(w, s))
-    del w
+    del w, x
 
     def run(rows):
-        t0 = time.perf_counter()
-        xq, st = oracle.quant_per_token(np.ascontiguousarray(xo[:rows]))
-        oracle.scaled_mm(xq, wq, st, sc)
-        return time.perf_counter() - t0
+        def f():
+            xq, st = oracle.quant_per_token(np.ascontiguousarray(xo[:rows]))
+            oracle.scaled_mm(xq, wq, st, sc)
+        return _timed(f)
 
-    rows = 16
-    t = run(rows)
-    while t < 1.0 and rows < wl.M:  # grow until the per-row cost is steady
-        rows = min(wl.M, rows * 4)
-        t = run(rows)
-    rows = int(max(16, min(wl.M, rows * target_s / t)))
-    t = run(rows)
+    rows, t = _rows_for(run, wl.M, target_s)
     ops = 2.0 * rows * wl.N * wl.K
     threads = oracle.threads()
-    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {wl.M} token rows x all {wl.N} channels, K={wl.K} "
-                      f"(quant + INT32 GEMM + epilogue), {t:.1f} s"}
+    rec = {"value": ops / t / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+           "sample": f"{rows} of {wl.M} token rows x all {wl.N} channels, K={wl.K} "
+                     f"(quant + INT32 GEMM + epilogue), {t:.1f} s",
+           "cpu_model": cpu_model()}
+    del xo, wq, sc
+    per = {}
+    for name in ("tiny", "decode"):
+        wk = synth.WORKLOADS[name]
+        xb = synth.bf16_bits(synth.activations(wk, 0))
+        wq_, sc_ = oracle.quant_weight(synth.weights(wk, 0).numpy())
+
+        def f():
+            xq_, st_ = oracle.quant_per_token(xb)
+            oracle.scaled_mm(xq_, wq_, st_, sc_)
+        t = float(np.median([_timed(f) for _ in range(5)]))
+        nbytes = wk.N * wk.K + 4 * wk.N + 3 * wk.M * wk.K + 4 * wk.M + 2 * wk.M * wk.N
+        per[name] = {"us": t * 1e6, "TOPS": 2.0 * wk.M * wk.N * wk.K / t / 1e12,
+                     "GB/s": nbytes / t / 1e9, "sample": f"whole workload {wk.M}x{wk.N}x{wk.K}, median of 5"}
+    wk = synth.WORKLOADS["w8a16"]
+    xb = synth.bf16_bits(synth.activations(wk, 0))
+    wq_, sc_ = oracle.quant_weight(synth.weights(wk, 0).numpy())
+    rows, t = _rows_for(lambda r: _timed(lambda: oracle.w8a16_ref(np.ascontiguousarray(xb[:r]), wq_, sc_)),
+                        wk.M, 5.0)
+    per["w8a16"] = {"TFLOPS": 2.0 * rows * wk.N * wk.K / t / 1e12,
+                    "sample": f"{rows} of {wk.M} rows x all {wk.N} channels, K={wk.K} (fp64 reference), {t:.1f} s"}
+    del xb, wq_
+    wk = synth.WORKLOADS["group128"]
+    xb = synth.bf16_bits(synth.activations(wk, 0))
+    wq_, sg_ = oracle.quant_weight(synth.weights(wk, 0).numpy(), group=128)
+
+    def run_g(r):
+        def f():
+            xq_, st_ = oracle.quant_per_token(np.ascontiguousarray(xb[:r]))
+            oracle.scaled_mm_group128(xq_, wq_, st_, sg_)
+        return _timed(f)
+    rows, t = _rows_for(run_g, wk.M, 5.0)
+    per["group128"] = {"TOPS": 2.0 * rows * wk.N * wk.K / t / 1e12,
+                       "sample": f"{rows} of {wk.M} rows x all {wk.N} channels, K={wk.K} "
+                                 f"(quant + group-128 GEMM), {t:.1f} s"}
+    rec["per_config"] = per
+    return rec
 
 
 def decode_gbs(dev, reps=20):
-    """Fused quant+GEMM at M in {1, 8}: algorithmic bytes / kernel time.
+    """Fused quant+GEMM at M in {1, 8}: algorithmic bytes / kernel time,
+    against 8 TB/s and against a plain read of the same bytes per call in
+    the same protocol (the measured ceiling).
     The calls cycle through enough weight copies that one cycle exceeds 2x
     the 256 MB last-level cache, and are captured in a HIP graph so that the
     events time the kernels back to back rather than the host's launch
     rate."""
+    ceil = ceilings(dev)["read_decode_bytes_graph"]
     wl = synth.WORKLOADS["decode"]
     w = synth.weights(wl, 0).to(dev)
     wq, sc = q8.q8_quant_weight(w)
@@ -190,12 +404,51 @@ def decode_gbs(dev, reps=20):
         for _ in range(3):
             g.replay()
         torch.cuda.synchronize()
-        ms = events_time(g.replay, reps) / ncopy
+        st = call_stats(g.replay, reps)
+        ms = st["mean"] / ncopy
         nbytes = wl.N * wl.K + 4 * wl.N + 2 * M * wl.K + 2 * M * wl.N + 4 * M + M * wl.K
-        out[f"M{M}"] = {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
-                        "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[f"M{M}"] = {"us": ms * 1e3, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
+                        "frac_read_ceiling": gbs / ceil["GB/s"],
+                        "per_call_us_p10_p50_p90": [round(st[k] / ncopy * 1e3, 3) for k in ("p10", "p50", "p90")],
                         "bytes": nbytes, "timing": "HIP graph of 24 calls, events"}
+        del g
+    out["read_ceiling"] = {"us": ceil["us"], "GB/s": ceil["GB/s"], "bytes": ceil["bytes"],
+                           "timing": ceil["timing"]}
     return out
+
+
+def tiny_latency(dev, ncopy: int = 64, reps: int = 20):
+    """The tiny workload (X [16,256], W [128,256]) through the one-call
+    layer: per call inside a HIP graph of 64 calls (the kernels back to back),
+    and per call launched from the host (events around each call)."""
+    wl = synth.WORKLOADS["tiny"]
+    x = synth.activations(wl, 0).to(dev)
+    w = synth.weights(wl, 0).to(dev)
+    wq, sc = q8.q8_quant_weight(w)
+    y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
+    xq = torch.empty((wl.M, wl.K), dtype=torch.int8, device=dev)
+    st = torch.empty((wl.M,), dtype=torch.float32, device=dev)
+
+    def call():
+        q8.q8_quant_scaled_mm(x, wq, sc, out=y, xq_out=xq, scale_tok_out=st)
+
+    def cycle():
+        for _ in range(ncopy):
+            call()
+    cycle()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cycle()
+    g.replay()
+    torch.cuda.synchronize()
+    gs = call_stats(g.replay, reps)
+    es = call_stats(call, 200)
+    return {"graph_us_per_call": gs["mean"] / ncopy * 1e3,
+            "graph_us_per_call_p10_p50_p90": [round(gs[k] / ncopy * 1e3, 3) for k in ("p10", "p50", "p90")],
+            "eager_us": _us(es), "shape": [wl.M, wl.N, wl.K],
+            "timing": "HIP graph of 64 calls (per call), and per eager call between events"}
 
 
 def group_tops(dev, iters=20):
@@ -208,9 +461,10 @@ def group_tops(dev, iters=20):
     f = lambda: q8.q8_scaled_mm_group128(xq, wq, st, sg, out=y)  # noqa: E731
     for _ in range(3):
         f()
-    ms = events_time(f, iters)
+    st = call_stats(f, iters)
+    ms = st["mean"]
     t = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
-    return {"us": ms * 1e3, "TOPS": t, "frac_int8_peak": t / PEAK_INT8_TOPS}
+    return {"us": ms * 1e3, "TOPS": t, "frac_int8_peak": t / PEAK_INT8_TOPS, "stats_us": _us(st)}
 
 
 def w8a16_tflops(dev, iters=20):
@@ -223,9 +477,10 @@ def w8a16_tflops(dev, iters=20):
     f = lambda: q8.w8a16_mm(x, wq, sc, out=y)  # noqa: E731
     for _ in range(5):
         f()
-    ms = events_time(f, iters)
+    st = call_stats(f, iters)
+    ms = st["mean"]
     t = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
-    return {"us": ms * 1e3, "TFLOPS": t, "frac_bf16_peak": t / PEAK_BF16_TFLOPS}
+    return {"us": ms * 1e3, "TFLOPS": t, "frac_bf16_peak": t / PEAK_BF16_TFLOPS, "stats_us": _us(st)}
 
 
 def copy_calibration(dev, nbytes=512 << 20, reps=3):
@@ -235,28 +490,6 @@ def copy_calibration(dev, nbytes=512 << 20, reps=3):
     ms = events_time(lambda: b.copy_(a), reps)
     return {"bytes_read": nbytes, "bytes_written": nbytes, "us": ms * 1e3,
             "GB/s": 2 * nbytes / (ms * 1e-3) / 1e9}
-
-
-def quant_after(quant, before, iters: int) -> float:
-    """Median time (ms) of quant() measured with events on the launch stream
-    when each call follows a call of before() (whose traffic evicts quant's
-    input from the caches, as in the step)."""
-    s = torch.cuda.current_stream()
-    for _ in range(3):
-        before()
-        quant()
-    s.synchronize()
-    ev = []
-    for _ in range(iters):
-        before()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(s)
-        quant()
-        e1.record(s)
-        ev.append((e0, e1))
-    s.synchronize()
-    ts = sorted(a.elapsed_time(b) for a, b in ev)
-    return ts[len(ts) // 2]
 
 
 def rmsnorm_quant_gbs(dev, iters=20):
@@ -272,9 +505,10 @@ def rmsnorm_quant_gbs(dev, iters=20):
     f = lambda: q8.q8_rmsnorm_quant(x, gam, 1e-6, residual=res, out=xq, scale_out=st)  # noqa: E731
     for _ in range(3):
         f()
-    ms = events_time(f, iters)
+    st = call_stats(f, iters)
+    ms = st["mean"]
     nbytes = 2 * wl.M * wl.K * 3 + wl.M * wl.K + 4 * wl.M + 2 * wl.K
-    return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+    return {"us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9, "stats_us": _us(st),
             "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": nbytes,
             "shape": [wl.M, wl.K]}
 
@@ -294,11 +528,12 @@ def group_act_tops(dev, iters=20):
     for _ in range(3):
         qf()
         g()
-    gms = events_time(g, iters)
+    gst = call_stats(g, iters)
+    gms = gst["mean"]
     qms = events_time(qf, iters)
     t = 2.0 * wl.M * wl.N * wl.K / (gms * 1e-3) / 1e12
     qbytes = 3 * wl.M * wl.K + 4 * wl.M * (wl.K // 128)
-    return {"gemm_us": gms * 1e3, "TOPS": t, "frac_int8_peak": t / PEAK_INT8_TOPS,
+    return {"gemm_us": gms * 1e3, "TOPS": t, "frac_int8_peak": t / PEAK_INT8_TOPS, "gemm_stats_us": _us(gst),
             "quant_us": qms * 1e3, "quant_GB/s": qbytes / (qms * 1e-3) / 1e9}
 
 
@@ -323,13 +558,14 @@ def fp8_block_tflops(dev, iters=20):
         g()
     for _ in range(5):
         step()
-    gms = events_time(g, iters)
+    gst = call_stats(g, iters)
+    gms = gst["mean"]
     qms = events_time(qf, iters)
     sms = events_time(step, iters)
     flops = 2.0 * wl.M * wl.N * wl.K
     t = flops / (gms * 1e-3) / 1e12
     qbytes = 3 * wl.M * wl.K + 4 * wl.M * (wl.K // 128)
-    return {"gemm_us": gms * 1e3, "TFLOPS": t, "frac_fp8_peak": t / PEAK_FP8_TFLOPS,
+    return {"gemm_us": gms * 1e3, "TFLOPS": t, "frac_fp8_peak": t / PEAK_FP8_TFLOPS, "gemm_stats_us": _us(gst),
             "quant_us": qms * 1e3, "quant_GB/s": qbytes / (qms * 1e-3) / 1e9,
             "step_us": sms * 1e3, "step_TFLOPS": flops / (sms * 1e-3) / 1e12,
             "shape": [wl.M, wl.N, wl.K]}
@@ -456,6 +692,7 @@ def m_sweep(dev, reps=10):
 
 
 SECONDARY = {"decode": lambda dev: decode_gbs(dev), "group128": lambda dev: group_tops(dev),
+             "tiny": lambda dev: tiny_latency(dev),
              "m_sweep": lambda dev: m_sweep(dev),
              "group128_act": lambda dev: group_act_tops(dev),
              "w8a16": lambda dev: w8a16_tflops(dev), "rmsnorm_quant": lambda dev: rmsnorm_quant_gbs(dev),
@@ -470,7 +707,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary",
-                    default="decode,group128,group128_act,w8a16,rmsnorm_quant,fp8_block,f16,m_sweep",
+                    default="decode,tiny,group128,group128_act,w8a16,rmsnorm_quant,fp8_block,f16,m_sweep",
                     help="comma list of secondary workloads, or 'none'")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -490,44 +727,69 @@ def main():
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     xq = torch.empty((M, K), dtype=torch.int8, device=dev)
     st = torch.empty((M,), dtype=torch.float32, device=dev)
+    quant = lambda: q8.q8_quant_per_token(xo, out=xq, scale_out=st)  # noqa: E731
+    gemm = lambda: q8.q8_scaled_mm(xq, wq, st, sc, out=y)  # noqa: E731
+    ops = 2.0 * M * N * K
 
-    def step():
-        q8.q8_quant_scaled_mm(xo, wq, sc, out=y, xq_out=xq, scale_tok_out=st)
+    # the GEMM alone, events on the launch stream, after about 60 ms of
+    # untimed calls: the board leaves its idle clock here, before the steps
+    log("gemm alone")
+    quant()
+    gemm_alone = call_stats(gemm, args.steps)
+
+    s = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e is not None:
+            e[0].record(s)
+        quant()
+        if e is not None:
+            e[1].record(s)
+        gemm()
+        if e is not None:
+            e[2].record(s)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(ev[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ops = 2.0 * M * N * K
     value = ops * args.steps / elapsed / 1e12
+    quant_in = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    gemm_in = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    gemm_ms = float(gemm_in.mean())
 
-    # dominant kernel (the INT8 GEMM) alone, events on the launch stream
-    gemm = lambda: q8.q8_scaled_mm(xq, wq, st, sc, out=y)  # noqa: E731
-    gemm_ms = events_time(gemm, args.steps)
-    quant = lambda: q8.q8_quant_per_token(xo, out=xq, scale_out=st)  # noqa: E731
-    quant_ms = events_time(quant, args.steps)
     achieved = ops / (gemm_ms * 1e-3) / 1e12
     quant_bytes = M * K * 2 + M * K + 4 * M
     traffic = gemm_traffic()
     algo_bytes = M * K + N * K + 4 * M + 4 * N + 2 * M * N
+    log("ceilings")
+    ceil = ceilings(dev)
+    mfma_ceil = ceil["mfma_int8_random"]["TOPS"]
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_INT8_TOPS,
                 "traffic": None if traffic is None else sum(traffic),
                 "traffic_read_write": traffic, "algorithmic_bytes": algo_bytes,
                 "kernel": "gemm_big_kernel (per-channel epilogue, 256 x 384 tiles)",
-                "kernel_us": gemm_ms * 1e3}
-    quant_step_ms = quant_after(quant, gemm, args.steps)
-    secondary = {"quant_kernel": {"us": quant_ms * 1e3,
-                                  "GB/s": quant_bytes / (quant_ms * 1e-3) / 1e9,
-                                  "timing": "back to back, X left in the last-level cache",
-                                  "in_step_us": quant_step_ms * 1e3,
+                "kernel_us": gemm_ms * 1e3,
+                "kernel_us_p10_p50_p90": [round(float(np.percentile(gemm_in, q)) * 1e3, 2) for q in (10, 50, 90)],
+                "timing": "events around the GEMM inside each of the timed steps",
+                "measured_ceiling": mfma_ceil, "frac_measured_ceiling": achieved / mfma_ceil,
+                "measured_ceiling_kind": "int8 MFMA-only loop, operands changing every MFMA",
+                "frac_256cu_2p4ghz_5033": achieved / 5033.2}
+    quant_step_ms = float(quant_in.mean())
+    secondary = {"quant_kernel": {"in_step_us": quant_step_ms * 1e3,
                                   "in_step_GB/s": quant_bytes / (quant_step_ms * 1e-3) / 1e9,
-                                  "in_step_timing": "each call right after a GEMM, as in the step: X read from HBM"}}
+                                  "in_step_timing": "events around the quantizer inside each timed step "
+                                                    "(X read from HBM after the previous GEMM)"},
+                 "gemm_alone": dict(_us(gemm_alone), TOPS=ops / (gemm_alone["mean"] * 1e-3) / 1e12,
+                                    timing="events around each call, back to back, before the steps"),
+                 "ceilings": ceil}
     names = [] if args.no_secondary or args.secondary == "none" else args.secondary.split(",")
     for name in names:
         if name not in SECONDARY:

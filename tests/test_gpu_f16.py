@@ -126,9 +126,12 @@ def test_quant_scaled_mm_f16_token_counts(M):
     wq, sc = q8.q8_quant_weight(dev(w))
     y, xq, st = q8.q8_quant_scaled_mm_f16(dev(x), wq, sc)
     xq_ref, st_ref = oracle.quant_per_token_f16(hbits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    np.testing.assert_array_equal(host(wq).numpy(), wq_ref)
+    np.testing.assert_array_equal(host(sc).numpy(), sc_ref)
     np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
     np.testing.assert_array_equal(host(st).numpy(), st_ref)
-    y_ref = oracle.scaled_mm_f16(xq_ref, host(wq).numpy(), st_ref, host(sc).numpy())
+    y_ref = oracle.scaled_mm_f16(xq_ref, wq_ref, st_ref, sc_ref)
     assert_ulp1(hbits(host(y)), y_ref, f"one-call f16 M={M}")
 
 
@@ -158,10 +161,14 @@ def test_prefill_f16_full_size_sampled_rows():
     wq, sc = q8.q8_quant_weight(dev(w))
     y, xq, st = q8.q8_quant_scaled_mm_f16(dev(x), wq, sc)
     xq_ref, st_ref = oracle.quant_per_token_f16(hbits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    np.testing.assert_array_equal(host(wq).numpy(), wq_ref)
+    np.testing.assert_array_equal(host(sc).numpy(), sc_ref)
     np.testing.assert_array_equal(host(st).numpy(), st_ref)
     np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
-    rows = np.array([0, 1, 255, 256, 4095, 8190, 8191, 777])
-    y_ref = oracle.scaled_mm_f16(xq_ref[rows], host(wq).numpy(), st_ref[rows], host(sc).numpy())
+    rng = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 4095, 8190, 8191, 777], rng.integers(0, wl.M, 56)]))
+    y_ref = oracle.scaled_mm_f16(xq_ref[rows], wq_ref, st_ref[rows], sc_ref)
     assert_ulp1(hbits(host(y))[rows], y_ref, "prefill f16 sampled rows")
 
 

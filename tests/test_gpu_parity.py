@@ -525,12 +525,13 @@ def test_scaled_mm_ragged_and_zero_rows():
     assert not (yb[7] & 0x7FFF).any() and not (yb[130] & 0x7FFF).any()
 
 
-def test_prefill_full_size_sampled_rows():
+def test_prefill_full_size_every_row():
     """The prefill workload at full size, in the benchmark's launch
-    configuration (fold, weight quant, then the one-call layer), compared on
-    sampled rows (first, last, tile edges, random)."""
+    configuration (fold, weight quant, then the one-call layer): codes and
+    scales bit-exact, and every one of the 8192 x 15360 outputs within 1 ulp
+    of the oracle."""
     wl = synth.WORKLOADS["prefill"]
-    say("prefill full size")
+    say("prefill full size, every row")
     x = synth.activations(wl, 0)
     w = synth.weights(wl, 0)
     s_ref = oracle.smooth_scales(bits(x))
@@ -546,12 +547,99 @@ def test_prefill_full_size_sampled_rows():
     np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
     np.testing.assert_array_equal(host(sc).numpy(), sc_ref)
     np.testing.assert_array_equal(host(wq).numpy(), wq_ref)
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 4095, 8190, 8191],
-                                     rng.integers(0, wl.M, 23)]))
-    y_ref = oracle.scaled_mm(xq_ref[rows], wq_ref, st_ref[rows], sc_ref)
     yh = bits(host(y))
-    assert_ulp1(yh[rows], y_ref, "prefill sampled rows")
+    del y
+    y_ref = oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref)
+    assert_ulp1(yh, y_ref, "prefill every row")
+
+
+def test_mm_i32_prefill_shape_sampled_rows():
+    """The raw INT32 product at exactly the prefill shape 8192 x 15360 x 5120
+    (the 256 x 384 tiles), on the workload's own codes: sampled rows (tile
+    edges of both tilings and random) bit-exact against the oracle."""
+    wl = synth.WORKLOADS["prefill"]
+    say("mm_i32 8192 x 15360 x 5120")
+    x = synth.activations(wl, 0)
+    w = synth.weights(wl, 0)
+    s_ref = oracle.smooth_scales(bits(x))
+    xq_ref, _ = oracle.quant_per_token(oracle.smooth_fold_x(bits(x), s_ref))
+    wq_ref, _ = oracle.quant_weight(oracle.smooth_fold_w(w.numpy(), s_ref))
+    del w
+    c = q8.q8_mm_i32(dev(torch.from_numpy(xq_ref)), dev(torch.from_numpy(wq_ref)))
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 255, 256, 383, 384, 4095, 4096, 8190, 8191],
+                                     rng.integers(0, wl.M, 52)]))
+    ch = host(c)[torch.from_numpy(rows)].numpy()
+    del c
+    ref = oracle.mm_i32(xq_ref[rows], wq_ref)
+    np.testing.assert_array_equal(ch, ref)
+
+
+def test_group128_int32_partials_on_k_slices():
+    """The group-128 epilogue folds the exact int32 sum of each 128-wide K
+    block.  Those block sums are checked on their own: q8_mm_i32 on the
+    128-wide K slice of each chosen block (pointer offsets into the full
+    operands, leading dimension K), at the group-scaled workload's shape
+    4096 x 5120 x 5120, every row, bit-exact against the oracle."""
+    wl = synth.WORKLOADS["group128"]
+    say("group-128 int32 partials on K slices")
+    x = synth.activations(wl, 0)
+    w = synth.weights(wl, 0)
+    xq_ref, _ = oracle.quant_per_token(bits(x))
+    wq_ref, _ = oracle.quant_weight(w.numpy(), group=128)
+    xd, wd = dev(torch.from_numpy(xq_ref)), dev(torch.from_numpy(wq_ref))
+    G = wl.K // 128
+    for g in (0, 1, 17, G - 2, G - 1):
+        sl = slice(128 * g, 128 * g + 128)
+        c = q8.q8_mm_i32(xd[:, sl], wd[:, sl])
+        ref = oracle.mm_i32(np.ascontiguousarray(xq_ref[:, sl]), np.ascontiguousarray(wq_ref[:, sl]))
+        np.testing.assert_array_equal(host(c).numpy(), ref)
+        assert np.abs(ref).max() < 2 ** 24  # (float)p_g is exact in the fold
+
+
+def _at_allocation_end(t: torch.Tensor) -> torch.Tensor:
+    """A copy of t on the GPU placed at the very end of an allocation whose
+    size is a whole number of 2 MiB (the caching allocator's segment
+    granule), so that no byte past its last element belongs to it."""
+    nb = t.numel() * t.element_size()
+    total = -(-(nb + (1 << 20)) // (2 << 20)) * (2 << 20)
+    buf = torch.empty(total, dtype=torch.uint8, device=DEV)
+    v = buf[total - nb:].view(t.dtype).view(t.shape)
+    v.copy_(t.to(DEV))
+    return v
+
+
+@pytest.mark.parametrize("M,N,K", [(4100, 4000, 512),    # 256 x 384; group 256 x 128; W8A16 256 x 320
+                                   (4000, 4000, 384),    # 256 x 256; W8A16 on the 256 x 128 tiles
+                                   (1100, 4112, 384),    # 128 x 128 tiles
+                                   (300, 1040, 256)])    # 32 x 128 tiles
+def test_operands_ending_at_allocation_end(M, N, K):
+    """Operands whose last byte is the last byte of their allocation, with
+    ragged tiles in M and N: the tiled kernels read only the caller's bytes
+    (tile rows past the edge, and the stage after K that the last stage
+    prefetches, read as zero instead of from past the allocation).  The
+    int32 product, the per-channel and group-scaled epilogues and W8A16,
+    every row against the oracle."""
+    say("operands at allocation end", M, N, K)
+    x, w = synth.custom(M, K, N, seed=M + 3 * N, outlier_cols=3)
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    xa = _at_allocation_end(torch.from_numpy(xq_ref))
+    wa = _at_allocation_end(torch.from_numpy(wq_ref))
+    c = q8.q8_mm_i32(xa, wa)
+    np.testing.assert_array_equal(host(c).numpy(), oracle.mm_i32(xq_ref, wq_ref))
+    y = q8.q8_scaled_mm(xa, wa, dev(st_ref), dev(sc_ref))
+    assert_ulp1(bits(host(y)), oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref), "at allocation end")
+    wg_ref, sg_ref = oracle.quant_weight(w.numpy(), group=128)
+    wga = _at_allocation_end(torch.from_numpy(wg_ref))
+    y = q8.q8_scaled_mm_group128(xa, wga, dev(st_ref), dev(sg_ref))
+    assert_ulp1(bits(host(y)), oracle.scaled_mm_group128(xq_ref, wg_ref, st_ref, sg_ref),
+                "group128 at allocation end")
+    xb = _at_allocation_end(x)
+    y = q8.w8a16_mm(xb, wa, dev(sc_ref))
+    rows = np.unique(np.concatenate([np.arange(max(0, M - 40), M), [0, 1, 255, 256]]))
+    _check_w8a16(bits(host(y))[rows], np.ascontiguousarray(bits(x)[rows]), wq_ref, sc_ref,
+                 "w8a16 at allocation end")
 
 
 # ----------------------------- per-group activations, group-128 weights --
@@ -586,9 +674,9 @@ def test_scaled_mm_group128_act_shapes(M, N, K):
     assert_ulp1(bits(host(y)), y_ref, f"group128 act {M}x{N}x{K}")
 
 
-def test_group128_act_full_size_sampled_rows():
+def test_group128_act_full_size_every_row():
     """The group-128 workload's shape (4096 x 5120 x 5120) with per-group
-    activation scales, in one launch; sampled rows against the oracle."""
+    activation scales, in one launch; every row against the oracle."""
     wl = synth.WORKLOADS["group128"]
     say("group128 act full size")
     x = synth.activations(wl, 0)
@@ -599,10 +687,11 @@ def test_group128_act_full_size_sampled_rows():
     wq, sw = q8.q8_quant_weight(dev(w), group=128)
     np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
     np.testing.assert_array_equal(host(sx).numpy(), sx_ref)
+    np.testing.assert_array_equal(host(sw).numpy(), sw_ref)
+    np.testing.assert_array_equal(host(wq).numpy(), wq_ref)
     y = q8.q8_scaled_mm_group128_act(xq, wq, sx, sw)
-    rows = np.array([0, 1, 127, 128, 2047, 4094, 4095, 777, 3333])
-    y_ref = oracle.scaled_mm_group128_act(xq_ref[rows], wq_ref, sx_ref[rows], sw_ref)
-    assert_ulp1(bits(host(y))[rows], y_ref, "group128 act sampled rows")
+    y_ref = oracle.scaled_mm_group128_act(xq_ref, wq_ref, sx_ref, sw_ref)
+    assert_ulp1(bits(host(y)), y_ref, "group128 act every row")
 
 
 # ------------------------------------------------------------ group 128 --
@@ -644,9 +733,11 @@ def test_group_scaled_large_tiles_ragged():
     assert_ulp1(bits(host(y))[rows], y_ref, "group128 act large tiles")
 
 
-def test_group128_full_size_sampled_rows():
+def test_group128_full_size_every_row():
+    """The group-scaled workload 4096 x 5120 x 5120 in one launch: codes and
+    scales bit-exact, every output within 1 ulp."""
     wl = synth.WORKLOADS["group128"]
-    say("group128 full size")
+    say("group128 full size, every row")
     x = synth.activations(wl, 0)
     w = synth.weights(wl, 0)
     xq_ref, st_ref = oracle.quant_per_token(bits(x))
@@ -654,10 +745,12 @@ def test_group128_full_size_sampled_rows():
     xq, st = q8.q8_quant_per_token(dev(x))
     wq, sg = q8.q8_quant_weight(dev(w), group=128)
     np.testing.assert_array_equal(host(sg).numpy(), sg_ref)
+    np.testing.assert_array_equal(host(wq).numpy(), wq_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    np.testing.assert_array_equal(host(st).numpy(), st_ref)
     y = q8.q8_scaled_mm_group128(xq, wq, st, sg)
-    rows = np.array([0, 1, 63, 64, 127, 128, 2047, 4094, 4095, 1234, 3000])
-    y_ref = oracle.scaled_mm_group128(xq_ref[rows], wq_ref, st_ref[rows], sg_ref)
-    assert_ulp1(bits(host(y))[rows], y_ref, "group128 sampled rows")
+    y_ref = oracle.scaled_mm_group128(xq_ref, wq_ref, st_ref, sg_ref)
+    assert_ulp1(bits(host(y)), y_ref, "group128 every row")
 
 
 # --------------------------------------------------------------- W8A16 --
@@ -756,14 +849,21 @@ def test_w8a16_big_tiles_sampled_rows(M, N, K, pad):
 
 
 def test_w8a16_full_size_sampled_rows():
+    """The W8A16 workload 8192 x 5120 x 13824 (256 x 320 tiles): weight codes
+    bit-exact, and about 240 rows (all 82 position-outlier rows, tile edges,
+    random) against the oracle's fp64 sums, every column."""
     wl = synth.WORKLOADS["w8a16"]
     say("w8a16 full size")
     x = synth.activations(wl, 0)
     w = synth.weights(wl, 0)
     wq_ref, sc_ref = oracle.quant_weight(w.numpy())
     wq, sc = q8.q8_quant_weight(dev(w))
+    np.testing.assert_array_equal(host(wq).numpy(), wq_ref)
+    np.testing.assert_array_equal(host(sc).numpy(), sc_ref)
     y = q8.w8a16_mm(dev(x), wq, sc)
-    rows = np.array([0, 1, 40, 81, 82, 83, 127, 128, 4096, 8190, 8191])
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([np.arange(0, 84), [127, 128, 255, 256, 4095, 4096, 8190, 8191],
+                                     rng.integers(84, wl.M, 150)]))
     xb = bits(x)
     _check_w8a16(bits(host(y))[rows], np.ascontiguousarray(xb[rows]), wq_ref, sc_ref,
                  "w8a16 sampled rows")

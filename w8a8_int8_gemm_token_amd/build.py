@@ -21,6 +21,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq8.so")
 SOURCES = [os.path.join(CSRC, "q8_abi.hip")]
+# measurement kernels for the benchmark (ceilings of this board), a library
+# of their own: nothing of the layer calls them
+CEIL_LIB = os.path.join(PKG, "libq8_ceilings.so")
+CEIL_SOURCES = [os.path.join(CSRC, "ceilings.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")] + \
     [os.path.join(ROOT, "include", "q8.h")]
 
@@ -34,14 +38,20 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile libq8.so (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
+def _compile(sources, lib, verbose, extra):
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, *extra, *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile libq8.so and the benchmark's libq8_ceilings.so (always
+    recompiles)."""
+    _compile(SOURCES, LIB, verbose, extra)
+    _compile(CEIL_SOURCES, CEIL_LIB, verbose, extra)
     return LIB
 
 

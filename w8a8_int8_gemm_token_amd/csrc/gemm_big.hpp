@@ -20,7 +20,8 @@
 //
 // Data movement and layout are those of gemm_i8_kernel: direct
 // buffer_load_dwordx4 ... lds of 8 rows x 128 bytes per wave instruction,
-// rows past the edge read as zero, chunk c of LDS row r at slot
+// the whole offset in the range-checked vector operand, so rows past the
+// edge and the stage after K read as zero, chunk c of LDS row r at slot
 // c ^ (r & 7) ^ ((r >> 3) & 1).  Schedule of a stage (four 32-deep
 // sub-steps): the next stage's loads go out behind the MFMAs of sub-step 0;
 // each sub-step's fragments are read behind the previous sub-step's MFMAs as
@@ -71,8 +72,8 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs p) {
     // ---- direct loads: instruction i of wave wid fills rows 8 (wid XIW + i)
     // .. + 7; lane l writes slot l % 8 of row l / 8 of that group from global
     // chunk (l % 8) ^ (l / 8) ^ (parity of the 8-row group)
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, (uint32_t)((int64_t)M * p.ldx));
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, (uint32_t)((int64_t)N * p.ldw));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, operand_extent(M, p.ldx, K));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, operand_extent(N, p.ldw, K));
     const int lrow = lane >> 3, lslot = lane & 7;
     const int xv[2] = {lrow * (int)p.ldx + ((lslot ^ lrow) << 4), lrow * (int)p.ldx + ((lslot ^ lrow ^ 1) << 4)};
     const int wv[2] = {lrow * (int)p.ldw + ((lslot ^ lrow) << 4), lrow * (int)p.ldw + ((lslot ^ lrow ^ 1) << 4)};
@@ -84,13 +85,13 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < XIW; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (Q8_LDS void*)(bx + (wid * XIW + i) * 1024), 16, xv[(wid * XIW + i) & 1],
-                xs0 + i * 8 * (int)p.ldx + koff, 0, 0);
+                xr, (Q8_LDS void*)(bx + (wid * XIW + i) * 1024), 16, lane_offset(xv[(wid * XIW + i) & 1],
+                xs0 + i * 8 * (int)p.ldx + koff), 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < WIW; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wr, (Q8_LDS void*)(bw + (wid * WIW + i) * 1024), 16, wv[(wid * WIW + i) & 1],
-                ws0 + i * 8 * (int)p.ldw + koff, 0, 0);
+                wr, (Q8_LDS void*)(bw + (wid * WIW + i) * 1024), 16, lane_offset(wv[(wid * WIW + i) & 1],
+                ws0 + i * 8 * (int)p.ldw + koff), 0, 0, 0);
     };
 
     // ---- fragment reads: sub-step kk takes chunk 2 kk + hi of the lane's

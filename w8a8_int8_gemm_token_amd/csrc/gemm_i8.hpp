@@ -41,10 +41,14 @@
 // Data movement (BK = 128 bytes of K per stage):
 //  * global -> LDS with buffer_load_dwordx4 ... lds (direct to LDS, no VGPR
 //    staging).  Every wave instruction moves 8 rows x 128 contiguous bytes
-//    (whole 128-byte lines).  One buffer resource per operand; a row past
-//    the matrix edge falls outside the resource's range and reads as zero
-//    (its products are never stored).  The row/stage part of the address is
-//    a scalar offset, so a lane keeps only two vector offsets per operand.
+//    (whole 128-byte lines).  One buffer resource per operand, over exactly
+//    the bytes the caller guarantees ((rows - 1) * ld + K); the whole offset
+//    of every load is its vector offset, the part the hardware checks
+//    against that range (a scalar offset is added after the check).  So a
+//    row past the matrix edge, and the stage after K that the last stage
+//    prefetches, read as zero without touching memory (their products are
+//    never stored).  A lane keeps two vector offsets per operand and adds
+//    the row/stage part, a wave-uniform value, per load.
 //  * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at slot
 //    c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).  The MFMA fragment reads
 //    (one 16-byte chunk per lane, 32 consecutive rows) are then free of bank
@@ -134,6 +138,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
+// Bytes of a row-major operand that the caller guarantees: rows - 1 full
+// leading dimensions, then the last row's kbytes.  A resource over exactly
+// this range turns every read past the last row's K-th byte -- the tile
+// rows past the edge, and the prefetch of the stage after K on the last
+// row -- into a zero read that touches no memory.  (rows * ld would not:
+// for a view that starts inside its rows, such as a K slice at a column
+// offset, rows * ld from that start runs past the end of the allocation.)
+__device__ __forceinline__ uint32_t operand_extent(int rows, int64_t ld, int kbytes) {
+    return rows > 0 ? (uint32_t)((int64_t)(rows - 1) * ld + kbytes) : 0u;
+}
+
+// Vector offset of one buffer load: the lane's part v plus a wave-uniform
+// part u (row and stage).  The empty asm keeps u an opaque scalar here, so
+// the compiler adds it right at the load instead of keeping one hoisted
+// vector sum per load alive across the K loop.
+__device__ __forceinline__ int lane_offset(int v, int u) {
+    asm volatile("" : "+s"(u));
+    return v + u;
+}
+
 template <int BM, int BN, int WM, int WN, int EPI_, int GM>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     constexpr int EPI = epi_base(EPI_);
@@ -197,10 +221,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     // (wid*XIW + i)*8 .. +8 of the tile; lane l writes LDS slot l%8 of row
     // l/8 of that group, i.e. global chunk (l%8) ^ f(row), and f(row)
     // = (l/8) ^ (parity of the instruction's 8-row group).
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, (uint32_t)((int64_t)M * p.ldx));
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, (uint32_t)((int64_t)N * p.ldw));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, operand_extent(M, p.ldx, W16 ? 2 * K : K));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, operand_extent(N, p.ldw, K));
     const int G = K >> 7;
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.s_w, (uint32_t)((int64_t)N * G * 4));
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.s_w, GRP ? (uint32_t)((int64_t)N * G * 4) : 0u);
     const int lrow = lane >> 3, lslot = lane & 7;
     const int xv[2] = {lrow * (int)p.ldx + ((lslot ^ lrow) << 4),
                        lrow * (int)p.ldx + ((lslot ^ lrow ^ 1) << 4)};
@@ -220,26 +244,26 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
             for (int i = 0; i < WLC; ++i) {
                 const int c = (int)threadIdx.x + i * NW * 64, r = c >> 2, q = c & 3;
                 wreg[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      wr, (n0 + r) * (int)p.ldw + q * 16, kt * 64, 0));
+                                                      wr, lane_offset((n0 + r) * (int)p.ldw + q * 16, kt * 64), 0, 0));
             }
         }
 #pragma unroll
         for (int i = 0; i < XIW; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (Q8_LDS void*)(bx + (wid * XIW + i) * 1024), 16, xv[(wid * XIW + i) & 1],
-                xs0 + i * 8 * (int)p.ldx + koff, 0, 0);
+                xr, (Q8_LDS void*)(bx + (wid * XIW + i) * 1024), 16, lane_offset(xv[(wid * XIW + i) & 1],
+                xs0 + i * 8 * (int)p.ldx + koff), 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < WIW; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wr, (Q8_LDS void*)(bw + (wid * WIW + i) * 1024), 16, wv[(wid * WIW + i) & 1],
-                ws0 + i * 8 * (int)p.ldw + koff, 0, 0);
+                wr, (Q8_LDS void*)(bw + (wid * WIW + i) * 1024), 16, lane_offset(wv[(wid * WIW + i) & 1],
+                ws0 + i * 8 * (int)p.ldw + koff), 0, 0, 0);
         if constexpr (SGI > 0) {
 #pragma unroll
             for (int i = 0; i < (SGI + NW - 1) / NW; ++i) {
                 const int j = wid + i * NW;  // 64-channel block of this load
                 if (j < SGI)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (Q8_LDS void*)(bs + j * 64), 4, sv,
-                                                             j * 64 * G * 4 + kt * 4, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (Q8_LDS void*)(bs + j * 64), 4,
+                                                             lane_offset(sv, j * 64 * G * 4 + kt * 4), 0, 0, 0);
             }
         }
         if constexpr (SXI > 0) {
@@ -248,7 +272,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
                 const int j = wid + i * NW;
                 if (j < SXI)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(sxr, (Q8_LDS void*)(bs + XOFF + j * 64), 4,
-                                                             svx, j * 64 * G * 4 + kt * 4, 0, 0);
+                                                             lane_offset(svx, j * 64 * G * 4 + kt * 4), 0, 0, 0);
             }
         }
     };

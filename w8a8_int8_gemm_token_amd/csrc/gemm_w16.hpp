@@ -71,8 +71,8 @@ __global__ __launch_bounds__(512) void gemm_w16_kernel(GemmArgs p) {
     const int hi = lane >> 5;
 
     // ---- activation loads (p.x is addressed in bytes, ldx in bytes)
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, (uint32_t)((int64_t)M * p.ldx));
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, (uint32_t)((int64_t)N * p.ldw));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, operand_extent(M, p.ldx, 2 * K));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, operand_extent(N, p.ldw, K));
     const int lrow = lane >> 3, lslot = lane & 7;
     const int xv[2] = {lrow * (int)p.ldx + ((lslot ^ lrow) << 4), lrow * (int)p.ldx + ((lslot ^ lrow ^ 1) << 4)};
     const int xs0 = (m0 + wid * XIW * 8) * (int)p.ldx;
@@ -84,13 +84,13 @@ __global__ __launch_bounds__(512) void gemm_w16_kernel(GemmArgs p) {
             const int c = tid + i * NW * 64, r = c >> 2, q = c & 3;
             if (i + 1 < WLC || c < WCH)
                 wreg[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      wr, (n0 + r) * (int)p.ldw + q * 16, kt * KS, 0));
+                                                      wr, lane_offset((n0 + r) * (int)p.ldw + q * 16, kt * KS), 0, 0));
         }
 #pragma unroll
         for (int i = 0; i < XIW; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (Q8_LDS void*)(bx + (wid * XIW + i) * 1024), 16, xv[(wid * XIW + i) & 1],
-                xs0 + i * 8 * (int)p.ldx + kt * BK, 0, 0);
+                xr, (Q8_LDS void*)(bx + (wid * XIW + i) * 1024), 16, lane_offset(xv[(wid * XIW + i) & 1],
+                xs0 + i * 8 * (int)p.ldx + kt * BK), 0, 0, 0);
     };
     // the staged weights -> exact 16-bit values: 16 codes of row r, chunk q,
     // become the 16-bit chunks 2q and 2q + 1 of that row
