@@ -641,14 +641,16 @@ def f16_layer(dev, iters=20):
 # the W8A16 down projection (5120 x 17408).
 SWEEP_SHAPES = (("qkv", "w8a8", 15360, 5120), ("gate_up", "w8a8", 17408, 5120),
                 ("o_proj", "w8a8", 5120, 5120), ("down_proj", "w8a16", 5120, 17408))
-SWEEP_M = (1, 2, 4, 8, 16, 32, 64, 96, 128, 256)
+SWEEP_M = (1, 2, 4, 8, 16, 32, 64, 96, 128, 192, 256, 384, 512)
 
 
 def m_sweep(dev, reps=10):
-    """Per-call time of each model shape at small token counts (decode,
-    speculative verify, small batches): calls cycle through enough weight
-    copies to exceed 2x the 256 MB last-level cache, captured in a HIP graph.
-    GB/s counts the weights, scales, activations and outputs once."""
+    """Per-call time of each model shape at 1-512 tokens (decode,
+    speculative verify, small batches, chunks): calls cycle through enough
+    weight copies to exceed 2x the 256 MB last-level cache, captured in a
+    HIP graph.  Where the library splits K over a workspace, the _ws entry
+    point is timed as well (ws_us).  GB/s counts the weights, scales,
+    activations and outputs once."""
     out = {}
     for name, kind, N, K in SWEEP_SHAPES:
         w = synth.weights(synth.WORKLOADS["decode"], 0, N=N, K=K).to(dev)
@@ -660,31 +662,47 @@ def m_sweep(dev, reps=10):
         for M in SWEEP_M:
             x = synth.activations(synth.WORKLOADS["decode"], 0, M=M, K=K).to(dev)
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            wsb = q8.q8_workspace_bytes(M, N, K)
+            ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev)
             if kind == "w8a8":
                 xq = torch.empty((M, K), dtype=torch.int8, device=dev)
                 st = torch.empty((M,), dtype=torch.float32, device=dev)
 
                 def call(wi):
                     q8.q8_quant_scaled_mm(x, wi, sc, out=y, xq_out=xq, scale_tok_out=st)
+
+                def call_ws(wi):
+                    q8.q8_quant_scaled_mm_ws(x, wi, sc, out=y, xq_out=xq, scale_tok_out=st, workspace=ws)
                 nbytes = N * K + 4 * N + 2 * M * K + M * K + 4 * M + 2 * M * N
             else:
                 def call(wi):
                     q8.w8a16_mm(x, wi, sc, out=y)
+
+                def call_ws(wi):
+                    q8.w8a16_mm_ws(x, wi, sc, out=y, workspace=ws)
                 nbytes = N * K + 4 * N + 2 * M * K + 2 * M * N
 
-            def cycle():
-                for wi in wqs:
-                    call(wi)
-            cycle()
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+            def graph_us(fn):
+                def cycle():
+                    for wi in wqs:
+                        fn(wi)
                 cycle()
-            g.replay()
-            torch.cuda.synchronize()
-            ms = events_time(g.replay, reps) / ncopy
-            row[f"M{M}"] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
-            del g
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    cycle()
+                g.replay()
+                torch.cuda.synchronize()
+                us = events_time(g.replay, reps) / ncopy * 1e3
+                del g
+                return us
+            us = graph_us(call)
+            row[f"M{M}"] = {"us": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+            if wsb:  # K split over a workspace (the _ws entry point)
+                us = graph_us(call_ws)
+                row[f"M{M}"].update({"ws_us": round(us, 2), "ws_GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                     "ws_bytes": wsb})
+            del ws
         out[f"{name} {kind} N={N} K={K}"] = row
         del wqs, wq
         torch.cuda.empty_cache()

@@ -182,6 +182,60 @@ q8_status q8_mm_i32(const int8_t *a, int64_t lda, const int8_t *b,
                     int64_t N, int64_t K, q8_stream stream);
 
 /* ------------------------------------------------------------------------
+ * Split K with a caller workspace.  Between the few-token kernels and the
+ * large tiles (roughly 65-512 tokens at the model's shapes) the output has
+ * too few tiles to keep 256 compute units busy.  The _ws entry points then
+ * split K: ks workgroups per output tile each sum a contiguous K range into
+ * a plane of the caller's workspace, and a second kernel adds the planes and
+ * applies the epilogue.  They compute exactly what their namesakes without
+ * _ws compute (same arguments, layouts, rules and errors, plus the two
+ * workspace arguments):
+ *  - q8_scaled_mm_ws, q8_quant_scaled_mm_ws: the planes hold exact int32
+ *    partial sums, added in int32, so acc and the bf16 output are the same
+ *    bits as q8_scaled_mm's ("...W8A8 INT8 (v3)", "Recipe" and "Serving").
+ *  - w8a16_mm_ws: the planes hold fp32 partial sums added in fp32 in plane
+ *    order; the result is W8A16's fp32-accumulated sum in another order
+ *    ("lued/Qwen3.8-27B-INT8-W8A16-MTP", "Why W8A16 on Ampere").
+ * Ownership: the workspace is the caller's device memory, read and written
+ * only during the call's kernels (no state is kept between calls, nothing
+ * needs clearing).  Calls that share one workspace must be ordered (the
+ * same stream); concurrent calls need their own.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of workspace the _ws entry points need for an (M, N, K) problem:
+ * 0 when they would not split K (then the workspace may be NULL), else
+ * ks * M * N * 4 for the library's split count ks (2 <= ks <= 10).  Never
+ * more than 31,457,280 bytes (30 MiB).  Nonpositive sizes give 0. */
+int64_t q8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* As q8_scaled_mm, with workspace [workspace_bytes] (device, 16-byte
+ * aligned).  Errors: those of q8_scaled_mm; Q8_EINVAL when a workspace is
+ * needed and workspace is NULL or workspace_bytes < q8_workspace_bytes(M,
+ * N, K); Q8_EUNSUPPORTED when it is misaligned. */
+q8_status q8_scaled_mm_ws(const int8_t *a, int64_t lda, const int8_t *b,
+                          int64_t ldb, const float *scale_tok,
+                          const float *scale_ch, q8_bf16 *c, int64_t ldc,
+                          int64_t M, int64_t N, int64_t K, void *workspace,
+                          int64_t workspace_bytes, q8_stream stream);
+
+/* As q8_quant_scaled_mm (the whole layer in one call), with a workspace as
+ * q8_scaled_mm_ws. */
+q8_status q8_quant_scaled_mm_ws(const q8_bf16 *x, int64_t ldx,
+                                const int8_t *b, int64_t ldb,
+                                const float *scale_ch, q8_bf16 *c,
+                                int64_t ldc, int8_t *xq, float *scale_tok,
+                                int64_t M, int64_t N, int64_t K,
+                                void *workspace, int64_t workspace_bytes,
+                                q8_stream stream);
+
+/* As w8a16_mm, with a workspace as q8_scaled_mm_ws. */
+q8_status w8a16_mm_ws(const q8_bf16 *x, int64_t ldx, const int8_t *w,
+                      int64_t ldw, const float *scale_ch, q8_bf16 *c,
+                      int64_t ldc, int64_t M, int64_t N, int64_t K,
+                      void *workspace, int64_t workspace_bytes,
+                      q8_stream stream);
+
+/* ------------------------------------------------------------------------
  * q8_quant_weight -- offline symmetric INT8 weight quantization of an fp32
  * weight W [N,K]: one scale per (row, contiguous span of `group` columns),
  *   scale[n*(K/group) + g] = absmax(span) / 127   (correctly rounded)

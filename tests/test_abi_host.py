@@ -161,3 +161,57 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros((4, 256), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         q8.q8_quant_per_token(x)
+
+
+def test_workspace_bytes_rule(lib):
+    """K is split only between the few-token kernels and the large tiles,
+    and the workspace never exceeds 480 tiles of 128 x 128 int32 values
+    (30 MiB): checked over the model's shapes and 1-16384 tokens."""
+    wb = lib.q8_workspace_bytes
+    assert wb(0, 5120, 5120) == 0 and wb(-1, 16, 128) == 0
+    for M in (1, 8, 32, 64):
+        assert wb(M, 5120, 5120) == 0            # the streaming kernels
+    assert wb(8192, 15360, 5120) == 0            # the large tiles
+    seen = 0
+    for N, K in ((5120, 5120), (15360, 5120), (17408, 5120), (5120, 17408), (5120, 13824)):
+        for M in list(range(65, 1025, 7)) + [2048, 4096, 8192, 16384]:
+            b = wb(M, N, K)
+            assert 0 <= b <= 480 * 128 * 128 * 4
+            if b:
+                ks = b // (4 * M * N)
+                assert b == ks * 4 * M * N and 2 <= ks <= 10
+                seen += 1
+    assert seen > 100
+    assert wb(128, 5120, 5120) == 6 * 128 * 5120 * 4   # 40 tiles: 6 splits of 896 (5 x 896 + 640)
+
+
+def test_workspace_validation(lib):
+    """A call that needs a workspace rejects a missing or short one with
+    Q8_EINVAL and a misaligned one with Q8_EUNSUPPORTED, before any HIP
+    call; when none is needed, NULL is accepted.  Covers every size the
+    removed split-K prototype's script swept (ks up to 12 at N = 15360,
+    M <= 512), where a fixed 256 MiB buffer was too short for 9-12 planes
+    of 512 x 15360 int32 values: the
+    library now sizes the planes itself and refuses a short workspace."""
+    M, N, K = 128, 5120, 5120
+    need = lib.q8_workspace_bytes(M, N, K)
+    assert need > 0
+    W = 0x50000
+    for fn, args in (
+            (lib.q8_scaled_mm_ws, (A, K, B, K, S, S, C, N, M, N, K)),
+            (lib.q8_quant_scaled_mm_ws, (A, K, B, K, S, C, N, A, S, M, N, K)),
+            (lib.w8a16_mm_ws, (A, K, B, K, S, C, N, M, N, K))):
+        assert fn(*args, None, need, None) == EINVAL
+        assert fn(*args, W, need - 1, None) == EINVAL
+        assert fn(*args, W + 8, need, None) == EUNSUP
+        assert fn(*args[:-3], 0, N, K, None, 0, None) == OK   # M = 0: nothing to do
+    # no split at M = 32: no workspace needed, NULL accepted (validation
+    # passes; with fake pointers the call is not made here)
+    assert lib.q8_workspace_bytes(32, N, K) == 0
+    # the old prototype's sweep: 256 MiB against the planes it wrote
+    old = 64 << 20 << 2
+    short = [(m, ks) for m in (65, 128, 256, 512) for ks in range(2, 13)
+             if ks * m * 15360 * 4 > old]
+    assert short == [(512, ks) for ks in range(9, 13)]   # what overran it
+    for m in (65, 128, 256, 512):
+        assert lib.q8_workspace_bytes(m, 15360, 5120) <= 480 * 128 * 128 * 4 < old

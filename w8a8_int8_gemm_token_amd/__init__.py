@@ -21,6 +21,8 @@ Functions mirror the C entry points:
   q8_quant_fp8_per_group128(x) -> (xq float8_e4m3fn, scale_grp)
   q8_quant_weight_fp8_block128(w) -> (wq float8_e4m3fn, scale_blk)
   q8_fp8_block_scaled_mm(xq, wq, scale_x, scale_w) -> y
+  q8_workspace_bytes(M, N, K) -> bytes; q8_scaled_mm_ws, q8_quant_scaled_mm_ws,
+  w8a16_mm_ws: the same with K split over a workspace (workspace=)
   ..._f16 variants of the per-token and per-group quantizers, q8_scaled_mm,
   q8_quant_scaled_mm, q8_scaled_mm_group128_act and w8a16_mm (fp16 in / out)
 Each also accepts preallocated outputs (``out=`` ...) so callers control
@@ -40,7 +42,8 @@ __all__ = [
     "q8_scaled_mm_group128_act", "q8_quant_fp8_per_group128", "q8_quant_weight_fp8_block128",
     "q8_fp8_block_scaled_mm", "q8_quant_per_token_f16", "q8_scaled_mm_f16",
     "q8_quant_scaled_mm_f16", "q8_quant_per_group128_f16", "q8_scaled_mm_group128_act_f16",
-    "w8a16_mm_f16", "EXPORTS", "MAX_K",
+    "w8a16_mm_f16", "q8_workspace_bytes", "q8_scaled_mm_ws", "q8_quant_scaled_mm_ws", "w8a16_mm_ws",
+    "EXPORTS", "MAX_K",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,7 +55,7 @@ EXPORTS = (
     "q8_scaled_mm_group128_act", "q8_quant_fp8_per_group128", "q8_quant_weight_fp8_block128",
     "q8_fp8_block_scaled_mm", "q8_quant_per_token_f16", "q8_scaled_mm_f16",
     "q8_quant_scaled_mm_f16", "q8_quant_per_group128_f16", "q8_scaled_mm_group128_act_f16",
-    "w8a16_mm_f16",
+    "w8a16_mm_f16", "q8_workspace_bytes", "q8_scaled_mm_ws", "q8_quant_scaled_mm_ws", "w8a16_mm_ws",
 )
 _STATUS = {0: "Q8_OK", 1: "Q8_EINVAL", 2: "Q8_EUNSUPPORTED", 3: "Q8_EHIP"}
 
@@ -105,6 +108,10 @@ def load():
         "q8_quant_per_group128_f16": ([P, I, P, I, P, I, I, P], S),
         "q8_scaled_mm_group128_act_f16": ([P, I, P, I, P, P, P, I, I, I, I, P], S),
         "w8a16_mm_f16": ([P, I, P, I, P, P, I, I, I, I, P], S),
+        "q8_workspace_bytes": ([I, I, I], I),
+        "q8_scaled_mm_ws": ([P, I, P, I, P, P, P, I, I, I, I, P, I, P], S),
+        "q8_quant_scaled_mm_ws": ([P, I, P, I, P, P, I, P, P, I, I, I, P, I, P], S),
+        "w8a16_mm_ws": ([P, I, P, I, P, P, I, I, I, I, P, I, P], S),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -274,6 +281,77 @@ def _quant_scaled_mm(name, dtype, x, b, scale_ch, out, xq_out, scale_tok_out):
         _ptr(x), _ld(x), _ptr(b), _ld(b), _ptr(scale_ch), _ptr(c), _ld(c),
         _ptr(xq), _ptr(st), M, N, K, _stream(x.device)))
     return c, xq, st
+
+
+def q8_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes the _ws entry points need for an (M, N, K) problem
+    (0 when they do not split K)."""
+    return int(load().q8_workspace_bytes(int(M), int(N), int(K)))
+
+
+def _workspace(M, N, K, device, workspace):
+    """The caller's workspace (any contiguous GPU tensor) and its size in
+    bytes, or one allocated with torch when the caller passes none."""
+    need = q8_workspace_bytes(M, N, K)
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty((need,), dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
+            or not workspace.is_contiguous():
+        raise ValueError("workspace: must be a contiguous GPU tensor")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def q8_scaled_mm_ws(a, b, scale_tok, scale_ch, out=None, workspace=None):
+    """As q8_scaled_mm, splitting K over a workspace where that is faster
+    (same bits as q8_scaled_mm)."""
+    M, N, K = _mk(a, b)
+    _dev(scale_tok, torch.float32, "scale_tok", 1)
+    _dev(scale_ch, torch.float32, "scale_ch", 1)
+    if scale_tok.numel() != M or scale_ch.numel() != N:
+        raise ValueError("scale sizes do not match M / N")
+    c = _gemm_out(M, N, a.device, out)
+    ws, nb = _workspace(M, N, K, a.device, workspace)
+    _check("q8_scaled_mm_ws", load().q8_scaled_mm_ws(
+        _ptr(a), _ld(a), _ptr(b), _ld(b), _ptr(scale_tok), _ptr(scale_ch),
+        _ptr(c), _ld(c), M, N, K, _ptr(ws), nb, _stream(a.device)))
+    return c
+
+
+def q8_quant_scaled_mm_ws(x, b, scale_ch, out=None, xq_out=None, scale_tok_out=None, workspace=None):
+    """As q8_quant_scaled_mm, splitting K over a workspace where that is
+    faster.  Returns (y, xq, scale_tok)."""
+    M, N, K = _mk(x, b, torch.bfloat16)
+    _dev(scale_ch, torch.float32, "scale_ch", 1)
+    if scale_ch.numel() != N:
+        raise ValueError("scale_ch size does not match N")
+    c = _gemm_out(M, N, x.device, out)
+    xq = xq_out if xq_out is not None else torch.empty((M, K), dtype=torch.int8, device=x.device)
+    st = scale_tok_out if scale_tok_out is not None else torch.empty((M,), dtype=torch.float32, device=x.device)
+    _dev(xq, torch.int8, "xq_out", 2)
+    if not xq.is_contiguous() or tuple(xq.shape) != (M, K):
+        raise ValueError("xq_out must be a contiguous [M, K] tensor")
+    _dev(st, torch.float32, "scale_tok_out", 1)
+    ws, nb = _workspace(M, N, K, x.device, workspace)
+    _check("q8_quant_scaled_mm_ws", load().q8_quant_scaled_mm_ws(
+        _ptr(x), _ld(x), _ptr(b), _ld(b), _ptr(scale_ch), _ptr(c), _ld(c),
+        _ptr(xq), _ptr(st), M, N, K, _ptr(ws), nb, _stream(x.device)))
+    return c, xq, st
+
+
+def w8a16_mm_ws(x, w, scale_ch, out=None, workspace=None):
+    """As w8a16_mm, splitting K over a workspace where that is faster."""
+    M, N, K = _mk(x, w, torch.bfloat16)
+    _dev(scale_ch, torch.float32, "scale_ch", 1)
+    if scale_ch.numel() != N:
+        raise ValueError("scale_ch size does not match N")
+    c = _gemm_out(M, N, x.device, out)
+    ws, nb = _workspace(M, N, K, x.device, workspace)
+    _check("w8a16_mm_ws", load().w8a16_mm_ws(
+        _ptr(x), _ld(x), _ptr(w), _ld(w), _ptr(scale_ch), _ptr(c), _ld(c),
+        M, N, K, _ptr(ws), nb, _stream(x.device)))
+    return c
 
 
 def q8_mm_i32(a, b, out=None):

@@ -22,6 +22,13 @@
 //                v_mfma_f32_32x32x16_bf16: y = bf16_rne(s_ch[n] * acc), acc
 //                the fp32 MFMA sum of x[m,k] * bf16(w[n,k])
 //   EPI_I32:     the raw int32 acc
+//   EPI_W16_PART, EPI_W16_PART_F16: EPI_W8A16 (bf16 or fp16 activations)
+//                without the scale: the raw fp32 acc
+// Split K: with p.kz > 0, workgroup row blockIdx.y sums only K elements
+// [blockIdx.y * kz, min(K, (blockIdx.y + 1) * kz)) and writes its raw
+// partial (EPI_I32, EPI_W16_PART*) to plane blockIdx.y, p.plane elements
+// after the previous one; a separate kernel sums the planes and applies the
+// epilogue.  Only these raw epilogues split.
 // "Qwen3.8-27B -- SmoothQuant + activation-aware GPTQ, W8A8 INT8 (v3)",
 // sections "Recipe" and "Serving" (INT8 x INT8 with per-token x per-channel
 // scales, bf16 out); "Qwen3.8-27B-GPTQ-INT8-W8A8-GS128", "Quantization
@@ -76,14 +83,16 @@
 namespace q8 {
 
 enum { EPI_I32 = 0, EPI_CHANNEL = 1, EPI_GROUP = 2, EPI_GROUP_ACT = 3, EPI_FP8_BLOCK = 4,
-       EPI_CHANNEL_F16 = 5, EPI_GROUP_ACT_F16 = 6, EPI_W8A16 = 7, EPI_W8A16_F16 = 8 };
+       EPI_CHANNEL_F16 = 5, EPI_GROUP_ACT_F16 = 6, EPI_W8A16 = 7, EPI_W8A16_F16 = 8,
+       EPI_W16_PART = 9, EPI_W16_PART_F16 = 10 };
 
 // The _F16 epilogues are EPI_CHANNEL, EPI_GROUP_ACT and EPI_W8A16 with fp16
 // outputs (EPI_W8A16_F16: fp16 activations as well).
 constexpr int epi_base(int e) {
     return e == EPI_CHANNEL_F16 ? EPI_CHANNEL
            : e == EPI_GROUP_ACT_F16 ? EPI_GROUP_ACT
-           : e == EPI_W8A16_F16 ? EPI_W8A16 : e;
+           : e == EPI_W8A16_F16 ? EPI_W8A16
+           : e == EPI_W16_PART_F16 ? EPI_W16_PART : e;
 }
 
 struct GemmArgs {
@@ -96,6 +105,8 @@ struct GemmArgs {
     void* c;             // [M, ldc] bf16 (fp16 for the _F16 epilogues) bits, or int32
     int64_t ldc;
     int M, N, K;
+    int kz;         // split K: K elements per workgroup row (blockIdx.y); 0 = all of K
+    int64_t plane;  // split K: elements between two partial planes of c
 };
 
 // s_waitcnt with vmcnt = N and lgkmcnt = 0 (expcnt untouched).
@@ -166,7 +177,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr bool W16 = EPI == EPI_W8A16;
+    constexpr bool W16 = EPI == EPI_W8A16 || EPI == EPI_W16_PART;
+    constexpr bool RAW = EPI == EPI_I32 || EPI == EPI_W16_PART;  // raw partial sums out
     // K elements per stage: 128 bytes of LDS row hold 128 codes or 64 bf16
     constexpr int KS = W16 ? 64 : 128;
     constexpr int XIW = BM / 8 / NW;                // 8-row direct loads per wave and stage
@@ -203,6 +215,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(16))) float ls1[LSN];
 
     const int M = p.M, N = p.N, K = p.K;
+    // this workgroup's K range (the whole of K unless K is split)
+    const int kz = RAW && p.kz > 0 ? p.kz : K;
+    const int kb = blockIdx.y * kz;
+    const int kn = min(kz, K - kb);
     const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
     const int id = xcd_remap(blockIdx.x, nbm * nbn);
     const int per_group = GM * nbn;
@@ -238,13 +254,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
 
     v4i wreg[W16 ? WLC : 1];
     auto issue = [&](int kt, int8_t* bx, int8_t* bw, float* bs) __attribute__((always_inline)) {
-        const int koff = kt * BK;
+        const int koff = kt * BK + (W16 ? 2 : 1) * kb;  // activation bytes
+        const int kwoff = kt * BK + kb;                  // int8 weight bytes (direct loads)
         if constexpr (W16) {  // first, so that a wait for them can leave the tile loads in flight
 #pragma unroll
             for (int i = 0; i < WLC; ++i) {
                 const int c = (int)threadIdx.x + i * NW * 64, r = c >> 2, q = c & 3;
                 wreg[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      wr, lane_offset((n0 + r) * (int)p.ldw + q * 16, kt * 64), 0, 0));
+                                                      wr, lane_offset((n0 + r) * (int)p.ldw + q * 16, kt * 64 + kb), 0, 0));
             }
         }
 #pragma unroll
@@ -256,7 +273,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
         for (int i = 0; i < WIW; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 wr, (Q8_LDS void*)(bw + (wid * WIW + i) * 1024), 16, lane_offset(wv[(wid * WIW + i) & 1],
-                ws0 + i * 8 * (int)p.ldw + koff), 0, 0, 0);
+                ws0 + i * 8 * (int)p.ldw + kwoff), 0, 0, 0);
         if constexpr (SGI > 0) {
 #pragma unroll
             for (int i = 0; i < (SGI + NW - 1) / NW; ++i) {
@@ -476,7 +493,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
         }
     };
 
-    const int KT = K / KS;
+    const int KT = kn / KS;
     issue(0, lx0, lw0, ls0);
     wait_vm_lgkm0<0>();
     wstore(lw0);
@@ -502,13 +519,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
             for (int g = 0; g < 4; ++g) {
                 const int ch = n0 + wn * WTN + b * 32 + g * 8 + hi * 4;
                 if (ch >= N) continue;
-                if constexpr (EPI == EPI_I32) {
+                if constexpr (RAW) {  // int32, or fp32 bits (EPI_W16_PART)
                     v4i o;
-                    o[0] = (int)acc[a][b][g * 4 + 0];
-                    o[1] = (int)acc[a][b][g * 4 + 1];
-                    o[2] = (int)acc[a][b][g * 4 + 2];
-                    o[3] = (int)acc[a][b][g * 4 + 3];
-                    *reinterpret_cast<v4i*>(static_cast<int32_t*>(p.c) + (int64_t)j * p.ldc + ch) = o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (EPI == EPI_I32) o[e] = acc[a][b][g * 4 + e];
+                        else o[e] = __float_as_int(acc[a][b][g * 4 + e]);
+                    }
+                    *reinterpret_cast<v4i*>(static_cast<int32_t*>(p.c) + (int64_t)blockIdx.y * p.plane +
+                                            (int64_t)j * p.ldc + ch) = o;
                 } else {
                     float v[4];
 #pragma unroll
@@ -546,7 +565,8 @@ inline bool gemm_offsets_fit(const GemmArgs& p) {
 template <int BM, int BN, int WM, int WN, int EPI, int GM>
 inline hipError_t launch_gemm_i8(const GemmArgs& p, hipStream_t stream) {
     const int nbm = (p.M + BM - 1) / BM, nbn = (p.N + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, EPI, GM>), dim3(nbm * nbn), dim3(WM * WN * 64),
+    const int ks = p.kz > 0 ? (p.K + p.kz - 1) / p.kz : 1;
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, EPI, GM>), dim3(nbm * nbn, ks), dim3(WM * WN * 64),
                        0, stream, p);
     return hipGetLastError();
 }

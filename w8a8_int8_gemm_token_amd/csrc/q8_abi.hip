@@ -15,6 +15,7 @@
 #include "gemm_w16.hpp"
 #include "stream_gemm.hpp"
 #include "fp8.hpp"
+#include "splitk.hpp"
 
 namespace {
 
@@ -140,6 +141,70 @@ hipError_t run_gemm_fp8_block(const GemmArgs& p, hipStream_t s) {
 
 hipError_t run_gemm_group(const GemmArgs& p, hipStream_t s) { return run_gemm_grouped<EPI_GROUP>(p, s); }
 
+// ---- split K (caller workspace) ----------------------------------------
+// Between the few-token kernels and the large tiles the tiled grid has too
+// few tiles to fill 256 CUs.  With a workspace the GEMM then runs on
+// 128 x 128 tiles with K split ks ways, ks = 480 / tiles (at most 10, and K
+// at least 768 per split), so that about 240-480 workgroups run; measured
+// over 65-512 tokens at N = 5120, 15360, 17408 (K = 5120) and the W8A16
+// shapes 5120 x 17408 and 5120 x 13824, this picked the fastest of 21
+// (tile, ks) pairs or one within 10% of it, 1.0-3.5x faster than the
+// unsplit route.  Since ks * tiles <= 480 and a tile covers at most
+// 128 x 128 outputs, the planes never need more than 480 * 128 * 128 * 4
+// bytes (30 MiB).
+struct SplitPlan {
+    int ks = 1;         // planes (1: no split)
+    int kz = 0;         // K elements per split, a multiple of 128
+    int64_t bytes = 0;  // workspace: ks planes of [M][N] 4-byte partial sums
+};
+
+inline SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
+    SplitPlan sp;
+    if (M <= SG_MAX_M || N <= 0 || K < 256) return sp;  // few tokens: the streaming kernels
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    int64_t ks = 480 / tiles;
+    if (ks > 10) ks = 10;
+    if (ks > K / 768) ks = K / 768;
+    if (ks < 2) return sp;
+    int64_t kz = (K + ks - 1) / ks;
+    kz = (kz + 127) / 128 * 128;
+    const int64_t ksr = (K + kz - 1) / kz;
+    if (ksr < 2) return sp;
+    sp.ks = (int)ksr;
+    sp.kz = (int)kz;
+    sp.bytes = ksr * M * N * 4;
+    return sp;
+}
+
+// Workspace argument check: none needed -> anything (NULL included) is
+// accepted; else non-null, at least `need` bytes (Q8_EINVAL) and 16-byte
+// aligned (Q8_EUNSUPPORTED).
+inline q8_status check_ws(const void* ws, int64_t ws_bytes, int64_t need) {
+    if (need == 0) return Q8_OK;
+    if (ws == nullptr || ws_bytes < need) return Q8_EINVAL;
+    return al(ws, 16) ? Q8_OK : Q8_EUNSUPPORTED;
+}
+
+// The tiled kernel over ks K ranges into the workspace planes, then the
+// reduction with the epilogue into p.c.  W16: the W8A16 mode (p.x bf16 or
+// fp16 addressed in bytes); F16: fp16 activations (W16) and outputs.
+template <bool W16, bool F16>
+hipError_t run_split(const GemmArgs& p, const SplitPlan& sp, void* ws, hipStream_t s) {
+    GemmArgs q = p;
+    q.c = ws;
+    q.ldc = p.N;
+    q.kz = sp.kz;
+    q.plane = (int64_t)p.M * p.N;
+    hipError_t e;
+    if constexpr (W16)
+        e = launch_gemm_i8<128, 128, 2, 2, F16 ? EPI_W16_PART_F16 : EPI_W16_PART, 8>(q, s);
+    else
+        e = launch_gemm_i8<128, 128, 2, 2, EPI_I32, 8>(q, s);
+    if (e != hipSuccess) return e;
+    return launch_splitk_reduce<W16 ? 1 : 0, F16>(static_cast<const int32_t*>(ws), sp.ks, q.plane, p.s_tok,
+                                                    p.s_w, static_cast<uint16_t*>(p.c), p.ldc, p.M, p.N, s);
+}
+
 template <bool F16>
 hipError_t run_quant(const uint16_t* x, int64_t ldx, int8_t* xq, int64_t ldxq, float* s, int M,
                      int K, hipStream_t stream) {
@@ -204,6 +269,42 @@ q8_status quant_scaled_mm_impl(const uint16_t* x, int64_t ldx, const int8_t* b, 
     if (e != hipSuccess) return Q8_EHIP;
     GemmArgs p{xq, K, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};
     return hip_status(run_gemm_i8<F16 ? EPI_CHANNEL_F16 : EPI_CHANNEL>(p, s));
+}
+
+template <bool F16>
+q8_status scaled_mm_ws_impl(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
+                            const float* scale_tok, const float* scale_ch, uint16_t* c, int64_t ldc,
+                            int64_t M, int64_t N, int64_t K, void* ws, int64_t ws_bytes, q8_stream stream) {
+    q8_status r = check_gemm(a, lda, 16, b, ldb, c, ldc, 8, M, N, K);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_tok);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_ch);
+    const SplitPlan sp = r == Q8_OK && M > 0 ? split_plan(M, N, K) : SplitPlan{};
+    if (r == Q8_OK && M > 0) r = check_ws(ws, ws_bytes, sp.bytes);
+    if (r != Q8_OK || M == 0) return r;
+    GemmArgs p{a, lda, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};
+    if (sp.ks > 1 && gemm_offsets_fit(p)) return hip_status(run_split<false, F16>(p, sp, ws, st(stream)));
+    return hip_status(run_gemm_i8<F16 ? EPI_CHANNEL_F16 : EPI_CHANNEL>(p, st(stream)));
+}
+
+template <bool F16>
+q8_status quant_scaled_mm_ws_impl(const uint16_t* x, int64_t ldx, const int8_t* b, int64_t ldb,
+                                  const float* scale_ch, uint16_t* c, int64_t ldc, int8_t* xq,
+                                  float* scale_tok, int64_t M, int64_t N, int64_t K, void* ws,
+                                  int64_t ws_bytes, q8_stream stream) {
+    q8_status r = check_gemm(x, ldx, 8, b, ldb, c, ldc, 8, M, N, K);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_ch);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_tok);
+    if (r == Q8_OK && M > 0 && !xq) r = Q8_EINVAL;
+    if (r == Q8_OK && M > 0 && !al(xq, 16)) r = Q8_EUNSUPPORTED;
+    const SplitPlan sp = r == Q8_OK && M > 0 ? split_plan(M, N, K) : SplitPlan{};
+    if (r == Q8_OK && M > 0) r = check_ws(ws, ws_bytes, sp.bytes);
+    if (r != Q8_OK || M == 0) return r;
+    GemmArgs p{xq, K, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};
+    if (sp.ks < 2 || !gemm_offsets_fit(p))
+        return quant_scaled_mm_impl<F16>(x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok, M, N, K, stream);
+    hipStream_t s = st(stream);
+    if (run_quant<F16>(x, ldx, xq, K, scale_tok, (int)M, (int)K, s) != hipSuccess) return Q8_EHIP;
+    return hip_status(run_split<false, F16>(p, sp, ws, s));
 }
 
 template <bool F16>
@@ -348,6 +449,22 @@ q8_status w8a16_impl(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ld
     if (220 * w320 < 100 * w128 && gemm_w16_offsets_fit(p)) return hip_status(launch_gemm_w16<F16>(p, st(stream)));
     return hip_status(launch_gemm_i8<256, 128, 4, 2, E, 8>(p, st(stream)));
 }
+
+template <bool F16>
+q8_status w8a16_ws_impl(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ldw, const float* scale_ch,
+                        uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* ws, int64_t ws_bytes,
+                        q8_stream stream) {
+    q8_status r = check_gemm(x, ldx, 8, w, ldw, c, ldc, 8, M, N, K);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_ch);
+    const SplitPlan sp = r == Q8_OK && M > 0 ? split_plan(M, N, K) : SplitPlan{};
+    if (r == Q8_OK && M > 0) r = check_ws(ws, ws_bytes, sp.bytes);
+    if (r != Q8_OK || M == 0) return r;
+    GemmArgs p{reinterpret_cast<const int8_t*>(x), 2 * ldx, w, ldw, nullptr, scale_ch, c, ldc,
+               (int)M, (int)N, (int)K};
+    if (sp.ks < 2 || !gemm_offsets_fit(p))
+        return w8a16_impl<F16>(x, ldx, w, ldw, scale_ch, c, ldc, M, N, K, stream);
+    return hip_status(run_split<true, F16>(p, sp, ws, st(stream)));
+}
 }  // namespace
 
 extern "C" {
@@ -482,6 +599,33 @@ q8_status q8_quant_weight_fp8_block128(const float* w, int64_t ldw, uint8_t* wq,
     hipLaunchKernelGGL(quant_weight_fp8_block_kernel, dim3((unsigned)blocks), dim3(256), 0, st(stream),
                        w, ldw, wq, ldwq, scale_blk, (int)(K / 128));
     return hip_status(hipGetLastError());
+}
+
+int64_t q8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return split_plan(M, N, K).bytes;
+}
+
+q8_status q8_scaled_mm_ws(const int8_t* a, int64_t lda, const int8_t* b, int64_t ldb,
+                          const float* scale_tok, const float* scale_ch, q8_bf16* c, int64_t ldc,
+                          int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                          q8_stream stream) {
+    return scaled_mm_ws_impl<false>(a, lda, b, ldb, scale_tok, scale_ch, c, ldc, M, N, K, workspace,
+                                    workspace_bytes, stream);
+}
+
+q8_status q8_quant_scaled_mm_ws(const q8_bf16* x, int64_t ldx, const int8_t* b, int64_t ldb,
+                                const float* scale_ch, q8_bf16* c, int64_t ldc, int8_t* xq,
+                                float* scale_tok, int64_t M, int64_t N, int64_t K, void* workspace,
+                                int64_t workspace_bytes, q8_stream stream) {
+    return quant_scaled_mm_ws_impl<false>(x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok, M, N, K, workspace,
+                                          workspace_bytes, stream);
+}
+
+q8_status w8a16_mm_ws(const q8_bf16* x, int64_t ldx, const int8_t* w, int64_t ldw, const float* scale_ch,
+                      q8_bf16* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
+                      int64_t workspace_bytes, q8_stream stream) {
+    return w8a16_ws_impl<false>(x, ldx, w, ldw, scale_ch, c, ldc, M, N, K, workspace, workspace_bytes, stream);
 }
 
 q8_status q8_fp8_block_scaled_mm(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb,
