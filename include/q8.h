@@ -236,6 +236,32 @@ q8_status w8a16_mm_ws(const q8_bf16 *x, int64_t ldx, const int8_t *w,
                       q8_stream stream);
 
 /* ------------------------------------------------------------------------
+ * q8_quant_scaled_mm_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): q8_quant_scaled_mm_ws with the library's own
+ * workspace, a device array of Q8_NOALLOC_MAX_WORKSPACE bytes that each
+ * GPU holds from the time the library is loaded there until the process
+ * ends.  Same arguments, result and errors as q8_quant_scaled_mm (the
+ * caller still passes the output, xq and scale_tok buffers), plus
+ * Q8_EUNSUPPORTED when the problem would need more than that workspace
+ * (never for the library's current split rule, whose largest need is 30
+ * MiB) and Q8_EHIP when HIP refuses the lookup of the array's address.
+ * It calls no allocating routine: the first call on a device looks up the
+ * array's device address (hipGetSymbolAddress) and keeps it.  Every call on
+ * one GPU uses that GPU's one array, which holds the last call's partial
+ * sums (each call writes every value it reads, so nothing needs clearing):
+ * calls that overlap on one GPU (different streams) race; order them.
+ * ---------------------------------------------------------------------- */
+#define Q8_NOALLOC_MAX_WORKSPACE ((int64_t)32 << 20)
+
+q8_status q8_quant_scaled_mm_noalloc(const q8_bf16 *x, int64_t ldx,
+                                     const int8_t *b, int64_t ldb,
+                                     const float *scale_ch, q8_bf16 *c,
+                                     int64_t ldc, int8_t *xq,
+                                     float *scale_tok, int64_t M, int64_t N,
+                                     int64_t K, q8_stream stream);
+
+/* ------------------------------------------------------------------------
  * q8_quant_weight -- offline symmetric INT8 weight quantization of an fp32
  * weight W [N,K]: one scale per (row, contiguous span of `group` columns),
  *   scale[n*(K/group) + g] = absmax(span) / 127   (correctly rounded)

@@ -22,7 +22,8 @@ Functions mirror the C entry points:
   q8_quant_weight_fp8_block128(w) -> (wq float8_e4m3fn, scale_blk)
   q8_fp8_block_scaled_mm(xq, wq, scale_x, scale_w) -> y
   q8_workspace_bytes(M, N, K) -> bytes; q8_scaled_mm_ws, q8_quant_scaled_mm_ws,
-  w8a16_mm_ws: the same with K split over a workspace (workspace=)
+  w8a16_mm_ws: the same with K split over a workspace (workspace=);
+  q8_quant_scaled_mm_noalloc: the layer with the library's own workspace
   ..._f16 variants of the per-token and per-group quantizers, q8_scaled_mm,
   q8_quant_scaled_mm, q8_scaled_mm_group128_act and w8a16_mm (fp16 in / out)
 Each also accepts preallocated outputs (``out=`` ...) so callers control
@@ -43,11 +44,12 @@ __all__ = [
     "q8_fp8_block_scaled_mm", "q8_quant_per_token_f16", "q8_scaled_mm_f16",
     "q8_quant_scaled_mm_f16", "q8_quant_per_group128_f16", "q8_scaled_mm_group128_act_f16",
     "w8a16_mm_f16", "q8_workspace_bytes", "q8_scaled_mm_ws", "q8_quant_scaled_mm_ws", "w8a16_mm_ws",
-    "EXPORTS", "MAX_K",
+    "q8_quant_scaled_mm_noalloc", "NOALLOC_MAX_WORKSPACE", "EXPORTS", "MAX_K",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 MAX_K = 130944
+NOALLOC_MAX_WORKSPACE = 32 << 20  # bytes of the allocation-free variant's own workspace
 EXPORTS = (
     "q8_status_str", "q8_quant_per_token", "q8_scaled_mm",
     "q8_scaled_mm_group128", "w8a16_mm", "q8_quant_scaled_mm", "q8_mm_i32",
@@ -56,6 +58,7 @@ EXPORTS = (
     "q8_fp8_block_scaled_mm", "q8_quant_per_token_f16", "q8_scaled_mm_f16",
     "q8_quant_scaled_mm_f16", "q8_quant_per_group128_f16", "q8_scaled_mm_group128_act_f16",
     "w8a16_mm_f16", "q8_workspace_bytes", "q8_scaled_mm_ws", "q8_quant_scaled_mm_ws", "w8a16_mm_ws",
+    "q8_quant_scaled_mm_noalloc",
 )
 _STATUS = {0: "Q8_OK", 1: "Q8_EINVAL", 2: "Q8_EUNSUPPORTED", 3: "Q8_EHIP"}
 
@@ -112,6 +115,7 @@ def load():
         "q8_scaled_mm_ws": ([P, I, P, I, P, P, P, I, I, I, I, P, I, P], S),
         "q8_quant_scaled_mm_ws": ([P, I, P, I, P, P, I, P, P, I, I, I, P, I, P], S),
         "w8a16_mm_ws": ([P, I, P, I, P, P, I, I, I, I, P, I, P], S),
+        "q8_quant_scaled_mm_noalloc": ([P, I, P, I, P, P, I, P, P, I, I, I, P], S),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -256,6 +260,14 @@ def q8_quant_scaled_mm(x, b, scale_ch, out=None, xq_out=None, scale_tok_out=None
     """The whole W8A8 layer: per-token quant of x, then the scaled INT8 GEMM.
     Returns (y bf16 [M,N], xq int8 [M,K], scale_tok fp32 [M])."""
     return _quant_scaled_mm("q8_quant_scaled_mm", torch.bfloat16, x, b, scale_ch, out, xq_out,
+                            scale_tok_out)
+
+
+def q8_quant_scaled_mm_noalloc(x, b, scale_ch, out, xq_out, scale_tok_out):
+    """As q8_quant_scaled_mm_ws with the library's own workspace: for callers
+    that cannot allocate (all outputs are the caller's tensors; nothing is
+    allocated here or in the library).  Returns (y, xq, scale_tok)."""
+    return _quant_scaled_mm("q8_quant_scaled_mm_noalloc", torch.bfloat16, x, b, scale_ch, out, xq_out,
                             scale_tok_out)
 
 

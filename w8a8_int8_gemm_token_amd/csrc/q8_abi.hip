@@ -6,6 +6,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "gemm_i8.hpp"
 #include "quant.hpp"
 #include "decode_fused.hpp"
@@ -337,6 +340,45 @@ q8_status scaled_mm_group128_act_impl(const int8_t* a, int64_t lda, const int8_t
     return hip_status(run_gemm_group_act<F16 ? EPI_GROUP_ACT_F16 : EPI_GROUP_ACT>(p, st(stream)));
 }
 
+// ---- the allocation-free variant's workspace ---------------------------
+// A file-scope device array stands in for the caller's workspace in
+// q8_quant_scaled_mm_noalloc.  Every GPU the library runs on holds its own
+// copy from the time the library is loaded there until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory:
+// its device address comes from hipGetSymbolAddress, looked up once per
+// device with that device current and kept in scratch_ptr.
+constexpr int64_t SCRATCH_BYTES = Q8_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) int32_t scratch[SCRATCH_BYTES / 4];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> scratch_ptr[MAX_DEVICES];
+std::mutex scratch_mutex;
+
+// Device address of this device's scratch array (the device `stream`
+// belongs to), or nullptr if HIP refuses the lookup.
+void* device_scratch(hipStream_t stream) {
+    int dev = -1;
+    if (stream != nullptr) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return nullptr;
+    }
+    if (dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p != nullptr) return p;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    p = scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p != nullptr) return p;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return nullptr;
+    scratch_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -599,6 +641,24 @@ q8_status q8_quant_weight_fp8_block128(const float* w, int64_t ldw, uint8_t* wq,
     hipLaunchKernelGGL(quant_weight_fp8_block_kernel, dim3((unsigned)blocks), dim3(256), 0, st(stream),
                        w, ldw, wq, ldwq, scale_blk, (int)(K / 128));
     return hip_status(hipGetLastError());
+}
+
+q8_status q8_quant_scaled_mm_noalloc(const q8_bf16* x, int64_t ldx, const int8_t* b, int64_t ldb,
+                                     const float* scale_ch, q8_bf16* c, int64_t ldc, int8_t* xq,
+                                     float* scale_tok, int64_t M, int64_t N, int64_t K, q8_stream stream) {
+    // the checks of q8_quant_scaled_mm_ws, before any HIP call
+    q8_status r = check_gemm(x, ldx, 8, b, ldb, c, ldc, 8, M, N, K);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_ch);
+    if (r == Q8_OK && M > 0) r = check_scale(scale_tok);
+    if (r == Q8_OK && M > 0 && !xq) r = Q8_EINVAL;
+    if (r == Q8_OK && M > 0 && !al(xq, 16)) r = Q8_EUNSUPPORTED;
+    if (r != Q8_OK || M == 0) return r;
+    const int64_t need = split_plan(M, N, K).bytes;
+    if (need > SCRATCH_BYTES) return Q8_EUNSUPPORTED;
+    void* ws = nullptr;
+    if (need > 0 && (ws = device_scratch(st(stream))) == nullptr) return Q8_EHIP;
+    return quant_scaled_mm_ws_impl<false>(x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok, M, N, K, ws,
+                                          need > 0 ? SCRATCH_BYTES : 0, stream);
 }
 
 int64_t q8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
