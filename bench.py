@@ -590,6 +590,19 @@ def f16_layer(dev, iters=20):
     ms = events_time(f, iters)
     ops = 2.0 * wl.M * wl.N * wl.K
     out = {"prefill": {"us": ms * 1e3, "TOPS": ops / (ms * 1e-3) / 1e12}}
+    # the per-token quantizer alone, fp16 and bf16 rows side by side, at the
+    # prefill width (10 chunks of 8 values per lane) and at K = 4096 (8)
+    quant = {}
+    for Kq in (wl.K, 4096):
+        xh = x[:, :Kq].contiguous()
+        xb = xh.to(torch.bfloat16)
+        xq_ = torch.empty((wl.M, Kq), dtype=torch.int8, device=dev)
+        for name, xx, fn in (("f16", xh, q8.q8_quant_per_token_f16), ("bf16", xb, q8.q8_quant_per_token)):
+            qms = call_stats(lambda: fn(xx, out=xq_, scale_out=st), iters)["mean"]
+            nb = 3 * wl.M * Kq + 4 * wl.M
+            quant[f"{name}_K{Kq}"] = {"us": qms * 1e3, "GB/s": nb / (qms * 1e-3) / 1e9}
+        del xh, xb, xq_
+    out["quant_per_token"] = dict(quant, timing="back to back, rows left in the last-level cache")
     del y, xq, st, wq, sc, x
     dw = synth.WORKLOADS["decode"]
     w = synth.weights(dw, 0).to(dev)

@@ -182,6 +182,21 @@ q8_status q8_mm_i32(const int8_t *a, int64_t lda, const int8_t *b,
                     int64_t N, int64_t K, q8_stream stream);
 
 /* ------------------------------------------------------------------------
+ * q8_wait_timeouts -- diagnostics of the few-token weight-streaming kernel
+ * (q8_scaled_mm, q8_quant_scaled_mm and w8a16_mm at up to 64 tokens, and in
+ * two passes up to 128).  Its waves hand weight segments over through
+ * counters in on-chip memory; every wait on them is bounded (about 2^20
+ * polls), so a broken hand-over gives a wrong result instead of a hung
+ * device, and each wait that gives up adds one to a per-device count.
+ * This call waits for the current device to finish its work
+ * (hipDeviceSynchronize), stores that device's count in *count and, with
+ * reset nonzero, sets it back to 0.  The count is 0 in correct operation.
+ * Errors: Q8_EINVAL for a NULL count; Q8_EHIP if HIP refuses the
+ * synchronization or the copy.  Not for hot paths: it synchronizes.
+ * ---------------------------------------------------------------------- */
+q8_status q8_wait_timeouts(uint32_t *count, int reset);
+
+/* ------------------------------------------------------------------------
  * Split K with a caller workspace.  Between the few-token kernels and the
  * large tiles (roughly 65-512 tokens at the model's shapes) the output has
  * too few tiles to keep 256 compute units busy.  The _ws entry points then

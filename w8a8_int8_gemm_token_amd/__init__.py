@@ -44,7 +44,7 @@ __all__ = [
     "q8_fp8_block_scaled_mm", "q8_quant_per_token_f16", "q8_scaled_mm_f16",
     "q8_quant_scaled_mm_f16", "q8_quant_per_group128_f16", "q8_scaled_mm_group128_act_f16",
     "w8a16_mm_f16", "q8_workspace_bytes", "q8_scaled_mm_ws", "q8_quant_scaled_mm_ws", "w8a16_mm_ws",
-    "q8_quant_scaled_mm_noalloc", "NOALLOC_MAX_WORKSPACE", "EXPORTS", "MAX_K",
+    "q8_quant_scaled_mm_noalloc", "q8_wait_timeouts", "NOALLOC_MAX_WORKSPACE", "EXPORTS", "MAX_K",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,7 +58,7 @@ EXPORTS = (
     "q8_fp8_block_scaled_mm", "q8_quant_per_token_f16", "q8_scaled_mm_f16",
     "q8_quant_scaled_mm_f16", "q8_quant_per_group128_f16", "q8_scaled_mm_group128_act_f16",
     "w8a16_mm_f16", "q8_workspace_bytes", "q8_scaled_mm_ws", "q8_quant_scaled_mm_ws", "w8a16_mm_ws",
-    "q8_quant_scaled_mm_noalloc",
+    "q8_quant_scaled_mm_noalloc", "q8_wait_timeouts",
 )
 _STATUS = {0: "Q8_OK", 1: "Q8_EINVAL", 2: "Q8_EUNSUPPORTED", 3: "Q8_EHIP"}
 
@@ -116,6 +116,7 @@ def load():
         "q8_quant_scaled_mm_ws": ([P, I, P, I, P, P, I, P, P, I, I, I, P, I, P], S),
         "w8a16_mm_ws": ([P, I, P, I, P, P, I, I, I, I, P, I, P], S),
         "q8_quant_scaled_mm_noalloc": ([P, I, P, I, P, P, I, P, P, I, I, I, P], S),
+        "q8_wait_timeouts": ([P, S], S),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -293,6 +294,15 @@ def _quant_scaled_mm(name, dtype, x, b, scale_ch, out, xq_out, scale_tok_out):
         _ptr(x), _ld(x), _ptr(b), _ld(b), _ptr(scale_ch), _ptr(c), _ld(c),
         _ptr(xq), _ptr(st), M, N, K, _stream(x.device)))
     return c, xq, st
+
+
+def q8_wait_timeouts(reset: bool = False) -> int:
+    """Waits of the weight-streaming kernel that gave up on the current
+    device since the library was loaded (0 in correct operation).
+    Synchronizes the device."""
+    n = ctypes.c_uint32(0)
+    _check("q8_wait_timeouts", load().q8_wait_timeouts(ctypes.byref(n), int(bool(reset))))
+    return int(n.value)
 
 
 def q8_workspace_bytes(M: int, N: int, K: int) -> int:

@@ -661,6 +661,19 @@ q8_status q8_quant_scaled_mm_noalloc(const q8_bf16* x, int64_t ldx, const int8_t
                                           need > 0 ? SCRATCH_BYTES : 0, stream);
 }
 
+q8_status q8_wait_timeouts(uint32_t* count, int reset) {
+    if (count == nullptr) return Q8_EINVAL;
+    if (hipDeviceSynchronize() != hipSuccess) return Q8_EHIP;
+    unsigned int v = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(sg_wait_timeouts), sizeof v) != hipSuccess) return Q8_EHIP;
+    *count = v;
+    if (reset && v != 0) {
+        const unsigned int zero = 0;
+        if (hipMemcpyToSymbol(HIP_SYMBOL(sg_wait_timeouts), &zero, sizeof zero) != hipSuccess) return Q8_EHIP;
+    }
+    return Q8_OK;
+}
+
 int64_t q8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
     return split_plan(M, N, K).bytes;

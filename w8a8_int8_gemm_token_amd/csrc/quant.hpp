@@ -154,15 +154,18 @@ __global__ __launch_bounds__(256) void quant_per_token_reg(
     v2h mx = v2h{0, 0};
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-        const int c = lane + 64 * i;
-        if (c < nch) {
-            // Streaming (non-temporal) load: the row is read once.  With X in
-            // HBM (as after a large GEMM) this quantizer takes 33 us instead
-            // of 43 at 8192 x 5120; with X still in the last-level cache it
-            // takes 31 instead of 27, since these loads do not keep it there.
-            v[i] = __builtin_nontemporal_load(&xr[c]);
-            mx = mag_max8(mx, v[i]);
-        }
+        // Chunks past the row end load the row's last chunk again: its
+        // values are in the row, so the absmax is unchanged, and the loop
+        // has no branch (a conditional load made the compiler copy the
+        // whole register array at every step in the fp16 instances: 246
+        // registers instead of 59 at NC = 8).
+        const int c = min(lane + 64 * i, nch - 1);
+        // Streaming (non-temporal) load: the row is read once.  With X in
+        // HBM (as after a large GEMM) this quantizer takes 33 us instead
+        // of 43 at 8192 x 5120; with X still in the last-level cache it
+        // takes 31 instead of 27, since these loads do not keep it there.
+        v[i] = __builtin_nontemporal_load(&xr[c]);
+        mx = mag_max8(mx, v[i]);
     }
     const float a = wave_max(mag_to_f32<F16>(mx));
     const RowScale q = row_scale(a);

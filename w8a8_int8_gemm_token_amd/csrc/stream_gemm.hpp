@@ -83,19 +83,26 @@ __host__ __device__ inline size_t sg_lds_bytes(int rows, int nbuf, int mg) {
     return ring > red ? ring : red;
 }
 
+// Waits of the streaming kernel that gave up (see sg_wait_ge), counted per
+// device since the library was loaded there; q8_wait_timeouts reads it.
+__device__ unsigned int sg_wait_timeouts;
+
 // Spin (short sleeps) until an LDS counter reaches target; bounded (about
 // 2^20 polls, tens of milliseconds) so a broken invariant gives wrong
-// output, not a hung device.  The poll is a ds_read written out (and waited
-// for inside the same statement): a compiler-visible LDS read would first
-// drain the loading waves' in-flight direct loads.
+// output, not a hung device -- and a count in sg_wait_timeouts, so that
+// the wrong output does not pass unnoticed.  The poll is a ds_read written
+// out (and waited for inside the same statement): a compiler-visible LDS
+// read would first drain the loading waves' in-flight direct loads.
 __device__ __forceinline__ void sg_wait_ge(int* c, int target) {
     const uint32_t a = (uint32_t)(uintptr_t)(Q8_LDS int*)c;
-    for (int it = 0; it < (1 << 20); ++it) {
+    int it = 0;
+    for (; it < (1 << 20); ++it) {
         int v;
         asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
         if (__builtin_amdgcn_readfirstlane(v) >= target) break;
         __builtin_amdgcn_s_sleep(1);
     }
+    if (it == (1 << 20) && (threadIdx.x & 63) == 0) atomicAdd(&sg_wait_timeouts, 1u);
     asm volatile("" ::: "memory");
 }
 
