@@ -186,8 +186,9 @@ q8_status q8_mm_i32(const int8_t *a, int64_t lda, const int8_t *b,
  * (q8_scaled_mm, q8_quant_scaled_mm and w8a16_mm at up to 64 tokens, and in
  * two passes up to 128).  Its waves hand weight segments over through
  * counters in on-chip memory; every wait on them is bounded (about 2^20
- * polls), so a broken hand-over gives a wrong result instead of a hung
- * device, and each wait that gives up adds one to a per-device count.
+ * polls, some 30 ms), so a broken hand-over gives a wrong result instead of
+ * a hung device.  A wave that has run for more than 10 ms -- which no call
+ * takes unless a wait gave up -- adds one to a per-device count.
  * This call waits for the current device to finish its work
  * (hipDeviceSynchronize), stores that device's count in *count and, with
  * reset nonzero, sets it back to 0.  The count is 0 in correct operation.
@@ -198,7 +199,7 @@ q8_status q8_wait_timeouts(uint32_t *count, int reset);
 
 /* ------------------------------------------------------------------------
  * Split K with a caller workspace.  Between the few-token kernels and the
- * large tiles (roughly 65-512 tokens at the model's shapes) the output has
+ * large tiles (roughly 33-512 tokens at the model's shapes) the output has
  * too few tiles to keep 256 compute units busy.  The _ws entry points then
  * split K: ks workgroups per output tile each sum a contiguous K range into
  * a plane of the caller's workspace, and a second kernel adds the planes and
@@ -218,9 +219,11 @@ q8_status q8_wait_timeouts(uint32_t *count, int reset);
  * ---------------------------------------------------------------------- */
 
 /* Bytes of workspace the _ws entry points need for an (M, N, K) problem:
- * 0 when they would not split K (then the workspace may be NULL), else
- * ks * M * N * 4 for the library's split count ks (2 <= ks <= 10).  Never
- * more than 31,457,280 bytes (30 MiB).  Nonpositive sizes give 0. */
+ * 0 when none of them splits K at that size (then the workspace may be
+ * NULL), else ks * M * N * 4 for the library's split count ks (2 <= ks <=
+ * 10; at 33-64 tokens the W8A8 calls keep the weight-streaming kernel, and
+ * leave the workspace unused, where that kernel runs).  Never more than
+ * 31,457,280 bytes (30 MiB).  Nonpositive sizes give 0. */
 int64_t q8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* As q8_scaled_mm, with workspace [workspace_bytes] (device, 16-byte

@@ -147,24 +147,29 @@ hipError_t run_gemm_group(const GemmArgs& p, hipStream_t s) { return run_gemm_gr
 // ---- split K (caller workspace) ----------------------------------------
 // Between the few-token kernels and the large tiles the tiled grid has too
 // few tiles to fill 256 CUs.  With a workspace the GEMM then runs on
-// 128 x 128 tiles with K split ks ways, ks = 480 / tiles (at most 10, and K
-// at least 768 per split), so that about 240-480 workgroups run; measured
-// over 65-512 tokens at N = 5120, 15360, 17408 (K = 5120) and the W8A16
-// shapes 5120 x 17408 and 5120 x 13824, this picked the fastest of 21
-// (tile, ks) pairs or one within 10% of it, 1.0-3.5x faster than the
-// unsplit route.  Since ks * tiles <= 480 and a tile covers at most
-// 128 x 128 outputs, the planes never need more than 480 * 128 * 128 * 4
-// bytes (30 MiB).
+// BM x 128 tiles (BM = 64 up to 64 tokens, else 128) with K split ks ways,
+// ks = 480 / tiles (at most 10, and K at least 768 per split), so that
+// about 240-480 workgroups run.  Measured over 24-512 tokens at N = 5120,
+// 15360 and 17408 (K = 5120) and the W8A16 shapes 5120 x 17408 and
+// 5120 x 13824 against 21 (tile, ks) pairs, this rule picks the fastest
+// pair or one within 10% of it: 1.0-3.5x faster than the unsplit route
+// from 65 tokens, and from 33 tokens wherever that route would run the
+// tiled kernel (at 33-64 tokens the W8A8 weight-streaming kernel stays,
+// where it runs: within 5% of the split or faster).  Since ks * tiles <= 480
+// and a tile covers at most 128 x 128 outputs, the planes never need more
+// than 480 * 128 * 128 * 4 bytes (30 MiB).
 struct SplitPlan {
     int ks = 1;         // planes (1: no split)
     int kz = 0;         // K elements per split, a multiple of 128
+    int bm = 128;       // tokens per tile
     int64_t bytes = 0;  // workspace: ks planes of [M][N] 4-byte partial sums
 };
 
 inline SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
     SplitPlan sp;
-    if (M <= SG_MAX_M || N <= 0 || K < 256) return sp;  // few tokens: the streaming kernels
-    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (M <= 32 || N <= 0 || K < 256) return sp;  // few tokens: the streaming kernels
+    sp.bm = M <= 64 ? 64 : 128;
+    const int64_t tiles = ((M + sp.bm - 1) / sp.bm) * ((N + 127) / 128);
     int64_t ks = 480 / tiles;
     if (ks > 10) ks = 10;
     if (ks > K / 768) ks = K / 768;
@@ -177,6 +182,13 @@ inline SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
     sp.kz = (int)kz;
     sp.bytes = ksr * M * N * 4;
     return sp;
+}
+
+// The W8A8 route runs the weight-streaming kernel (one pass) at this size:
+// run_gemm_i8's own test for it.
+inline bool w8a8_streams(const GemmArgs& p) {
+    const bool few = p.M <= 32 || ((p.N + 127) / 128) * ((p.M + 31) / 32) < 128;
+    return few && sg_fits(p.M, p.N, p.K, p.ldw, SG_MAX_M);
 }
 
 // Workspace argument check: none needed -> anything (NULL included) is
@@ -198,11 +210,9 @@ hipError_t run_split(const GemmArgs& p, const SplitPlan& sp, void* ws, hipStream
     q.ldc = p.N;
     q.kz = sp.kz;
     q.plane = (int64_t)p.M * p.N;
-    hipError_t e;
-    if constexpr (W16)
-        e = launch_gemm_i8<128, 128, 2, 2, F16 ? EPI_W16_PART_F16 : EPI_W16_PART, 8>(q, s);
-    else
-        e = launch_gemm_i8<128, 128, 2, 2, EPI_I32, 8>(q, s);
+    constexpr int E = W16 ? (F16 ? EPI_W16_PART_F16 : EPI_W16_PART) : EPI_I32;
+    const hipError_t e = sp.bm == 64 ? launch_gemm_i8<64, 128, 2, 2, E, 8>(q, s)
+                                     : launch_gemm_i8<128, 128, 2, 2, E, 8>(q, s);
     if (e != hipSuccess) return e;
     return launch_splitk_reduce<W16 ? 1 : 0, F16>(static_cast<const int32_t*>(ws), sp.ks, q.plane, p.s_tok,
                                                     p.s_w, static_cast<uint16_t*>(p.c), p.ldc, p.M, p.N, s);
@@ -285,7 +295,8 @@ q8_status scaled_mm_ws_impl(const int8_t* a, int64_t lda, const int8_t* b, int64
     if (r == Q8_OK && M > 0) r = check_ws(ws, ws_bytes, sp.bytes);
     if (r != Q8_OK || M == 0) return r;
     GemmArgs p{a, lda, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};
-    if (sp.ks > 1 && gemm_offsets_fit(p)) return hip_status(run_split<false, F16>(p, sp, ws, st(stream)));
+    if (sp.ks > 1 && !w8a8_streams(p) && gemm_offsets_fit(p))
+        return hip_status(run_split<false, F16>(p, sp, ws, st(stream)));
     return hip_status(run_gemm_i8<F16 ? EPI_CHANNEL_F16 : EPI_CHANNEL>(p, st(stream)));
 }
 
@@ -303,7 +314,7 @@ q8_status quant_scaled_mm_ws_impl(const uint16_t* x, int64_t ldx, const int8_t* 
     if (r == Q8_OK && M > 0) r = check_ws(ws, ws_bytes, sp.bytes);
     if (r != Q8_OK || M == 0) return r;
     GemmArgs p{xq, K, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};
-    if (sp.ks < 2 || !gemm_offsets_fit(p))
+    if (sp.ks < 2 || w8a8_streams(p) || !gemm_offsets_fit(p))
         return quant_scaled_mm_impl<F16>(x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok, M, N, K, stream);
     hipStream_t s = st(stream);
     if (run_quant<F16>(x, ldx, xq, K, scale_tok, (int)M, (int)K, s) != hipSuccess) return Q8_EHIP;

@@ -83,26 +83,33 @@ __host__ __device__ inline size_t sg_lds_bytes(int rows, int nbuf, int mg) {
     return ring > red ? ring : red;
 }
 
-// Waits of the streaming kernel that gave up (see sg_wait_ge), counted per
-// device since the library was loaded there; q8_wait_timeouts reads it.
+// Waves of the streaming kernel that ran for more than SG_WAVE_LIMIT_TICKS
+// (see sg_wait_ge), counted per device since the library was loaded there;
+// q8_wait_timeouts reads it.
 __device__ unsigned int sg_wait_timeouts;
+
+// 10 ms of the 100 MHz real-time counter: far beyond any call of this
+// kernel (well under 1 ms), and below the time one bounded wait takes to
+// give up (2^20 polls of at least a 64-clock sleep, about 30 ms).
+constexpr uint64_t SG_WAVE_LIMIT_TICKS = 1000000;
 
 // Spin (short sleeps) until an LDS counter reaches target; bounded (about
 // 2^20 polls, tens of milliseconds) so a broken invariant gives wrong
-// output, not a hung device -- and a count in sg_wait_timeouts, so that
-// the wrong output does not pass unnoticed.  The poll is a ds_read written
-// out (and waited for inside the same statement): a compiler-visible LDS
-// read would first drain the loading waves' in-flight direct loads.
+// output, not a hung device.  A wave whose wait gave up has run far longer
+// than any call takes, and counts itself in sg_wait_timeouts at its end (a
+// clock read at its start and end, outside the waits: recording inside the
+// poll loop changed its code and cost 5-15% on W8A16 calls).  The poll is
+// a ds_read written out (and waited for inside the same statement): a
+// compiler-visible LDS read would first drain the loading waves' in-flight
+// direct loads.
 __device__ __forceinline__ void sg_wait_ge(int* c, int target) {
     const uint32_t a = (uint32_t)(uintptr_t)(Q8_LDS int*)c;
-    int it = 0;
-    for (; it < (1 << 20); ++it) {
+    for (int it = 0; it < (1 << 20); ++it) {
         int v;
         asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
         if (__builtin_amdgcn_readfirstlane(v) >= target) break;
         __builtin_amdgcn_s_sleep(1);
     }
-    if (it == (1 << 20) && (threadIdx.x & 63) == 0) atomicAdd(&sg_wait_timeouts, 1u);
     asm volatile("" ::: "memory");
 }
 
@@ -184,6 +191,7 @@ __global__ __launch_bounds__(1024, (sg_waves_per_simd<I8, MG>())) void stream_ge
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int g = 0; g < MG; ++g) acc[t][g] = acc_t{};
+    const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
     if (wid < 8) {
         // ---- multiplying wave: K blocks BPW*wid .. BPW*wid + BPW-1 of
         // every segment
@@ -300,6 +308,8 @@ __global__ __launch_bounds__(1024, (sg_waves_per_simd<I8, MG>())) void stream_ge
     }
 
     // ---- sum the 8 multiplying waves' partial tiles, epilogue
+    if (__builtin_amdgcn_s_memrealtime() - t_start > SG_WAVE_LIMIT_TICKS && lane == 0)
+        atomicAdd(&sg_wait_timeouts, 1u);
     block_barrier();  // every wave is done with the ring
     acc_t* red = reinterpret_cast<acc_t*>(lds);
     if (wid < 8) {
