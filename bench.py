@@ -67,12 +67,12 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 # (null).
 GEMM_COUNTERS = {
     "sources_sha256": {
-        "gemm_big.hpp": "86785bac67fcdcaaf077878f83390f6fc1805d1d3c6b704b21311aa69f3681a1",
-        "gemm_i8.hpp": "cd18b8b57aa890022611210e3ae06f99127a3762c9173ed154adcd2b6d701081",
+        "gemm_big.hpp": "eeee3448928a0b32c573e0dfc06829632561485523d13d9e132dcaed845f613a",
+        "gemm_i8.hpp": "febc8517b77d8095609f9562f5666c5cbbab9ae7ee7319a48cf8b27227353afa",
         "q8_device.hpp": "93921317d9ee2061ee8f6a130188921aef7ffc81f9e84a6867f9e2ea825e1a33",
     },
-    "fetch_kib": 367721.7, "write_kib": 261641.9,
-    "copy_kib": 524288.0, "copy_fetch_kib": 262155.5, "copy_write_kib": 524288.0,
+    "fetch_kib": 367721.4, "write_kib": 261999.8,
+    "copy_kib": 524288.0, "copy_fetch_kib": 262155.6, "copy_write_kib": 524288.0,
 }
 
 
@@ -768,31 +768,33 @@ def main():
     quant()
     gemm_alone = call_stats(gemm, args.steps)
 
+    # events in the timed steps: one before the first step, then one after
+    # each quantizer and one after each GEMM (the end of a step is the start
+    # of the next), on the stream the library launches on
     s = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
 
-    def step(e=None):
-        if e is not None:
-            e[0].record(s)
+    def step(i=None):
         quant()
-        if e is not None:
-            e[1].record(s)
+        if i is not None:
+            ev[2 * i + 1].record(s)
         gemm()
-        if e is not None:
-            e[2].record(s)
+        if i is not None:
+            ev[2 * i + 2].record(s)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
+    ev[0].record(s)
     for i in range(args.steps):
-        step(ev[i])
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     value = ops * args.steps / elapsed / 1e12
-    quant_in = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    gemm_in = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    quant_in = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)])
+    gemm_in = np.array([ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)])
     gemm_ms = float(gemm_in.mean())
 
     achieved = ops / (gemm_ms * 1e-3) / 1e12
