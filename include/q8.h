@@ -199,7 +199,7 @@ q8_status q8_wait_timeouts(uint32_t *count, int reset);
 
 /* ------------------------------------------------------------------------
  * Split K with a caller workspace.  Between the few-token kernels and the
- * large tiles (roughly 33-512 tokens at the model's shapes) the output has
+ * large tiles (roughly 24-512 tokens at the model's shapes) the output has
  * too few tiles to keep 256 compute units busy.  The _ws entry points then
  * split K: ks workgroups per output tile each sum a contiguous K range into
  * a plane of the caller's workspace, and a second kernel adds the planes and
@@ -221,7 +221,7 @@ q8_status q8_wait_timeouts(uint32_t *count, int reset);
 /* Bytes of workspace the _ws entry points need for an (M, N, K) problem:
  * 0 when none of them splits K at that size (then the workspace may be
  * NULL), else ks * M * N * 4 for the library's split count ks (2 <= ks <=
- * 10; at 33-64 tokens the W8A8 calls keep the weight-streaming kernel, and
+ * 10; at 24-64 tokens the W8A8 calls keep the weight-streaming kernel, and
  * leave the workspace unused, where that kernel runs).  Never more than
  * 31,457,280 bytes (30 MiB).  Nonpositive sizes give 0. */
 int64_t q8_workspace_bytes(int64_t M, int64_t N, int64_t K);

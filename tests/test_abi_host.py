@@ -169,13 +169,14 @@ def test_workspace_bytes_rule(lib):
     (30 MiB): checked over the model's shapes and 1-16384 tokens."""
     wb = lib.q8_workspace_bytes
     assert wb(0, 5120, 5120) == 0 and wb(-1, 16, 128) == 0
-    for M in (1, 8, 32):
+    for M in (1, 8, 16, 23):
         assert wb(M, 5120, 5120) == 0            # the streaming kernels
+    assert wb(32, 5120, 17408) == 10 * 32 * 5120 * 4  # 32 x 128 tiles from 24 tokens
     assert wb(64, 5120, 17408) == 10 * 64 * 5120 * 4  # 64 x 128 tiles from 33 tokens
     assert wb(8192, 15360, 5120) == 0            # the large tiles
     seen = 0
     for N, K in ((5120, 5120), (15360, 5120), (17408, 5120), (5120, 17408), (5120, 13824)):
-        for M in list(range(33, 1025, 7)) + [2048, 4096, 8192, 16384]:
+        for M in list(range(24, 1025, 7)) + [2048, 4096, 8192, 16384]:
             b = wb(M, N, K)
             assert 0 <= b <= 480 * 128 * 128 * 4
             if b:
@@ -206,9 +207,8 @@ def test_workspace_validation(lib):
         assert fn(*args, W, need - 1, None) == EINVAL
         assert fn(*args, W + 8, need, None) == EUNSUP
         assert fn(*args[:-3], 0, N, K, None, 0, None) == OK   # M = 0: nothing to do
-    # no split at M = 32: no workspace needed, NULL accepted (validation
-    # passes; with fake pointers the call is not made here)
-    assert lib.q8_workspace_bytes(32, N, K) == 0
+    # no split below 24 tokens: no workspace needed (NULL accepted)
+    assert lib.q8_workspace_bytes(16, N, K) == 0
     # the old prototype's sweep: 256 MiB against the planes it wrote
     old = 64 << 20 << 2
     short = [(m, ks) for m in (65, 128, 256, 512) for ks in range(2, 13)

@@ -135,6 +135,32 @@ def test_quant_scaled_mm_f16_token_counts(M):
     assert_ulp1(hbits(host(y)), y_ref, f"one-call f16 M={M}")
 
 
+@pytest.mark.parametrize("M,N,K,pad", [(5, 2048, 2304, 0), (12, 4112, 1280, 16), (16, 17408, 5120, 16)])
+def test_quant_scaled_mm_f16_few_tokens_outside_decode(M, N, K, pad):
+    """fp16 activations, up to 16 tokens outside the one-kernel decode path
+    (the quantizer, then the weight-streaming kernel): strided x, w and y, a
+    zero row."""
+    say("few tokens outside decode f16", M, N, K, pad)
+    xf, wf = synth.custom(M, K + pad, N, seed=5 * M + K, outlier_cols=K // 90)
+    xf = xf.float().half()
+    xf[M // 2] = 0
+    x = xf[:, :K].contiguous()
+    w = wf[:, :K].contiguous()
+    xq_ref, st_ref = oracle.quant_per_token_f16(hbits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y_ref = oracle.scaled_mm_f16(xq_ref, wq_ref, st_ref, sc_ref)
+    wq_full = torch.zeros((N, K + pad), dtype=torch.int8, device=DEV)
+    wq_full[:, :K] = dev(torch.from_numpy(wq_ref))
+    yfull = torch.full((M, N + pad), -1, dtype=torch.int16, device=DEV).view(torch.float16)
+    y, xq, st = q8.q8_quant_scaled_mm_f16(dev(xf)[:, :K], wq_full[:, :K], dev(torch.from_numpy(sc_ref)),
+                                          out=yfull[:, :N])
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    np.testing.assert_array_equal(host(st).numpy(), st_ref)
+    assert_ulp1(hbits(host(y).contiguous()), y_ref, f"few tokens f16 {M}x{N}x{K}")
+    if pad:
+        assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (8, 256, 1024), (65, 272, 1152), (200, 384, 2048),
                                    (300, 5120, 256), (600, 5120, 256)])  # 64 x 128, 128 x 128 tiles
 def test_group128_act_f16(M, N, K):

@@ -496,6 +496,44 @@ def test_scaled_mm_two_streaming_passes(M, N, K, pad):
     assert_ulp1(bits(host(y2)), y_ref, f"quant_scaled_mm {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,pad", [
+    (16, 16, 256, 0),       # one partial segment, one workgroup
+    (3, 2048, 4352, 16),    # few tokens where the one-kernel decode path does not fit (K % 1024)
+    (12, 4112, 1280, 16),   # partial last segment, ragged last workgroup, strided operands
+    (9, 5120, 5120, 0),     # o_proj-like
+    (16, 15360, 5120, 16),  # q/k/v-like, strided
+    (16, 17408, 5120, 0),   # gate/up-like
+])
+def test_quant_scaled_mm_few_tokens_outside_decode(M, N, K, pad):
+    """Up to 16 tokens outside the one-kernel decode path (more than 8
+    tokens, or K not a multiple of 1024): the quantizer, then the
+    weight-streaming kernel. Codes and scales bit-exact, outputs within 1
+    ulp of the oracle, with a zero row, a row whose codes take the division
+    fallback, strided x, w and y."""
+    say("few tokens outside decode", M, N, K, pad)
+    xf, wf = synth.custom(M, K + pad, N, seed=11 * M + N + K, outlier_cols=K // 80)
+    x = xf[:, :K].contiguous()
+    x[M // 2] = 0
+    if M > 2:
+        x[M - 1, :4] = torch.tensor([1.0, 0.5, -0.5, 0.75])
+        x[M - 1, 4:] = 0
+    xf[:, :K] = x
+    w = wf[:, :K].contiguous()
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y_ref = oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref)
+    wq_full = torch.zeros((N, K + pad), dtype=torch.int8, device=DEV)
+    wq_full[:, :K] = dev(torch.from_numpy(wq_ref))
+    sc = dev(torch.from_numpy(sc_ref))
+    yfull = torch.full((M, N + pad), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    y, xq, st = q8.q8_quant_scaled_mm(dev(xf)[:, :K], wq_full[:, :K], sc, out=yfull[:, :N])
+    np.testing.assert_array_equal(host(st).numpy(), st_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    assert_ulp1(bits(host(y).contiguous()), y_ref, f"few tokens {M}x{N}x{K}")
+    if pad:
+        assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
+
+
 @pytest.mark.parametrize("M,N,K", [(97, 9216, 384), (200, 9216, 256), (450, 8192, 128)])
 def test_scaled_mm_mid_token_tiles(M, N, K):
     """65-512 tokens where 256 x 256 tiles are too few: 32 x 128, 64 x 128

@@ -75,7 +75,8 @@ def test_quant_scaled_mm_ws(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(65, 5120, 17408), (128, 5120, 13824), (300, 1040, 2048),
                                    (512, 5120, 13824), (200, 4112, 4480),
-                                   (40, 5120, 17408), (64, 5120, 13824), (33, 1040, 4096)])
+                                   (40, 5120, 17408), (64, 5120, 13824), (33, 1040, 4096),
+                                   (24, 5120, 17408), (32, 5120, 13824), (27, 2064, 3072)])
 def test_w8a16_mm_ws(M, N, K):
     say("w8a16_mm_ws", M, N, K, "workspace", q8.q8_workspace_bytes(M, N, K))
     assert q8.q8_workspace_bytes(M, N, K) > 0

@@ -147,17 +147,18 @@ hipError_t run_gemm_group(const GemmArgs& p, hipStream_t s) { return run_gemm_gr
 // ---- split K (caller workspace) ----------------------------------------
 // Between the few-token kernels and the large tiles the tiled grid has too
 // few tiles to fill 256 CUs.  With a workspace the GEMM then runs on
-// BM x 128 tiles (BM = 64 up to 64 tokens, else 128) with K split ks ways,
-// ks = 480 / tiles (at most 10, and K at least 768 per split), so that
-// about 240-480 workgroups run.  Measured over 24-512 tokens at N = 5120,
-// 15360 and 17408 (K = 5120) and the W8A16 shapes 5120 x 17408 and
-// 5120 x 13824 against 21 (tile, ks) pairs, this rule picks the fastest
-// pair or one within 10% of it: 1.0-3.5x faster than the unsplit route
-// from 65 tokens, and from 33 tokens wherever that route would run the
-// tiled kernel (at 33-64 tokens the W8A8 weight-streaming kernel stays,
-// where it runs: within 5% of the split or faster).  Since ks * tiles <= 480
-// and a tile covers at most 128 x 128 outputs, the planes never need more
-// than 480 * 128 * 128 * 4 bytes (30 MiB).
+// BM x 128 tiles (BM = 32 up to 32 tokens, 64 up to 64, else 128) with K
+// split ks ways, ks = 480 / tiles (at most 10, and K at least 768 per
+// split), so that about 240-480 workgroups run.  Measured over 24-512
+// tokens at N = 5120, 15360 and 17408 (K = 5120) and the W8A16 shapes
+// 5120 x 17408 and 5120 x 13824 against 21 (tile, ks) pairs, this rule
+// picks the fastest pair or one within 10% of it: 1.0-3.5x faster than the
+// unsplit route from 65 tokens, and from 24 tokens wherever that route
+// would run the tiled kernel or (W8A16) the weight-streaming kernel at 24
+// tokens and more (the W8A8 weight-streaming kernel stays where it runs:
+// within 5% of the split or faster).  Since ks * tiles <= 480 and a tile
+// covers at most 128 x 128 outputs, the planes never need more than
+// 480 * 128 * 128 * 4 bytes (30 MiB).
 struct SplitPlan {
     int ks = 1;         // planes (1: no split)
     int kz = 0;         // K elements per split, a multiple of 128
@@ -167,8 +168,8 @@ struct SplitPlan {
 
 inline SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
     SplitPlan sp;
-    if (M <= 32 || N <= 0 || K < 256) return sp;  // few tokens: the streaming kernels
-    sp.bm = M <= 64 ? 64 : 128;
+    if (M < 24 || N <= 0 || K < 256) return sp;  // few tokens: the streaming kernels
+    sp.bm = M <= 32 ? 32 : M <= 64 ? 64 : 128;
     const int64_t tiles = ((M + sp.bm - 1) / sp.bm) * ((N + 127) / 128);
     int64_t ks = 480 / tiles;
     if (ks > 10) ks = 10;
@@ -211,8 +212,9 @@ hipError_t run_split(const GemmArgs& p, const SplitPlan& sp, void* ws, hipStream
     q.kz = sp.kz;
     q.plane = (int64_t)p.M * p.N;
     constexpr int E = W16 ? (F16 ? EPI_W16_PART_F16 : EPI_W16_PART) : EPI_I32;
-    const hipError_t e = sp.bm == 64 ? launch_gemm_i8<64, 128, 2, 2, E, 8>(q, s)
-                                     : launch_gemm_i8<128, 128, 2, 2, E, 8>(q, s);
+    const hipError_t e = sp.bm == 32   ? launch_gemm_i8<32, 128, 1, 4, E, 8>(q, s)
+                         : sp.bm == 64 ? launch_gemm_i8<64, 128, 2, 2, E, 8>(q, s)
+                                       : launch_gemm_i8<128, 128, 2, 2, E, 8>(q, s);
     if (e != hipSuccess) return e;
     return launch_splitk_reduce<W16 ? 1 : 0, F16>(static_cast<const int32_t*>(ws), sp.ks, q.plane, p.s_tok,
                                                     p.s_w, static_cast<uint16_t*>(p.c), p.ldc, p.M, p.N, s);
