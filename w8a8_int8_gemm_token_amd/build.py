@@ -8,7 +8,14 @@ hipcc cross-compiles for gfx950 without a GPU.  Flags:
   no fast-math               '/' and sqrtf stay correctly rounded, denormals
                              are kept (the codes depend on exact quotients);
   -target-feature -packed-fp32-ops
-                             plain (unpacked) fp32 VALU code only.
+                             plain (unpacked) fp32 VALU code only;
+  -mllvm -amdgpu-mfma-vgpr-form
+                             MFMA results in ordinary VGPRs, not AGPRs: the
+                             per-block folds of the group-scaled and FP8
+                             GEMMs read every accumulator with VALU
+                             instructions, which cannot take AGPR operands
+                             (one v_accvgpr_read per element and block
+                             otherwise).  No kernel's occupancy changes.
 """
 from __future__ import annotations
 
@@ -33,6 +40,7 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]
