@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--secondary decode,tiny,group128,group128_act,w8a16,
-                                 rmsnorm_quant,fp8_block,f16,m_sweep | none]
+                                 rmsnorm_quant,fp8_block,f16,m_sweep,vendor | none]
                     [--calibrate-copy]
 
 A step is one pass of the W8A8 hot path over the prefill workload
@@ -28,8 +28,10 @@ clock it holds under this load.  Prints one JSON line:
   secondary    = decode (M=1, M=8) per call in a HIP graph with the weight
              copies rotated past the 256 MB last-level cache, against 8 TB/s
              and against a plain read of the same bytes in the same protocol;
-             the tiny workload's latency; the measured ceilings; and the
-             other workloads (p10/p50/p90 of per-call event times)
+             the tiny workload's latency; the measured ceilings; the
+             other workloads (p10/p50/p90 of per-call event times); and the
+             vendor BLAS (hipBLASLt through torch) on plain GEMMs of the
+             same shapes, for context
 --calibrate-copy adds a plain device-to-device copy of 512 MiB (torch's copy
 kernel), so that a hardware-counter run of this script also measures the
 bytes the counters report for a transfer of known size.
@@ -722,12 +724,58 @@ def m_sweep(dev, reps=10):
     return out
 
 
+def vendor_gemms(dev, iters=20) -> dict:
+    """The vendor BLAS (hipBLASLt, through torch's _int_mm, matmul and
+    _scaled_mm) on this board at the workloads' shapes, timed like the
+    layer's own lines (events per call after a settling run): plain INT8 x
+    INT8 -> INT32 at the prefill and group-128 shapes (no scales, no
+    quantizer), a plain bf16 GEMM at the W8A16 shape (no dequantization),
+    and FP8 E4M3 with one scale per row and column at the FP8 block shape
+    (no per-block fold).  Each does less than the layer's kernel at that
+    shape; they are context, not the layer."""
+    out = {"library": "hipBLASLt via torch (" + torch.__version__ + ")"}
+
+    def run(name, f, flops):
+        try:
+            f()
+            torch.cuda.synchronize()
+            st = call_stats(f, iters)
+            out[name] = {"us": round(st["p50"] * 1e3, 1), "TOPS": round(flops / (st["p50"] * 1e-3) / 1e12, 1),
+                         "stats_us": _us(st)}
+        except Exception as e:  # an op this torch build lacks
+            out[name] = {"error": f"{type(e).__name__}: {str(e)[:120]}"}
+    g = torch.Generator(device=dev).manual_seed(0)
+    for name, key in (("int8_prefill", "prefill"), ("int8_group128_shape", "group128")):
+        wl = synth.WORKLOADS[key]
+        a = torch.randint(-127, 128, (wl.M, wl.K), dtype=torch.int8, device=dev, generator=g)
+        b = torch.randint(-127, 128, (wl.N, wl.K), dtype=torch.int8, device=dev, generator=g)
+        run(name, lambda: torch._int_mm(a, b.t()), 2.0 * wl.M * wl.N * wl.K)
+        del a, b
+    wl = synth.WORKLOADS["w8a16"]
+    a = torch.randn((wl.M, wl.K), dtype=torch.bfloat16, device=dev, generator=g)
+    b = torch.randn((wl.N, wl.K), dtype=torch.bfloat16, device=dev, generator=g)
+    run("bf16_w8a16_shape", lambda: a @ b.t(), 2.0 * wl.M * wl.N * wl.K)
+    del a, b
+    wl = synth.WORKLOADS["fp8_block"]
+    a = torch.randn((wl.M, wl.K), device=dev, generator=g).to(torch.float8_e4m3fn)
+    b = torch.randn((wl.N, wl.K), device=dev, generator=g).to(torch.float8_e4m3fn)
+    sa = torch.ones((wl.M, 1), device=dev)
+    sb = torch.ones((1, wl.N), device=dev)
+    run("fp8_rowwise_fp8_block_shape",
+        lambda: torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16),
+        2.0 * wl.M * wl.N * wl.K)
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 SECONDARY = {"decode": lambda dev: decode_gbs(dev), "group128": lambda dev: group_tops(dev),
              "tiny": lambda dev: tiny_latency(dev),
              "m_sweep": lambda dev: m_sweep(dev),
              "group128_act": lambda dev: group_act_tops(dev),
              "w8a16": lambda dev: w8a16_tflops(dev), "rmsnorm_quant": lambda dev: rmsnorm_quant_gbs(dev),
-             "fp8_block": lambda dev: fp8_block_tflops(dev), "f16": lambda dev: f16_layer(dev)}
+             "fp8_block": lambda dev: fp8_block_tflops(dev), "f16": lambda dev: f16_layer(dev),
+             "vendor": lambda dev: vendor_gemms(dev)}
 
 
 def main():
@@ -738,7 +786,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary",
-                    default="decode,tiny,group128,group128_act,w8a16,rmsnorm_quant,fp8_block,f16,m_sweep",
+                    default="decode,tiny,group128,group128_act,w8a16,rmsnorm_quant,fp8_block,f16,m_sweep,vendor",
                     help="comma list of secondary workloads, or 'none'")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()

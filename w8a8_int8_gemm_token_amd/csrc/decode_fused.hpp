@@ -18,34 +18,41 @@
 //    itself: redundant VALU work that runs while the weights stream, and no
 //    communication between workgroups;
 //  * waves 8..15 move the workgroup's R x K weight tile to LDS with
-//    buffer_load_dwordx4 ... lds (1 KB of one row per instruction, each wave
-//    a contiguous eighth of the tile).  A CU
-//    accepts only so many loads at a time, so a wave issuing the tile stalls
-//    at issue until earlier loads drain; keeping the quantizing waves free of
-//    weight loads is what lets the two overlap.  The quantizing waves run at
-//    a raised wave priority so that their activation loads are issued ahead
-//    of the weight stream;
-//  * after one barrier, wave w multiplies its K range of both 16-row tiles
-//    with v_mfma_i32_16x16x64_i8 (channels = A operand, tokens = B); rows and
-//    tokens past the ends repeat the last valid one (broadcast LDS reads, and
-//    their outputs are never stored), so the phase has no branches and its
-//    LDS reads can be issued ahead of the MFMAs.  The 16 partial int32 tiles
-//    are summed in LDS (exact), and waves 0..1 apply
-//    y = bf16_rne(((float)acc * s_tok[m]) * s_ch[n]).
+//    buffer_load_dwordx4 ... lds (1 KB of one row per instruction; wave d
+//    rows d, d + 8, ...), all of it issued at once, K segment (1024) by K
+//    segment; as each segment of its rows lands (vmcnt) a wave increments
+//    that segment's LDS counter.  A CU accepts only so many loads at a
+//    time, so a wave issuing the tile stalls at issue until earlier loads
+//    drain; keeping the quantizing waves free of weight loads is what lets
+//    the two overlap.  The quantizing waves run at a raised wave priority
+//    so that their activation loads are issued ahead of the weight stream;
+//  * once the code tile is complete, waves 0..7 multiply segment by segment
+//    as the segments land (wave w: K blocks 16 s + 2w and 16 s + 2w + 1 of
+//    segment s), both 16-row tiles with v_mfma_i32_16x16x64_i8 (channels =
+//    A operand, tokens = B), so that only the last segment's products
+//    remain when the weight stream ends; rows and tokens past the ends
+//    repeat the last valid one (broadcast LDS reads, and their outputs are
+//    never stored).  The 8 partial int32 tiles are summed in LDS (exact),
+//    and waves 0..1 apply y = bf16_rne(((float)acc * s_tok[m]) * s_ch[n]).
+//    The waits on the counters are bounded (lds_sync.hpp).
 // LDS layout (both tiles row-major with row stride K): 16-byte unit u of row
 // r is stored at unit u ^ (r & 15), so the fragment reads (16 rows, one unit
-// each) are free of bank conflicts.  Workgroup 0 also writes the codes and
-// the token scales to the caller's buffers.
+// each) are free of bank conflicts.  Workgroup 0 also writes the token
+// scales to the caller's buffer; the codes go out in 1 KB pieces spread over
+// the first workgroups.
 #pragma once
 
 #include "gemm_i8.hpp"
+#include "lds_sync.hpp"
 #include "quant.hpp"
 
 namespace q8 {
 
 constexpr int DECODE_MAX_M = 8;
 constexpr int DECODE_MAX_ROWS = 32;
-constexpr int DECODE_LDS_BYTES = 160 * 1024;
+// dynamic LDS limit: 160 KB less the kernel's static counters, the dynamic
+// array starting at the next 1024-byte boundary
+constexpr int DECODE_LDS_BYTES = 160 * 1024 - 1024;
 
 struct DecodeArgs {
     const uint16_t* x;  // [M, ldx] bf16 (fp16) activations
@@ -83,8 +90,9 @@ template <int NC, bool F16>
 __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
     constexpr int K = NC * 1024;
     constexpr int NQ = 2 * NC;  // 16-byte activation chunks per lane (one row per wave)
-    constexpr int KBW = NC;     // 64-deep K blocks per wave in the MFMA phase
     extern __shared__ __attribute__((aligned(1024))) int8_t lds[];
+    __shared__ int ready[NC];  // loading waves whose rows of K segment s landed (8 = all)
+    __shared__ int qdone;      // quantizing waves done (8 = the code tile is complete)
 
     const int M = p.M;
     const int lane = threadIdx.x & 63;
@@ -106,6 +114,11 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[e] = p.s_ch[ch + e];
     }
+    if (threadIdx.x < NC) ready[threadIdx.x] = 0;
+    if (threadIdx.x == 0) qdone = 0;
+    wait_lgkm0();
+    block_barrier();
+    const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
 
     if (wid < 8) {
         // ---- quantizing wave: token row m = wid; chunk c = lane + 64 i
@@ -133,62 +146,91 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
                 const int c8 = lane + 64 * i;  // 8-byte code piece
                 const int uu = c8 >> 1;
                 *reinterpret_cast<v2u*>(ct + m * K + ((uu ^ m) << 4) + ((c8 & 1) << 3)) = cd;
-                if (blockIdx.x == 0) *reinterpret_cast<v2u*>(p.xq + (int64_t)m * K + 8 * c8) = cd;
             }
         }
-        wait_lgkm0();  // code tile written (the global stores may stay in flight)
+        wait_lgkm0();  // this wave's codes are in the tile
         __builtin_amdgcn_s_setprio(0);
+        if (lane == 0) sg_signal(&qdone);
+
+        // ---- multiplying: segment s (K 1024 s .. + 1023) once its rows
+        // landed; this wave takes K blocks 16 s + 2 wid and + 1 of both
+        // 16-row tiles
+        sg_wait_ge(&qdone, 8);
+        const int tc = min(tok, M - 1);     // token row of the B fragment
+        const int r0 = min(tok, rows - 1);  // weight rows of the A fragments
+        const int r1 = min(16 + tok, rows - 1);
+        const int8_t* bp = ct + tc * K;
+        const int8_t* a0p = wt + r0 * K;
+        const int8_t* a1p = wt + r1 * K;
+        v4i acc0 = v4i{}, acc1 = v4i{};
+#pragma unroll
+        for (int sg = 0; sg < NC; ++sg) {
+            sg_wait_ge(&ready[sg], 8);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int u = 4 * (16 * sg + 2 * wid + j) + kg;  // 16-byte unit of K
+                const v4i b = *reinterpret_cast<const v4i*>(bp + ((u ^ tc) << 4));
+                const v4i a0 = *reinterpret_cast<const v4i*>(a0p + ((u ^ (r0 & 15)) << 4));
+                const v4i a1 = *reinterpret_cast<const v4i*>(a1p + ((u ^ (r1 & 15)) << 4));
+                acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b, acc1, 0, 0, 0);
+            }
+        }
+        v4i* red = reinterpret_cast<v4i*>(lds);
+        if (__builtin_amdgcn_s_memrealtime() - t_start > SG_WAVE_LIMIT_TICKS && lane == 0)
+            atomicAdd(&sg_wait_timeouts, 1u);
+        block_barrier();  // every wave is done reading the weight tile
+        red[wid * 64 + lane] = acc0;
+        red[(8 + wid) * 64 + lane] = acc1;
     } else {
-        // ---- loading wave d: 1 KB blocks [d * per, (d + 1) * per) of the
-        // row-major tile (a contiguous run of the weight matrix); lane l
-        // moves global unit l ^ (r & 15) of a block of row r to LDS unit l
+        // ---- loading wave d: rows d, d + 8, ... of the tile, segment by
+        // segment (1 KB of one row per instruction; lane l moves global unit
+        // l ^ (r & 15) of the row's block to LDS unit l); after each segment
+        // lands (vmcnt) the wave increments its counter
         const int d = wid - 8;
+        const int cnt = rows > d ? (rows - d + 7) / 8 : 0;
         const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + (int64_t)n0 * p.ldw,
                                                     (uint32_t)((int64_t)rows * p.ldw));
-        const int nblk = rows * NC;
-        const int per = (nblk + 7) / 8;
-        const int b1 = min(nblk, (d + 1) * per);
-        for (int i = d * per; i < b1; ++i) {
-            const int r = i / NC, u = i - r * NC;
-            const int voff = r * (int)p.ldw + u * 1024 + ((lane ^ (r & 15)) << 4);
-            // cache policy 2 = non-temporal: every weight byte is read once
-            // per call (measured 0.4-0.6 us faster per call at N = K = 5120)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (Q8_LDS void*)(wt + r * K + u * 1024), 16,
-                                                     voff, 0, 0, 2);
-        }
-        wait_vm_lgkm0<0>();  // this wave's part of the tile landed
-    }
-    block_barrier();  // weight tile and code tile complete
-
-    // ---- MFMA: wave wid takes K blocks [wid * KBW, +KBW) of both tiles
-    const int tc = min(tok, M - 1);          // token row of the B fragment
-    const int r0 = min(tok, rows - 1);       // weight rows of the A fragments
-    const int r1 = min(16 + tok, rows - 1);
-    const int8_t* bp = ct + tc * K;
-    const int8_t* a0p = wt + r0 * K;
-    const int8_t* a1p = wt + r1 * K;
-    v4i acc0 = v4i{}, acc1 = v4i{};
 #pragma unroll
-    for (int j = 0; j < KBW; ++j) {
-        const int u = 4 * (wid * KBW + j) + kg;  // 16-byte unit of K
-        const v4i b = *reinterpret_cast<const v4i*>(bp + ((u ^ tc) << 4));
-        const v4i a0 = *reinterpret_cast<const v4i*>(a0p + ((u ^ (r0 & 15)) << 4));
-        const v4i a1 = *reinterpret_cast<const v4i*>(a1p + ((u ^ (r1 & 15)) << 4));
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b, acc1, 0, 0, 0);
+        for (int sg = 0; sg < NC; ++sg) {
+            for (int j = 0; j < cnt; ++j) {
+                const int r = d + 8 * j;
+                const int voff = r * (int)p.ldw + sg * 1024 + ((lane ^ (r & 15)) << 4);
+                // cache policy 2 = non-temporal: every weight byte is read
+                // once per call (measured 0.4-0.6 us faster per call at
+                // N = K = 5120)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (Q8_LDS void*)(wt + r * K + sg * 1024), 16,
+                                                         voff, 0, 0, 2);
+            }
+        }
+#pragma unroll
+        for (int sg = 0; sg < NC; ++sg) {
+            sg_wait_vm((NC - 1 - sg) * cnt);  // segments 0..sg landed
+            if (lane == 0) sg_signal(&ready[sg]);
+        }
+        if (__builtin_amdgcn_s_memrealtime() - t_start > SG_WAVE_LIMIT_TICKS && lane == 0)
+            atomicAdd(&sg_wait_timeouts, 1u);
+        block_barrier();  // every wave is done reading the weight tile
     }
 
-    // ---- sum the 16 waves' partial tiles (exact int32), epilogue
-    block_barrier();  // every wave is done reading the weight tile
-    v4i* red = reinterpret_cast<v4i*>(lds);
-    red[wid * 64 + lane] = acc0;
-    red[(16 + wid) * 64 + lane] = acc1;
+    // ---- sum the 8 multiplying waves' partial tiles (exact int32),
+    // epilogue; the codes out
     wait_lgkm0();
     block_barrier();
+    if (wid == 2) {
+        // 1 KB piece q (token q / NC, K units 64 (q % NC) .. + 63) goes out
+        // from workgroup q (mod the grid), so that no workgroup carries all
+        for (int q = blockIdx.x; q < M * NC; q += gridDim.x) {
+            const int m = q / NC, u = 64 * (q - m * NC) + lane;
+            *reinterpret_cast<v4u*>(p.xq + (int64_t)m * K + 16 * u) =
+                *reinterpret_cast<const v4u*>(ct + m * K + ((u ^ m) << 4));
+        }
+    }
     if (!writer) return;
+    const v4i* red = reinterpret_cast<const v4i*>(lds);
     v4i s = v4i{};
 #pragma unroll
-    for (int w = 0; w < 16; ++w) s += red[(wid * 16 + w) * 64 + lane];
+    for (int w = 0; w < 8; ++w) s += red[(wid * 8 + w) * 64 + lane];
     const float st = row_scale_s[tok];
     float y[4];
 #pragma unroll
