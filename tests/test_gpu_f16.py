@@ -135,7 +135,8 @@ def test_quant_scaled_mm_f16_token_counts(M):
     assert_ulp1(hbits(host(y)), y_ref, f"one-call f16 M={M}")
 
 
-@pytest.mark.parametrize("M,N,K,pad", [(5, 2048, 2304, 0), (12, 4112, 1280, 16), (16, 17408, 5120, 16)])
+@pytest.mark.parametrize("M,N,K,pad", [(5, 2048, 2304, 0), (12, 4112, 1280, 16), (16, 17408, 5120, 16),
+                                     (13, 4112, 3072, 16)])
 def test_quant_scaled_mm_f16_few_tokens_outside_decode(M, N, K, pad):
     """fp16 activations, up to 16 tokens outside the one-kernel decode path
     (the quantizer, then the weight-streaming kernel): strided x, w and y, a

@@ -534,6 +534,44 @@ def test_quant_scaled_mm_few_tokens_outside_decode(M, N, K, pad):
         assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
 
 
+@pytest.mark.parametrize("M,N,K,pad", [
+    (9, 16, 1024, 0),       # one K segment, one small channel tile
+    (16, 1040, 2048, 16),   # last channel tile ragged, strided operands
+    (13, 4112, 3072, 0),    # three segments
+    (10, 8192, 4096, 32),   # four segments, strided
+    (16, 5120, 5120, 0),    # o_proj-like, five segments
+    (11, 15360, 5120, 16),  # q/k/v-like: three workgroups per CU, strided
+])
+def test_quant_scaled_mm_9_16_tokens(M, N, K, pad):
+    """9-16 tokens, K a multiple of 1024 (the quantizer, then the
+    weight-streaming kernel with one or two 16-token groups), over one to
+    five K segments, small and ragged channel tiles and several workgroups
+    per CU. Codes and scales bit-exact, outputs within 1 ulp of the oracle,
+    with a zero row, a row whose codes take the division fallback, strided
+    x, w and y; the padding columns of y untouched."""
+    say("9-16 tokens", M, N, K, pad)
+    xf, wf = synth.custom(M, K + pad, N, seed=13 * M + N + K, outlier_cols=K // 70)
+    x = xf[:, :K].contiguous()
+    x[M // 3] = 0
+    x[M - 1, :4] = torch.tensor([1.0, 0.5, -0.5, 0.75])  # 0.5/fl(1/127) ~ 63.5
+    x[M - 1, 4:] = 0
+    xf[:, :K] = x
+    w = wf[:, :K].contiguous()
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y_ref = oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref)
+    wq_full = torch.zeros((N, K + pad), dtype=torch.int8, device=DEV)
+    wq_full[:, :K] = dev(torch.from_numpy(wq_ref))
+    sc = dev(torch.from_numpy(sc_ref))
+    yfull = torch.full((M, N + pad), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    y, xq, st = q8.q8_quant_scaled_mm(dev(xf)[:, :K], wq_full[:, :K], sc, out=yfull[:, :N])
+    np.testing.assert_array_equal(host(st).numpy(), st_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    assert_ulp1(bits(host(y).contiguous()), y_ref, f"9-16 tokens {M}x{N}x{K}")
+    if pad:
+        assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
+
+
 @pytest.mark.parametrize("M,N,K", [(97, 9216, 384), (200, 9216, 256), (450, 8192, 128)])
 def test_scaled_mm_mid_token_tiles(M, N, K):
     """65-512 tokens where 256 x 256 tiles are too few: 32 x 128, 64 x 128
