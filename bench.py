@@ -69,12 +69,12 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 # (null).
 GEMM_COUNTERS = {
     "sources_sha256": {
-        "gemm_big.hpp": "eeee3448928a0b32c573e0dfc06829632561485523d13d9e132dcaed845f613a",
+        "gemm_big.hpp": "8fdf1c7bc31a1e14bde9abe6fe27a066c4ac91c62b301cdfb7a258b52749a483",
         "gemm_i8.hpp": "febc8517b77d8095609f9562f5666c5cbbab9ae7ee7319a48cf8b27227353afa",
         "q8_device.hpp": "93921317d9ee2061ee8f6a130188921aef7ffc81f9e84a6867f9e2ea825e1a33",
     },
-    "fetch_kib": 367721.4, "write_kib": 261999.8,
-    "copy_kib": 524288.0, "copy_fetch_kib": 262155.6, "copy_write_kib": 524288.0,
+    "fetch_kib": 367721.1, "write_kib": 262771.8,
+    "copy_kib": 524288.0, "copy_fetch_kib": 262155.5, "copy_write_kib": 524288.0,
 }
 
 

@@ -25,9 +25,10 @@
 // c ^ (r & 7) ^ ((r >> 3) & 1).  Schedule of a stage (four 32-deep
 // sub-steps): the next stage's loads go out behind the MFMAs of sub-step 0;
 // each sub-step's fragments are read behind the previous sub-step's MFMAs as
-// they release the registers; after sub-step 3 the wave waits for its loads
-// of the next stage, and one barrier publishes that stage and frees this
-// one.
+// they release the registers; halfway through sub-step 3 the wave waits for
+// its loads of the next stage and one barrier publishes that stage and
+// frees this one, and the second half of sub-step 3 runs behind the next
+// stage's first fragment reads.
 #pragma once
 
 #include "gemm_i8.hpp"
@@ -114,16 +115,21 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs p) {
         for (int b = 0; b < TN; ++b) acc[a][b] = v16i{};
     v4i fw[TN], fx[TM];
 
-    auto read = [&](int kk, const int8_t* bx, const int8_t* bw) __attribute__((always_inline)) {
+    // token blocks [a0, a1) of sub-step kk
+    auto read_x = [&](int kk, const int8_t* bx, int a0, int a1) __attribute__((always_inline)) {
 #pragma unroll
-        for (int a = 0; a < TM; ++a) fx[a] = *reinterpret_cast<const v4i*>(bx + xbase[kk] + a * 32 * BK);
+        for (int a = a0; a < a1; ++a) fx[a] = *reinterpret_cast<const v4i*>(bx + xbase[kk] + a * 32 * BK);
+    };
+    auto read = [&](int kk, const int8_t* bx, const int8_t* bw) __attribute__((always_inline)) {
+        read_x(kk, bx, 0, TM);
 #pragma unroll
         for (int b = 0; b < TN; ++b) fw[b] = *reinterpret_cast<const v4i*>(bw + wbase[kk] + b * 32 * BK);
     };
-    // token block a outer: fx[a] is free again after the TN MFMAs that use it
-    auto mfma = [&]() __attribute__((always_inline)) {
+    // MFMAs [t0, t1) of a sub-step, token block a outer: fx[a] is free again
+    // after the TN MFMAs that use it
+    auto mfma = [&](int t0 = 0, int t1 = NM) __attribute__((always_inline)) {
 #pragma unroll
-        for (int t = 0; t < NM; ++t) {
+        for (int t = t0; t < t1; ++t) {
             const int a = t / TN, b = t % TN;
             acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[b], fx[a], acc[a][b], 0, 0, 0);
         }
@@ -144,11 +150,21 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs p) {
         read(3, cx, cw);
         interleave<NM, NR, 0>();
         __builtin_amdgcn_sched_barrier(0);
-        mfma();
+        // sub-step 3 in two halves around the hand-over: the MFMAs of token
+        // blocks 0-1, the barrier, then the next stage's fragments of those
+        // blocks (their registers free again) behind the MFMAs of blocks
+        // 2-3, then the rest (3% faster than all 12 MFMAs before the
+        // barrier: a stage's first reads no longer start with the matrix
+        // pipe idle)
+        mfma(0, NM / 2);
         __builtin_amdgcn_sched_barrier(0);
         wait_vm_lgkm0<0>();
         block_barrier();
-        read(0, nx, nw);
+        read_x(0, nx, 0, TM / 2);
+        mfma(NM / 2, NM);
+        read_x(0, nx, TM / 2, TM);
+#pragma unroll
+        for (int b = 0; b < TN; ++b) fw[b] = *reinterpret_cast<const v4i*>(nw + wbase[0] + b * 32 * BK);
         __builtin_amdgcn_sched_barrier(0);
     };
 

@@ -128,15 +128,20 @@ __global__ __launch_bounds__(512) void gemm_w16_kernel(GemmArgs p) {
 #pragma unroll
         for (int b = 0; b < TN; ++b) acc[a][b] = v16f{};
     v4i fw[TN], fx[TM];
-    auto read = [&](int kk, const int8_t* bx, const int8_t* bw) __attribute__((always_inline)) {
+    // token blocks [a0, a1) of sub-step kk
+    auto read_x = [&](int kk, const int8_t* bx, int a0, int a1) __attribute__((always_inline)) {
 #pragma unroll
-        for (int a = 0; a < TM; ++a) fx[a] = *reinterpret_cast<const v4i*>(bx + xbase[kk] + a * 32 * BK);
+        for (int a = a0; a < a1; ++a) fx[a] = *reinterpret_cast<const v4i*>(bx + xbase[kk] + a * 32 * BK);
+    };
+    auto read = [&](int kk, const int8_t* bx, const int8_t* bw) __attribute__((always_inline)) {
+        read_x(kk, bx, 0, TM);
 #pragma unroll
         for (int b = 0; b < TN; ++b) fw[b] = *reinterpret_cast<const v4i*>(bw + wbase[kk] + b * 32 * BK);
     };
-    auto mfma = [&]() __attribute__((always_inline)) {
+    // MFMAs [t0, t1) of a sub-step, token block a outer
+    auto mfma = [&](int t0 = 0, int t1 = NM) __attribute__((always_inline)) {
 #pragma unroll
-        for (int t = 0; t < NM; ++t) {
+        for (int t = t0; t < t1; ++t) {
             const int a = t / TN, b = t % TN;
             if constexpr (F16)
                 acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fw[b]),
@@ -162,13 +167,21 @@ __global__ __launch_bounds__(512) void gemm_w16_kernel(GemmArgs p) {
         read(3, cx, cw);
         interleave<NM, NR, 0>();
         __builtin_amdgcn_sched_barrier(0);
-        mfma();
+        // sub-step 3 in two halves around the hand-over (as in
+        // gemm_big_kernel): token block 0, the weight conversion and the
+        // barrier, then the next stage's block-0 fragments behind the MFMAs
+        // of token block 1, then the rest
+        mfma(0, NM / 2);
         __builtin_amdgcn_sched_barrier(0);
         wait_vm_lgkm0<XIW>();  // this thread's weight loads landed (issued first)
         wstore(nw);
         wait_vm_lgkm0<0>();
         block_barrier();
-        read(0, nx, nw);
+        read_x(0, nx, 0, TM / 2);
+        mfma(NM / 2, NM);
+        read_x(0, nx, TM / 2, TM);
+#pragma unroll
+        for (int b = 0; b < TN; ++b) fw[b] = *reinterpret_cast<const v4i*>(nw + wbase[0] + b * 32 * BK);
         __builtin_amdgcn_sched_barrier(0);
     };
 
