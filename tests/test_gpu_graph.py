@@ -12,10 +12,13 @@ import w8a8_int8_gemm_token_amd as q8
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M", [1, 8, 300])
-def test_graph_replay_matches_eager(M):
+@pytest.mark.parametrize("M,K,N", [(1, 1024, 512), (8, 1024, 512), (300, 1024, 512),
+                                   (8, 5120, 5120),    # one-kernel decode, five K segments
+                                   (3, 5120, 15360),   # ... three workgroups per CU
+                                   (16, 5120, 5120)])  # quantizer + weight-streaming kernel
+def test_graph_replay_matches_eager(M, K, N):
     dev = "cuda:0"
-    x, w = synth.custom(M, 1024, 512, seed=40 + M, outlier_cols=8)
+    x, w = synth.custom(M, K, N, seed=40 + M, outlier_cols=8)
     x, w = x.to(dev), w.to(dev)
     wq, sc = q8.q8_quant_weight(w)
     y_ref, xq_ref, st_ref = q8.q8_quant_scaled_mm(x, wq, sc)
