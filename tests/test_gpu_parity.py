@@ -955,3 +955,45 @@ def test_repeat_calls_bitwise_identical():
     y1, _, _ = q8.q8_quant_scaled_mm(xd, wq, sc)
     y2, _, _ = q8.q8_quant_scaled_mm(xd, wq, sc)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def _random_shapes(n, seed):
+    """n seeded (M, N, K) shapes over every route of the one-call layer:
+    1-600 tokens, N a multiple of 16, K a multiple of 128 up to 6144, sized
+    so that the oracle finishes each in well under a second."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.choice([rng.integers(1, 17), rng.integers(17, 129), rng.integers(129, 601)]))
+        N = 16 * int(rng.integers(1, 376))
+        K = 128 * int(rng.integers(1, 49))
+        if M * N * K <= 3e9:
+            out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes(24, 2026))
+def test_random_shapes_every_route(M, N, K):
+    """Seeded random shapes through q8_quant_scaled_mm and w8a16_mm, and
+    their _ws forms where the library splits K: W8A8 codes and scales
+    bit-exact and outputs within 1 ulp of the oracle (the _ws output the same
+    bits as the plain call), W8A16 within its stated bound."""
+    say("random shape", M, N, K, "workspace", q8.q8_workspace_bytes(M, N, K))
+    x, w = synth.custom(M, K, N, seed=M * 7 + N + K, outlier_cols=max(1, K // 100))
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y_ref = oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref)
+    wq, sc = dev(torch.from_numpy(wq_ref)), dev(torch.from_numpy(sc_ref))
+    xd = dev(x)
+    y, xq, st = q8.q8_quant_scaled_mm(xd, wq, sc)
+    np.testing.assert_array_equal(host(st).numpy(), st_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    yb = bits(host(y))
+    assert_ulp1(yb, y_ref, f"random {M}x{N}x{K}")
+    y3 = q8.w8a16_mm(xd, wq, sc)
+    _check_w8a16(bits(host(y3)), bits(x), wq_ref, sc_ref, f"random w8a16 {M}x{N}x{K}")
+    if q8.q8_workspace_bytes(M, N, K):
+        y2, _, _ = q8.q8_quant_scaled_mm_ws(xd, wq, sc)
+        np.testing.assert_array_equal(bits(host(y2)), yb)
+        y4 = q8.w8a16_mm_ws(xd, wq, sc)
+        _check_w8a16(bits(host(y4)), bits(x), wq_ref, sc_ref, f"random w8a16_ws {M}x{N}x{K}")
