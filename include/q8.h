@@ -182,9 +182,9 @@ q8_status q8_mm_i32(const int8_t *a, int64_t lda, const int8_t *b,
                     int64_t N, int64_t K, q8_stream stream);
 
 /* ------------------------------------------------------------------------
- * q8_wait_timeouts -- diagnostics of the few-token weight-streaming kernel
+ * q8_wait_timeouts -- diagnostics of the few-token weight-streaming kernels
  * (q8_scaled_mm, q8_quant_scaled_mm and w8a16_mm at up to 64 tokens, and in
- * two passes up to 128).  Its waves hand weight segments over through
+ * two passes up to 128).  Their waves hand weight segments over through
  * counters in on-chip memory; every wait on them is bounded (about 2^20
  * polls, some 30 ms), so a broken hand-over gives a wrong result instead of
  * a hung device.  A wave that has run for more than 10 ms -- which no call

@@ -460,6 +460,52 @@ def test_scaled_mm_few_tokens_partial_segment(M, N, K, pad):
 
 
 @pytest.mark.parametrize("M,N,K,pad", [
+    (1, 16, 1024, 0),       # one workgroup of 4 channels, one segment
+    (16, 16, 8192, 16),     # 16 tokens, eight segments, strided operands
+    (9, 1040, 2048, 16),    # 8 channels per workgroup, the last one ragged
+    (5, 2064, 3072, 0),     # 12 channels per workgroup, the last one of 4
+    (16, 4096, 4096, 16),   # 16 channels per workgroup, 256 workgroups
+    (12, 3008, 8192, 0),
+    (3, 4096, 1024, 0),
+])
+def test_codes_decode_kernel(M, N, K, pad):
+    """Up to 16 tokens of int8 codes with K a multiple of 1024 and N <= 4096:
+    the decode kernel's whole-tile weight stream on the codes, B fragments
+    loaded from global memory (q8_scaled_mm; the one-call layer from 9
+    tokens, behind the row quantizer). Against the oracle, strided codes,
+    weights and output, padding left untouched; fp16 output as well."""
+    say("codes decode kernel", M, N, K, pad)
+    xf, wf = synth.custom(M, K + pad, N, seed=17 * M + N + K, outlier_cols=K // 64)
+    x = xf[:, :K].contiguous()
+    x[M // 2] = 0  # a zero row: scale 0, codes 0
+    xf[:, :K] = x
+    w = wf[:, :K].contiguous()
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y_ref = oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref)
+    wq_full = torch.zeros((N, K + pad), dtype=torch.int8, device=DEV)
+    wq_full[:, :K] = dev(torch.from_numpy(wq_ref))
+    wq = wq_full[:, :K]
+    sc = dev(torch.from_numpy(sc_ref))
+    st = dev(torch.from_numpy(st_ref))
+    xq_full = torch.full((M, K + pad), 77, dtype=torch.int8, device=DEV)
+    xq_full[:, :K] = dev(torch.from_numpy(xq_ref))
+    yfull = torch.full((M, N + pad), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    y = q8.q8_scaled_mm(xq_full[:, :K], wq, st, sc, out=yfull[:, :N])
+    assert_ulp1(bits(host(y).contiguous()), y_ref, f"codes decode {M}x{N}x{K}")
+    if pad:
+        assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
+    assert q8.q8_wait_timeouts(reset=True) == 0
+    y2, xq2, st2 = q8.q8_quant_scaled_mm(dev(xf)[:, :K], wq, sc)
+    np.testing.assert_array_equal(host(xq2).numpy(), xq_ref)
+    np.testing.assert_array_equal(host(st2).numpy(), st_ref)
+    np.testing.assert_array_equal(bits(host(y2)), bits(host(y).contiguous()))
+    yh = q8.q8_scaled_mm_f16(xq_full[:, :K], wq, st, sc)
+    yh_ref = oracle.scaled_mm_f16(xq_ref, wq_ref, st_ref, sc_ref)
+    assert_ulp1(host(yh).view(torch.int16).numpy().view(np.uint16), yh_ref, f"codes decode f16 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,pad", [
     (65, 1040, 1024, 16),   # 64 + 1 tokens
     (100, 5120, 1152, 0),   # the second pass has 36 tokens and a partial K segment
     (128, 2048, 4096, 16),

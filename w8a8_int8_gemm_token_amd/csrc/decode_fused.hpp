@@ -40,6 +40,8 @@
 // each) are free of bank conflicts.  Workgroup 0 also writes the token
 // scales to the caller's buffer; the codes go out in 1 KB pieces spread over
 // the first workgroups.
+// decode_pre_kernel (below) runs the same weight stream and per-segment
+// multiply on activations that are already int8 codes, up to 16 tokens.
 #pragma once
 
 #include "gemm_i8.hpp"
@@ -76,13 +78,66 @@ __host__ __device__ inline size_t decode_wt_bytes(int K, int rows) {
     const size_t wt = (size_t)rows * K;
     return wt > red ? wt : red;
 }
-__host__ __device__ inline size_t decode_lds_bytes(int K, int rows) {
-    return decode_wt_bytes(K, rows) + (size_t)DECODE_MAX_M * K + 256;
+// codes: the fused kernel's 8 x K code tile and token scales (none for the
+// pre-quantized kernel)
+__host__ __device__ inline size_t decode_lds_bytes(int K, int rows, bool codes = true) {
+    return decode_wt_bytes(K, rows) + (codes ? (size_t)DECODE_MAX_M * K + 256 : 0);
 }
 
 // LDS accesses done; vector memory loads may stay in flight.
 __device__ __forceinline__ void wait_lgkm0() {
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // vmcnt 63, expcnt 7, lgkmcnt 0
+}
+
+// Loading wave d (0..7) of a decode workgroup: rows d, d + 8, ... of the
+// workgroup's weight tile (rows x K, row stride K in LDS), segment by
+// segment, 1 KB of one row per instruction (lane l moves global unit
+// l ^ (r & 15) of the row's block to LDS unit l); once its rows of segment
+// s landed (vmcnt) the wave increments ready[s].
+template <int NC>
+__device__ __forceinline__ void decode_load_tile(const int8_t* w, int64_t ldw, int rows, int8_t* wt,
+                                                 int* ready, int d, int lane, uint64_t t_start) {
+    constexpr int K = NC * 1024;
+    const int cnt = rows > d ? (rows - d + 7) / 8 : 0;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)((int64_t)rows * ldw));
+#pragma unroll
+    for (int sg = 0; sg < NC; ++sg) {
+        for (int j = 0; j < cnt; ++j) {
+            const int r = d + 8 * j;
+            const int voff = r * (int)ldw + sg * 1024 + ((lane ^ (r & 15)) << 4);
+            // cache policy 2 = non-temporal: every weight byte is read once
+            // per call (measured 0.4-0.6 us faster per call at N = K = 5120)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (Q8_LDS void*)(wt + r * K + sg * 1024), 16, voff, 0, 0,
+                                                     2);
+        }
+    }
+#pragma unroll
+    for (int sg = 0; sg < NC; ++sg) {
+        sg_wait_vm((NC - 1 - sg) * cnt);  // segments 0..sg landed
+        if (lane == 0) sg_signal(&ready[sg]);
+    }
+    if (__builtin_amdgcn_s_memrealtime() - t_start > SG_WAVE_LIMIT_TICKS && lane == 0)
+        atomicAdd(&sg_wait_timeouts, 1u);
+}
+
+// Output lane of a decode workgroup (wave t < 2, lane l: token l % 16,
+// channels n0 + 16 t + 4 (l / 16) + e): the sum of the 8 multiplying
+// waves' partial tiles (exact int32), then y = ((float)acc * st) * sc[e].
+template <bool F16>
+__device__ __forceinline__ void decode_write(const v4i* red, int wid, int lane, float st, v4f sc, uint16_t* out) {
+    v4i s = v4i{};
+#pragma unroll
+    for (int w = 0; w < 8; ++w) s += red[(wid * 8 + w) * 64 + lane];
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float u = (float)s[e] * st;
+        y[e] = u * sc[e];
+    }
+    v2u o;
+    o[0] = pack16x2<F16>(y[0], y[1]);
+    o[1] = pack16x2<F16>(y[2], y[3]);
+    *reinterpret_cast<v2u*>(out) = o;
 }
 
 // NC = K / 1024.  F16: fp16 activations and outputs instead of bf16.
@@ -183,33 +238,7 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
         red[wid * 64 + lane] = acc0;
         red[(8 + wid) * 64 + lane] = acc1;
     } else {
-        // ---- loading wave d: rows d, d + 8, ... of the tile, segment by
-        // segment (1 KB of one row per instruction; lane l moves global unit
-        // l ^ (r & 15) of the row's block to LDS unit l); after each segment
-        // lands (vmcnt) the wave increments its counter
-        const int d = wid - 8;
-        const int cnt = rows > d ? (rows - d + 7) / 8 : 0;
-        const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + (int64_t)n0 * p.ldw,
-                                                    (uint32_t)((int64_t)rows * p.ldw));
-#pragma unroll
-        for (int sg = 0; sg < NC; ++sg) {
-            for (int j = 0; j < cnt; ++j) {
-                const int r = d + 8 * j;
-                const int voff = r * (int)p.ldw + sg * 1024 + ((lane ^ (r & 15)) << 4);
-                // cache policy 2 = non-temporal: every weight byte is read
-                // once per call (measured 0.4-0.6 us faster per call at
-                // N = K = 5120)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (Q8_LDS void*)(wt + r * K + sg * 1024), 16,
-                                                         voff, 0, 0, 2);
-            }
-        }
-#pragma unroll
-        for (int sg = 0; sg < NC; ++sg) {
-            sg_wait_vm((NC - 1 - sg) * cnt);  // segments 0..sg landed
-            if (lane == 0) sg_signal(&ready[sg]);
-        }
-        if (__builtin_amdgcn_s_memrealtime() - t_start > SG_WAVE_LIMIT_TICKS && lane == 0)
-            atomicAdd(&sg_wait_timeouts, 1u);
+        decode_load_tile<NC>(p.w + (int64_t)n0 * p.ldw, p.ldw, rows, wt, ready, wid - 8, lane, t_start);
         block_barrier();  // every wave is done reading the weight tile
     }
 
@@ -226,22 +255,105 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
                 *reinterpret_cast<const v4u*>(ct + m * K + ((u ^ m) << 4));
         }
     }
-    if (!writer) return;
-    const v4i* red = reinterpret_cast<const v4i*>(lds);
-    v4i s = v4i{};
+    if (writer)
+        decode_write<F16>(reinterpret_cast<const v4i*>(lds), wid, lane, row_scale_s[tok], sc,
+                          p.c + (int64_t)tok * p.ldc + ch);
+}
+
+// The same weight stream and per-segment multiply for activations that are
+// already quantized (q8_scaled_mm's int8 codes with their token scales, and
+// the one-call layer from 9 tokens on, behind the row quantizer): up to 16
+// tokens, which one 16-column B operand holds.  The multiplying waves load
+// their B fragments straight from the codes in global memory -- all 2 NC
+// of them, issued before the first wait -- so LDS holds only the weight
+// tile (a 16 x K code tile would not fit beside it).  Waves 0..7 multiply,
+// waves 8..15 load, as in decode_fused_kernel.
+struct DecodePreArgs {
+    const int8_t* a;  // [M, lda] int8 activation codes (lda % 16 == 0, 16-byte aligned)
+    int64_t lda;
+    const float* s_tok;  // [M]
+    const int8_t* w;     // [N, ldw] int8 weight codes
+    int64_t ldw;
+    const float* s_ch;  // [N]
+    uint16_t* c;        // [M, ldc] bf16 (fp16) out
+    int64_t ldc;
+    int M, N, K;
+    int rows;  // R: channels per workgroup (multiple of 4)
+};
+
+template <int NC, bool F16>
+__global__ __launch_bounds__(1024) void decode_pre_kernel(DecodePreArgs p) {
+    extern __shared__ __attribute__((aligned(1024))) int8_t lds[];
+    __shared__ int ready[NC];  // loading waves whose rows of K segment s landed (8 = all)
+
+    const int M = p.M;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int R = p.rows;
+    const int n0 = blockIdx.x * R;
+    const int rows = min(R, p.N - n0);
+    int8_t* wt = lds;  // [R][K] weight tile
+
+    const int tok = lane & 15, kg = lane >> 4;
+    const int ch = n0 + 16 * wid + 4 * kg;
+    const bool writer = wid < 2 && tok < M && 16 * wid + 4 * kg < rows;
+    v4f sc = v4f{};
+    float st = 0.0f;
+    if (writer) {
 #pragma unroll
-    for (int w = 0; w < 8; ++w) s += red[(wid * 8 + w) * 64 + lane];
-    const float st = row_scale_s[tok];
-    float y[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float u = (float)s[e] * st;
-        y[e] = u * sc[e];
+        for (int e = 0; e < 4; ++e) sc[e] = p.s_ch[ch + e];
+        st = p.s_tok[tok];
     }
-    v2u o;
-    o[0] = pack16x2<F16>(y[0], y[1]);
-    o[1] = pack16x2<F16>(y[2], y[3]);
-    *reinterpret_cast<v2u*>(p.c + (int64_t)tok * p.ldc + ch) = o;
+    if (threadIdx.x < NC) ready[threadIdx.x] = 0;
+    wait_lgkm0();
+    block_barrier();
+    const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+
+    if (wid < 8) {
+        // ---- multiplying wave: K blocks 16 s + 2 wid and + 1 of segment s,
+        // both 16-row tiles; lane (tok, kg) holds 16 codes of token tc
+        const int tc = min(tok, M - 1);     // token row of the B fragment
+        const int r0 = min(tok, rows - 1);  // weight rows of the A fragments
+        const int r1 = min(16 + tok, rows - 1);
+        const int8_t* bp = p.a + (int64_t)tc * p.lda;
+        v4i b[NC][2];
+        __builtin_amdgcn_s_setprio(3);  // ahead of the weight stream
+#pragma unroll
+        for (int sg = 0; sg < NC; ++sg)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[sg][j] = *reinterpret_cast<const v4i*>(bp + 16 * (4 * (16 * sg + 2 * wid + j) + kg));
+        __builtin_amdgcn_s_setprio(0);
+        const int8_t* a0p = wt + r0 * (NC * 1024);
+        const int8_t* a1p = wt + r1 * (NC * 1024);
+        v4i acc0 = v4i{}, acc1 = v4i{};
+#pragma unroll
+        for (int sg = 0; sg < NC; ++sg) {
+            sg_wait_ge(&ready[sg], 8);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int u = 4 * (16 * sg + 2 * wid + j) + kg;  // 16-byte unit of K
+                const v4i a0 = *reinterpret_cast<const v4i*>(a0p + ((u ^ (r0 & 15)) << 4));
+                const v4i a1 = *reinterpret_cast<const v4i*>(a1p + ((u ^ (r1 & 15)) << 4));
+                acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b[sg][j], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b[sg][j], acc1, 0, 0, 0);
+            }
+        }
+        v4i* red = reinterpret_cast<v4i*>(lds);
+        if (__builtin_amdgcn_s_memrealtime() - t_start > SG_WAVE_LIMIT_TICKS && lane == 0)
+            atomicAdd(&sg_wait_timeouts, 1u);
+        block_barrier();  // every wave is done reading the weight tile
+        red[wid * 64 + lane] = acc0;
+        red[(8 + wid) * 64 + lane] = acc1;
+    } else {
+        decode_load_tile<NC>(p.w + (int64_t)n0 * p.ldw, p.ldw, rows, wt, ready, wid - 8, lane, t_start);
+        block_barrier();  // every wave is done reading the weight tile
+    }
+
+    wait_lgkm0();
+    block_barrier();
+    if (writer)
+        decode_write<F16>(reinterpret_cast<const v4i*>(lds), wid, lane, st, sc, p.c + (int64_t)tok * p.ldc + ch);
 }
 
 template <int NC, bool F16>
@@ -271,6 +383,33 @@ inline hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
+template <int NC, bool F16>
+inline hipError_t launch_decode_pre_t(const DecodePreArgs& p, hipStream_t stream) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&decode_pre_kernel<NC, F16>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, DECODE_LDS_BYTES);
+    if (attr != hipSuccess) return attr;
+    const int grid = (p.N + p.rows - 1) / p.rows;
+    hipLaunchKernelGGL((decode_pre_kernel<NC, F16>), dim3(grid), dim3(1024),
+                       decode_lds_bytes(p.K, p.rows, false), stream, p);
+    return hipGetLastError();
+}
+
+template <bool F16>
+inline hipError_t launch_decode_pre(const DecodePreArgs& p, hipStream_t stream) {
+    switch (p.K / 1024) {
+        case 1: return launch_decode_pre_t<1, F16>(p, stream);
+        case 2: return launch_decode_pre_t<2, F16>(p, stream);
+        case 3: return launch_decode_pre_t<3, F16>(p, stream);
+        case 4: return launch_decode_pre_t<4, F16>(p, stream);
+        case 5: return launch_decode_pre_t<5, F16>(p, stream);
+        case 6: return launch_decode_pre_t<6, F16>(p, stream);
+        case 7: return launch_decode_pre_t<7, F16>(p, stream);
+        case 8: return launch_decode_pre_t<8, F16>(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
 // M <= 8 tokens, K a multiple of 1024 up to 8192, ~N/256 channels per
 // workgroup (at most 32) whose tile and the code tile fit in LDS, and 32-bit
 // buffer offsets.
@@ -279,9 +418,9 @@ inline hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream) {
 // Beyond that the CUs take several workgroups in turn, and R (at least 16,
 // so the per-workgroup quantization stays small next to its weight stream)
 // minimizes the channels the busiest CU streams: ceil(ceil(N/R) / 256) * R.
-inline int decode_rows(int N, int K) {
+inline int decode_rows(int N, int K, bool codes = true) {
     int rmax = DECODE_MAX_ROWS;
-    while (rmax >= 4 && decode_lds_bytes(K, rmax) > (size_t)DECODE_LDS_BYTES) rmax -= 4;
+    while (rmax >= 4 && decode_lds_bytes(K, rmax, codes) > (size_t)DECODE_LDS_BYTES) rmax -= 4;
     if (rmax < 4) return 0;
     const int r1 = (((N + 255) / 256) + 3) & ~3;
     if (r1 <= rmax) return r1;
@@ -297,6 +436,16 @@ inline int decode_rows(int N, int K) {
 inline bool decode_fits(int M, int N, int K, int64_t ldw) {
     if (M < 1 || M > DECODE_MAX_M || K % 1024 != 0 || K > 8192) return false;
     const int R = decode_rows(N, K);
+    if (R < 4) return false;
+    return (int64_t)R * ldw < ((int64_t)1 << 31);
+}
+
+// The pre-quantized kernel: M <= 16 tokens, codes with lda % 16 == 0 (the
+// GEMM entry points' rule), otherwise as decode_fits without the code tile.
+constexpr int DECODE_PRE_MAX_M = 16;
+inline bool decode_pre_fits(int M, int N, int K, int64_t ldw) {
+    if (M < 1 || M > DECODE_PRE_MAX_M || K % 1024 != 0 || K > 8192) return false;
+    const int R = decode_rows(N, K, false);
     if (R < 4) return false;
     return (int64_t)R * ldw < ((int64_t)1 << 31);
 }

@@ -62,6 +62,19 @@ inline q8_status check_scale(const float* s) {
 template <int EPI>
 hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
     if constexpr (EPI == EPI_CHANNEL || EPI == EPI_CHANNEL_F16) {
+        // up to 16 tokens, K a multiple of 1024 and N <= 4096 (one workgroup
+        // of at most 16 channels per CU): the decode kernel's weight stream on
+        // the codes, whole weight tile in LDS and each K segment multiplied as
+        // it lands.  Per call in a graph on rotating weight copies: 4096 x 4096
+        // 5.9-7.0 against 6.4-7.6 us, 2048 x 8192 6.6-8.6 against 8.5-9.3 us
+        // (1-16 tokens).  From 5120 channels the streaming kernel's 3-slot
+        // ring is as fast or faster (5120: 7.1-8.5 against 7.1-8.1 us; 15360
+        // and 17408, several workgroups per CU in turn: 13-20% faster).
+        if (p.N <= 4096 && p.ldx % 16 == 0 && decode_pre_fits(p.M, p.N, p.K, p.ldw)) {
+            const DecodePreArgs d{p.x, p.ldx, p.s_tok, p.w, p.ldw, p.s_w, static_cast<uint16_t*>(p.c), p.ldc,
+                                  p.M, p.N, p.K, decode_rows(p.N, p.K, false)};
+            return launch_decode_pre<EPI == EPI_CHANNEL_F16>(d, s);
+        }
         // few tokens: stream the weights once, unless the tiled kernel already
         // has half a wave of tiles or more (M > 32 with many channels)
         const bool few = p.M <= 32 || ((p.N + 127) / 128) * ((p.M + 31) / 32) < 128;
