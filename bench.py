@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--secondary decode,tiny,group128,group128_act,w8a16,
-                                 rmsnorm_quant,fp8_block,f16,m_sweep,vendor | none]
+                                 rmsnorm_quant,fp8_block,f16,m_sweep,codes_sweep,
+                                 vendor | none]
                     [--calibrate-copy]
 
 A step is one pass of the W8A8 hot path over the prefill workload
@@ -659,6 +660,24 @@ SWEEP_SHAPES = (("qkv", "w8a8", 15360, 5120), ("gate_up", "w8a8", 17408, 5120),
 SWEEP_M = (1, 2, 4, 8, 16, 32, 64, 96, 128, 192, 256, 384, 512)
 
 
+def rotating_graph_us(fn, wqs, reps):
+    """Per-call time of fn(w) over the weight copies wqs, one cycle captured
+    in a HIP graph and replayed (launch gaps included)."""
+    def cycle():
+        for wi in wqs:
+            fn(wi)
+    cycle()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cycle()
+    g.replay()
+    torch.cuda.synchronize()
+    us = events_time(g.replay, reps) / len(wqs) * 1e3
+    del g
+    return us
+
+
 def m_sweep(dev, reps=10):
     """Per-call time of each model shape at 1-512 tokens (decode,
     speculative verify, small batches, chunks): calls cycle through enough
@@ -697,28 +716,45 @@ def m_sweep(dev, reps=10):
                     q8.w8a16_mm_ws(x, wi, sc, out=y, workspace=ws)
                 nbytes = N * K + 4 * N + 2 * M * K + 2 * M * N
 
-            def graph_us(fn):
-                def cycle():
-                    for wi in wqs:
-                        fn(wi)
-                cycle()
-                torch.cuda.synchronize()
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    cycle()
-                g.replay()
-                torch.cuda.synchronize()
-                us = events_time(g.replay, reps) / ncopy * 1e3
-                del g
-                return us
-            us = graph_us(call)
+            us = rotating_graph_us(call, wqs, reps)
             row[f"M{M}"] = {"us": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
             if wsb:  # K split over a workspace (the _ws entry point)
-                us = graph_us(call_ws)
+                us = rotating_graph_us(call_ws, wqs, reps)
                 row[f"M{M}"].update({"ws_us": round(us, 2), "ws_GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
                                      "ws_bytes": wsb})
             del ws
         out[f"{name} {kind} N={N} K={K}"] = row
+        del wqs, wq
+        torch.cuda.empty_cache()
+    return out
+
+
+CODES_SHAPES = (("qkv", 15360, 5120), ("gate_up", 17408, 5120), ("o_proj", 5120, 5120),
+                ("4096x4096", 4096, 4096), ("2048x8192", 2048, 8192))
+
+
+def codes_sweep(dev, reps=10):
+    """q8_scaled_mm on int8 codes that are already at hand (as after the
+    fused RMSNorm + quantizer), per call at 1, 8 and 16 tokens, in the
+    m_sweep protocol (rotating weight copies past the last-level cache, one
+    cycle in a HIP graph): the model's W8A8 shapes and two narrower layers,
+    where the decode-structured kernel on codes runs (N <= 4096)."""
+    out = {}
+    for name, N, K in CODES_SHAPES:
+        w = synth.weights(synth.WORKLOADS["decode"], 0, N=N, K=K).to(dev)
+        wq, sc = q8.q8_quant_weight(w)
+        del w
+        ncopy = max(2, -(-600_000_000 // (N * K)))
+        wqs = [wq] + [wq.clone() for _ in range(ncopy - 1)]
+        row = {}
+        for M in (1, 8, 16):
+            x = synth.activations(synth.WORKLOADS["decode"], 0, M=M, K=K).to(dev)
+            xq, st = q8.q8_quant_per_token(x)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            us = rotating_graph_us(lambda wi: q8.q8_scaled_mm(xq, wi, st, sc, out=y), wqs, reps)
+            nbytes = N * K + 4 * N + M * K + 4 * M + 2 * M * N
+            row[f"M{M}"] = {"us": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        out[f"{name} N={N} K={K}"] = row
         del wqs, wq
         torch.cuda.empty_cache()
     return out
@@ -771,7 +807,7 @@ def vendor_gemms(dev, iters=20) -> dict:
 
 SECONDARY = {"decode": lambda dev: decode_gbs(dev), "group128": lambda dev: group_tops(dev),
              "tiny": lambda dev: tiny_latency(dev),
-             "m_sweep": lambda dev: m_sweep(dev),
+             "m_sweep": lambda dev: m_sweep(dev), "codes_sweep": lambda dev: codes_sweep(dev),
              "group128_act": lambda dev: group_act_tops(dev),
              "w8a16": lambda dev: w8a16_tflops(dev), "rmsnorm_quant": lambda dev: rmsnorm_quant_gbs(dev),
              "fp8_block": lambda dev: fp8_block_tflops(dev), "f16": lambda dev: f16_layer(dev),
@@ -786,7 +822,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary",
-                    default="decode,tiny,group128,group128_act,w8a16,rmsnorm_quant,fp8_block,f16,m_sweep,vendor",
+                    default="decode,tiny,group128,group128_act,w8a16,rmsnorm_quant,fp8_block,f16,m_sweep,"
+                            "codes_sweep,vendor",
                     help="comma list of secondary workloads, or 'none'")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()

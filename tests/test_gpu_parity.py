@@ -386,8 +386,10 @@ def test_quant_scaled_mm_token_counts(M):
     (8, 5120, 5120, 0),    # the decode workload's shape
     (5, 8192, 2048, 32),   # 32 per workgroup: two weight rows per wave
     (7, 2048, 8192, 0),    # the largest K of the one-kernel path
-    (8, 17408, 5120, 0),   # gate/up: 871 workgroups of 20 channels, several per CU
+    (8, 17408, 5120, 0),   # gate/up: quantizer + streaming kernel (the fused tile would
+                           # stream 32 KB more per CU)
     (2, 15360, 5120, 16),  # q/k/v-like: three workgroups per CU
+    (4, 13824, 5120, 0),   # 692 workgroups of 20 channels, the last wave partly filled
     (8, 5120, 8192, 0),    # tile does not fit in LDS: two-kernel path
     (9, 1024, 2048, 0),    # more tokens than the one-kernel path takes
 ])

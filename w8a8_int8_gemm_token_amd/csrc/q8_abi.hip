@@ -288,7 +288,7 @@ q8_status quant_scaled_mm_impl(const uint16_t* x, int64_t ldx, const int8_t* b, 
     if (r == Q8_OK && M > 0 && !al(xq, 16)) r = Q8_EUNSUPPORTED;
     if (r != Q8_OK || M == 0) return r;
     hipStream_t s = st(stream);
-    if (decode_fits((int)M, (int)N, (int)K, ldb)) {
+    if (decode_fits((int)M, (int)N, (int)K, ldb) && decode_beats_stream((int)N, (int)K)) {
         const DecodeArgs d{x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok,
                            (int)M, (int)N, (int)K, decode_rows((int)N, (int)K)};
         return hip_status(launch_decode<F16>(d, s));

@@ -310,6 +310,22 @@ inline int sg_rows(int N) {
     return best;
 }
 
+// The one-call layer at up to 8 tokens: the fused decode kernel (every
+// workgroup quantizes the rows for itself while its weights stream) unless
+// its whole-tile LDS budget makes the busiest CU stream 32 KB or more of
+// weights beyond what the row quantizer + streaming kernel would.  Per call
+// in a graph on rotating weight copies, 1-8 tokens: at 17408 x 5120 (the
+// fused kernel's 871 workgroups of 20 rows, 80 rows per CU, against 726 of
+// 24, 72 rows) 21.1-23.7 us fused against 20.4-21.0 us; at 13824 x 5120
+// (60 against 56 rows per CU) 16.5-18.4 us fused against 18.0-19.0.
+inline bool decode_beats_stream(int N, int K) {
+    const int rf = decode_rows(N, K), rs = sg_rows(N);
+    if (rf < 4) return false;
+    const int64_t cf = (int64_t)((((int64_t)N + rf - 1) / rf + 255) / 256) * rf;
+    const int64_t cs = (int64_t)((((int64_t)N + rs - 1) / rs + 255) / 256) * rs;
+    return (cf - cs) * K < 32768;
+}
+
 // M <= max_m, K a multiple of 128, 32-bit buffer offsets for the tile.
 inline bool sg_fits(int M, int N, int K, int64_t ldw, int max_m) {
     if (M < 1 || M > max_m || K % 128 != 0 || (K + SG_SEG - 1) / SG_SEG > SG_MAX_SEG) return false;
