@@ -74,9 +74,11 @@ __device__ __forceinline__ v2u i8x4_to_bf16x4(u32 d) {
     const float f1 = (float)(int8_t)((d >> 8) & 0xFF);
     const float f2 = (float)(int8_t)((d >> 16) & 0xFF);
     const float f3 = (float)(int8_t)(d >> 24);
-    // the conversions are exact, so truncating to the top 16 bits is exact
-    return v2u{(__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u),
-               (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u)};
+    // the conversions are exact, so truncating to the top 16 bits is exact;
+    // one v_perm_b32 per pair takes bytes 2-3 of each (the shift + and-or
+    // the plain expression compiles to is two instructions)
+    return v2u{__builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u),
+               __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u)};
 }
 
 // 4 int8 codes (one dword) -> 4 exact fp16 values (two dwords): |q| <= 128
