@@ -72,9 +72,9 @@ GEMM_COUNTERS = {
     "sources_sha256": {
         "gemm_big.hpp": "8fdf1c7bc31a1e14bde9abe6fe27a066c4ac91c62b301cdfb7a258b52749a483",
         "gemm_i8.hpp": "febc8517b77d8095609f9562f5666c5cbbab9ae7ee7319a48cf8b27227353afa",
-        "q8_device.hpp": "93921317d9ee2061ee8f6a130188921aef7ffc81f9e84a6867f9e2ea825e1a33",
+        "q8_device.hpp": "ed736ec37d5cbc69b0a47c089b8e905c0402c85d7e50b9ebeef5c8e1b0b2ec0e",
     },
-    "fetch_kib": 367721.1, "write_kib": 262771.8,
+    "fetch_kib": 367718.6, "write_kib": 262624.1,
     "copy_kib": 524288.0, "copy_fetch_kib": 262155.5, "copy_write_kib": 524288.0,
 }
 
