@@ -82,10 +82,15 @@ __device__ __forceinline__ v2u i8x4_to_bf16x4(u32 d) {
 }
 
 // 4 int8 codes (one dword) -> 4 exact fp16 values (two dwords): |q| <= 128
-// fits the 11-bit fp16 significand.
+// fits the 11-bit fp16 significand, so the round-toward-zero pack of the
+// exact fp32 values (one v_cvt_pkrtz_f16_f32 per pair) is exact.
 __device__ __forceinline__ v2u i8x4_to_f16x4(u32 d) {
-    return v2u{pack_f16x2((float)(int8_t)(d & 0xFF), (float)(int8_t)((d >> 8) & 0xFF)),
-               pack_f16x2((float)(int8_t)((d >> 16) & 0xFF), (float)(int8_t)(d >> 24))};
+    const float f0 = (float)(int8_t)(d & 0xFF);
+    const float f1 = (float)(int8_t)((d >> 8) & 0xFF);
+    const float f2 = (float)(int8_t)((d >> 16) & 0xFF);
+    const float f3 = (float)(int8_t)(d >> 24);
+    return v2u{__builtin_bit_cast(u32, __builtin_amdgcn_cvt_pkrtz(f0, f1)),
+               __builtin_bit_cast(u32, __builtin_amdgcn_cvt_pkrtz(f2, f3))};
 }
 template <bool F16>
 __device__ __forceinline__ v2u i8x4_to_h16x4(u32 d) {
