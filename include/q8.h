@@ -158,8 +158,9 @@ q8_status w8a16_mm(const q8_bf16 *x, int64_t ldx, const int8_t *w,
  * The quantized activations and their scales are written to the caller's
  * xq / scale_tok buffers (they are outputs, and the GEMM's inputs).  For
  * M <= 8 and K a multiple of 1024 up to 8192 one kernel does both (every
- * workgroup quantizes the rows for itself while its weights stream in).
- * Otherwise two kernels run back to back on `stream`: the row quantizer,
+ * workgroup quantizes the rows for itself while its weights stream in), and
+ * so does one for small layers (M <= 16, K below 1024, at most 16 MB of
+ * weights).  Otherwise two kernels run back to back on `stream`: the row quantizer,
  * then the GEMM of q8_scaled_mm (for few tokens a weight-streaming kernel
  * that reads each weight byte once, else the tiled GEMM).
  *   x [M, ldx] bf16; b [N, ldb] int8; scale_ch [N]; c [M, ldc] bf16;

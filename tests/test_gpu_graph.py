@@ -15,7 +15,9 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("M,K,N", [(1, 1024, 512), (8, 1024, 512), (300, 1024, 512),
                                    (8, 5120, 5120),    # one-kernel decode, five K segments
                                    (3, 5120, 15360),   # ... three workgroups per CU
-                                   (16, 5120, 5120)])  # quantizer + weight-streaming kernel
+                                   (16, 5120, 5120),   # quantizer + weight-streaming kernel
+                                   (16, 256, 128),     # the small-layer kernel (the tiny workload)
+                                   (5, 640, 2064)])    # ... three workgroups, the last one ragged
 def test_graph_replay_matches_eager(M, K, N):
     dev = "cuda:0"
     x, w = synth.custom(M, K, N, seed=40 + M, outlier_cols=8)

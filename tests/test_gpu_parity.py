@@ -462,6 +462,54 @@ def test_scaled_mm_few_tokens_partial_segment(M, N, K, pad):
 
 
 @pytest.mark.parametrize("M,N,K,pad", [
+    (16, 128, 256, 0),      # the tiny workload's shape: two workgroups
+    (1, 16, 128, 0),        # one wave's channels, one K block pair
+    (5, 1040, 640, 16),     # last workgroup ragged (16 of 64 channels), strided operands
+    (8, 2048, 896, 16),     # the largest K below 1024 (code rows of 56 units)
+    (9, 64, 384, 0),        # 24 units per code row
+    (12, 4096, 512, 0),
+    (7, 208, 896, 32),
+    (13, 512, 128, 16),     # 16 tokens' tile, 8 units per code row
+])
+def test_small_layer_kernel(M, N, K, pad):
+    """Few tokens with K < 1024 and a small weight matrix: the one-call
+    layer in one kernel (weight fragments straight to registers, the rows
+    quantized into an LDS code tile, 16 x 16 MFMA tiles). Codes,
+    scales and outputs against the oracle, with a zero row, a near-tie row,
+    strided x, w and y (padding untouched), and the fp16 variant."""
+    say("small layer kernel", M, N, K, pad)
+    xf, wf = synth.custom(M, K + pad, N, seed=19 * M + N + K, outlier_cols=max(1, K // 64))
+    x = xf[:, :K].contiguous()
+    x[M // 2] = 0
+    if M > 2:  # a row whose codes come from the division fallback
+        x[M - 1, :4] = torch.tensor([1.0, 0.5, -0.5, 0.75])
+        x[M - 1, 4:] = 0
+    xf[:, :K] = x
+    w = wf[:, :K].contiguous()
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sc_ref = oracle.quant_weight(w.numpy())
+    y_ref = oracle.scaled_mm(xq_ref, wq_ref, st_ref, sc_ref)
+    wq_full = torch.zeros((N, K + pad), dtype=torch.int8, device=DEV)
+    wq_full[:, :K] = dev(torch.from_numpy(wq_ref))
+    wq = wq_full[:, :K]
+    sc = dev(torch.from_numpy(sc_ref))
+    yfull = torch.full((M, N + pad), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    y, xq, st = q8.q8_quant_scaled_mm(dev(xf)[:, :K], wq, sc, out=yfull[:, :N])
+    np.testing.assert_array_equal(host(st).numpy(), st_ref)
+    np.testing.assert_array_equal(host(xq).numpy(), xq_ref)
+    assert_ulp1(bits(host(y).contiguous()), y_ref, f"small layer {M}x{N}x{K}")
+    if pad:
+        assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
+    xh = x.float().half()
+    xqh_ref, sth_ref = oracle.quant_per_token_f16(host(xh).view(torch.int16).numpy().view(np.uint16))
+    yh, xqh, sth = q8.q8_quant_scaled_mm_f16(dev(xh), wq, sc)
+    np.testing.assert_array_equal(host(sth).numpy(), sth_ref)
+    np.testing.assert_array_equal(host(xqh).numpy(), xqh_ref)
+    assert_ulp1(host(yh).view(torch.int16).numpy().view(np.uint16),
+                oracle.scaled_mm_f16(xqh_ref, wq_ref, sth_ref, sc_ref), f"small layer f16 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,pad", [
     (1, 16, 1024, 0),       # one workgroup of 4 channels, one segment
     (16, 16, 8192, 16),     # 16 tokens, eight segments, strided operands
     (9, 1040, 2048, 16),    # 8 channels per workgroup, the last one ragged

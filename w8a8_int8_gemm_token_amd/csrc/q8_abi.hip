@@ -17,6 +17,7 @@
 #include "gemm_big.hpp"
 #include "gemm_w16.hpp"
 #include "stream_gemm.hpp"
+#include "small_fused.hpp"
 #include "fp8.hpp"
 #include "splitk.hpp"
 
@@ -292,6 +293,10 @@ q8_status quant_scaled_mm_impl(const uint16_t* x, int64_t ldx, const int8_t* b, 
         const DecodeArgs d{x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok,
                            (int)M, (int)N, (int)K, decode_rows((int)N, (int)K)};
         return hip_status(launch_decode<F16>(d, s));
+    }
+    if (small_fits((int)M, (int)N, (int)K, ldb)) {
+        const SmallArgs sa{x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok, (int)M, (int)N, (int)K};
+        return hip_status(launch_small<F16>(sa, s));
     }
     hipError_t e = run_quant<F16>(x, ldx, xq, K, scale_tok, (int)M, (int)K, s);
     if (e != hipSuccess) return Q8_EHIP;
