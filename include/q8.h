@@ -157,7 +157,8 @@ q8_status w8a16_mm(const q8_bf16 *x, int64_t ldx, const int8_t *w,
  * quantization of x (as q8_quant_per_token) followed by q8_scaled_mm.
  * The quantized activations and their scales are written to the caller's
  * xq / scale_tok buffers (they are outputs, and the GEMM's inputs).  For
- * M <= 8 and K a multiple of 1024 up to 8192 one kernel does both (every
+ * M <= 8 and K up to 8192 (a few hundred workgroups of channels at most)
+ * one kernel does both (every
  * workgroup quantizes the rows for itself while its weights stream in), and
  * so does one for small layers (M <= 16, K below 1024, at most 16 MB of
  * weights).  Otherwise two kernels run back to back on `stream`: the row quantizer,

@@ -392,6 +392,12 @@ def test_quant_scaled_mm_token_counts(M):
     (4, 13824, 5120, 0),   # 692 workgroups of 20 channels, the last wave partly filled
     (8, 5120, 8192, 0),    # tile does not fit in LDS: two-kernel path
     (9, 1024, 2048, 0),    # more tokens than the one-kernel path takes
+    # K a multiple of 128 only: the last 1024-wide segment is partial
+    (8, 3584, 3584, 0),    # 3.5 segments
+    (1, 18944, 3584, 16),  # several workgroups per CU, strided operands
+    (5, 1040, 1152, 0),    # one full segment and 128 more
+    (7, 2048, 7296, 16),   # eight segments, the last of 128
+    (3, 2048, 4352, 16),
 ])
 def test_decode_one_call_shapes(M, N, K, pad):
     """The one-call layer at decode batch sizes (one kernel for M <= 8 when

@@ -1,6 +1,6 @@
 // decode_fused.hpp -- the whole W8A8 layer for decode-sized batches in one
-// kernel: per-token quantization of X (M <= 8 rows) and the INT8 GEMM with
-// the per-token x per-channel epilogue.
+// kernel: per-token quantization of X (M <= 8 rows, K a multiple of 128 up
+// to 8192) and the INT8 GEMM with the per-token x per-channel epilogue.
 //
 // Decode streams the whole weight matrix once per call and is bound by HBM
 // bandwidth ("Qwen3.8-27B-INT8-W8A8", section "Throughput": decode is
@@ -90,24 +90,29 @@ __device__ __forceinline__ void wait_lgkm0() {
 }
 
 // Loading wave d (0..7) of a decode workgroup: rows d, d + 8, ... of the
-// workgroup's weight tile (rows x K, row stride K in LDS), segment by
-// segment, 1 KB of one row per instruction (lane l moves global unit
-// l ^ (r & 15) of the row's block to LDS unit l); once its rows of segment
-// s landed (vmcnt) the wave increments ready[s].
-template <int NC>
-__device__ __forceinline__ void decode_load_tile(const int8_t* w, int64_t ldw, int rows, int8_t* wt,
+// workgroup's weight tile (rows x K, row stride KP = 1024 NC in LDS),
+// segment by segment, 1 KB of one row per instruction (lane l moves global
+// unit l ^ (r & 15) of the row's block to LDS unit l; a unit past K gets an
+// offset beyond the buffer resource and lands as zeros); once its rows of
+// segment s landed (vmcnt) the wave increments ready[s].
+template <int NC, bool PK>
+__device__ __forceinline__ void decode_load_tile(const int8_t* w, int64_t ldw, int rows, int K, int8_t* wt,
                                                  int* ready, int d, int lane, uint64_t t_start) {
-    constexpr int K = NC * 1024;
+    constexpr int KP = NC * 1024;
+    if constexpr (!PK) K = KP;  // whole segments: no unit is past K
     const int cnt = rows > d ? (rows - d + 7) / 8 : 0;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)((int64_t)rows * ldw));
 #pragma unroll
     for (int sg = 0; sg < NC; ++sg) {
         for (int j = 0; j < cnt; ++j) {
             const int r = d + 8 * j;
-            const int voff = r * (int)ldw + sg * 1024 + ((lane ^ (r & 15)) << 4);
+            const int ku = sg * 1024 + ((lane ^ (r & 15)) << 4);  // K byte of this lane's unit
+            // past K: offset 2^31, beyond any resource here (decode_fits keeps
+            // rows * ldw below 2^31), which reads as zero
+            const int voff = !PK || ku < K ? r * (int)ldw + ku : INT32_MIN;
             // cache policy 2 = non-temporal: every weight byte is read once
             // per call (measured 0.4-0.6 us faster per call at N = K = 5120)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (Q8_LDS void*)(wt + r * K + sg * 1024), 16, voff, 0, 0,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (Q8_LDS void*)(wt + r * KP + sg * 1024), 16, voff, 0, 0,
                                                      2);
         }
     }
@@ -140,11 +145,16 @@ __device__ __forceinline__ void decode_write(const v4i* red, int wid, int lane, 
     *reinterpret_cast<v2u*>(out) = o;
 }
 
-// NC = K / 1024.  F16: fp16 activations and outputs instead of bf16.
-template <int NC, bool F16>
+// NC = ceil(K / 1024), K a multiple of 128.  PK: the last K segment is
+// partial (its weights past K land as zeros, and whatever the code tile
+// holds past K multiplies them); without it K = 1024 NC and the kernel
+// carries none of the checks (they cost 0.25 us per call at 8 tokens,
+// 5120 x 5120).  F16: fp16 activations and outputs instead of bf16.
+template <int NC, bool PK, bool F16>
 __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
-    constexpr int K = NC * 1024;
-    constexpr int NQ = 2 * NC;  // 16-byte activation chunks per lane (one row per wave)
+    constexpr int KP = NC * 1024;  // row stride of both LDS tiles
+    constexpr int NQ = 2 * NC;     // 16-byte activation chunks per lane (one row per wave)
+    const int K = PK ? p.K : KP;
     extern __shared__ __attribute__((aligned(1024))) int8_t lds[];
     __shared__ int ready[NC];  // loading waves whose rows of K segment s landed (8 = all)
     __shared__ int qdone;      // quantizing waves done (8 = the code tile is complete)
@@ -155,9 +165,9 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
     const int R = p.rows;
     const int n0 = blockIdx.x * R;
     const int rows = min(R, p.N - n0);
-    int8_t* wt = lds;                                         // [R][K] weight tile
-    int8_t* ct = lds + decode_wt_bytes(K, R);                 // [8][K] code tile
-    float* row_scale_s = reinterpret_cast<float*>(ct + DECODE_MAX_M * K);  // [8] token scales
+    int8_t* wt = lds;                                         // [R][KP] weight tile
+    int8_t* ct = lds + decode_wt_bytes(KP, R);                // [8][KP] code tile
+    float* row_scale_s = reinterpret_cast<float*>(ct + DECODE_MAX_M * KP);  // [8] token scales
 
     // ---- epilogue operands of the output waves (wave t < 2, lane l: token
     // l % 16, channels n0 + 16t + 4(l / 16) + e), fetched first
@@ -183,8 +193,9 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
         v4u v[NQ];
         if (has_row) {
             const v4u* xr = reinterpret_cast<const v4u*>(p.x + (int64_t)m * p.ldx);
+            const int last = K / 8 - 1;  // past the row end: its last chunk again
 #pragma unroll
-            for (int i = 0; i < NQ; ++i) v[i] = xr[lane + 64 * i];
+            for (int i = 0; i < NQ; ++i) v[i] = xr[PK ? min(lane + 64 * i, last) : lane + 64 * i];
         }
         if (has_row) {
             v2h mx = v2h{0, 0};
@@ -200,7 +211,7 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
                 const v2u cd = codes8<F16>(v[i], q);
                 const int c8 = lane + 64 * i;  // 8-byte code piece
                 const int uu = c8 >> 1;
-                *reinterpret_cast<v2u*>(ct + m * K + ((uu ^ m) << 4) + ((c8 & 1) << 3)) = cd;
+                *reinterpret_cast<v2u*>(ct + m * KP + ((uu ^ m) << 4) + ((c8 & 1) << 3)) = cd;
             }
         }
         wait_lgkm0();  // this wave's codes are in the tile
@@ -214,9 +225,9 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
         const int tc = min(tok, M - 1);     // token row of the B fragment
         const int r0 = min(tok, rows - 1);  // weight rows of the A fragments
         const int r1 = min(16 + tok, rows - 1);
-        const int8_t* bp = ct + tc * K;
-        const int8_t* a0p = wt + r0 * K;
-        const int8_t* a1p = wt + r1 * K;
+        const int8_t* bp = ct + tc * KP;
+        const int8_t* a0p = wt + r0 * KP;
+        const int8_t* a1p = wt + r1 * KP;
         v4i acc0 = v4i{}, acc1 = v4i{};
 #pragma unroll
         for (int sg = 0; sg < NC; ++sg) {
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
         red[wid * 64 + lane] = acc0;
         red[(8 + wid) * 64 + lane] = acc1;
     } else {
-        decode_load_tile<NC>(p.w + (int64_t)n0 * p.ldw, p.ldw, rows, wt, ready, wid - 8, lane, t_start);
+        decode_load_tile<NC, PK>(p.w + (int64_t)n0 * p.ldw, p.ldw, rows, K, wt, ready, wid - 8, lane, t_start);
         block_barrier();  // every wave is done reading the weight tile
     }
 
@@ -251,8 +262,9 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(DecodeArgs p) {
         // from workgroup q (mod the grid), so that no workgroup carries all
         for (int q = blockIdx.x; q < M * NC; q += gridDim.x) {
             const int m = q / NC, u = 64 * (q - m * NC) + lane;
-            *reinterpret_cast<v4u*>(p.xq + (int64_t)m * K + 16 * u) =
-                *reinterpret_cast<const v4u*>(ct + m * K + ((u ^ m) << 4));
+            if (!PK || 16 * u < K)
+                *reinterpret_cast<v4u*>(p.xq + (int64_t)m * K + 16 * u) =
+                    *reinterpret_cast<const v4u*>(ct + m * KP + ((u ^ m) << 4));
         }
     }
     if (writer)
@@ -346,7 +358,8 @@ __global__ __launch_bounds__(1024) void decode_pre_kernel(DecodePreArgs p) {
         red[wid * 64 + lane] = acc0;
         red[(8 + wid) * 64 + lane] = acc1;
     } else {
-        decode_load_tile<NC>(p.w + (int64_t)n0 * p.ldw, p.ldw, rows, wt, ready, wid - 8, lane, t_start);
+        decode_load_tile<NC, false>(p.w + (int64_t)n0 * p.ldw, p.ldw, rows, NC * 1024, wt, ready, wid - 8, lane,
+                                    t_start);
         block_barrier();  // every wave is done reading the weight tile
     }
 
@@ -356,29 +369,34 @@ __global__ __launch_bounds__(1024) void decode_pre_kernel(DecodePreArgs p) {
         decode_write<F16>(reinterpret_cast<const v4i*>(lds), wid, lane, st, sc, p.c + (int64_t)tok * p.ldc + ch);
 }
 
-template <int NC, bool F16>
+template <int NC, bool PK, bool F16>
 inline hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t stream) {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_fused_kernel<NC, F16>),
+        reinterpret_cast<const void*>(&decode_fused_kernel<NC, PK, F16>),
         hipFuncAttributeMaxDynamicSharedMemorySize, DECODE_LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const int grid = (p.N + p.rows - 1) / p.rows;
-    hipLaunchKernelGGL((decode_fused_kernel<NC, F16>), dim3(grid), dim3(1024),
-                       decode_lds_bytes(p.K, p.rows), stream, p);
+    hipLaunchKernelGGL((decode_fused_kernel<NC, PK, F16>), dim3(grid), dim3(1024),
+                       decode_lds_bytes(NC * 1024, p.rows), stream, p);
     return hipGetLastError();
+}
+
+template <int NC, bool F16>
+inline hipError_t launch_decode_nc(const DecodeArgs& p, hipStream_t stream) {
+    return p.K == NC * 1024 ? launch_decode_t<NC, false, F16>(p, stream) : launch_decode_t<NC, true, F16>(p, stream);
 }
 
 template <bool F16>
 inline hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream) {
-    switch (p.K / 1024) {
-        case 1: return launch_decode_t<1, F16>(p, stream);
-        case 2: return launch_decode_t<2, F16>(p, stream);
-        case 3: return launch_decode_t<3, F16>(p, stream);
-        case 4: return launch_decode_t<4, F16>(p, stream);
-        case 5: return launch_decode_t<5, F16>(p, stream);
-        case 6: return launch_decode_t<6, F16>(p, stream);
-        case 7: return launch_decode_t<7, F16>(p, stream);
-        case 8: return launch_decode_t<8, F16>(p, stream);
+    switch ((p.K + 1023) / 1024) {
+        case 1: return launch_decode_nc<1, F16>(p, stream);
+        case 2: return launch_decode_nc<2, F16>(p, stream);
+        case 3: return launch_decode_nc<3, F16>(p, stream);
+        case 4: return launch_decode_nc<4, F16>(p, stream);
+        case 5: return launch_decode_nc<5, F16>(p, stream);
+        case 6: return launch_decode_nc<6, F16>(p, stream);
+        case 7: return launch_decode_nc<7, F16>(p, stream);
+        case 8: return launch_decode_nc<8, F16>(p, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -410,17 +428,18 @@ inline hipError_t launch_decode_pre(const DecodePreArgs& p, hipStream_t stream) 
     return hipErrorInvalidValue;
 }
 
-// M <= 8 tokens, K a multiple of 1024 up to 8192, ~N/256 channels per
-// workgroup (at most 32) whose tile and the code tile fit in LDS, and 32-bit
-// buffer offsets.
+// M <= 8 tokens, K a multiple of 128 up to 8192, ~N/256 channels per
+// workgroup (at most 32) whose tile and the code tile fit in LDS (rows
+// padded to whole 1024-wide segments), and 32-bit buffer offsets.
 // Channels per workgroup (a multiple of 4), or 0 if no size fits LDS.  Up
 // to 256 * 32 channels, one workgroup per CU: R = N / 256 rounded up.
 // Beyond that the CUs take several workgroups in turn, and R (at least 16,
 // so the per-workgroup quantization stays small next to its weight stream)
 // minimizes the channels the busiest CU streams: ceil(ceil(N/R) / 256) * R.
 inline int decode_rows(int N, int K, bool codes = true) {
+    const int KP = (K + 1023) / 1024 * 1024;
     int rmax = DECODE_MAX_ROWS;
-    while (rmax >= 4 && decode_lds_bytes(K, rmax, codes) > (size_t)DECODE_LDS_BYTES) rmax -= 4;
+    while (rmax >= 4 && decode_lds_bytes(KP, rmax, codes) > (size_t)DECODE_LDS_BYTES) rmax -= 4;
     if (rmax < 4) return 0;
     const int r1 = (((N + 255) / 256) + 3) & ~3;
     if (r1 <= rmax) return r1;
@@ -434,7 +453,7 @@ inline int decode_rows(int N, int K, bool codes = true) {
 }
 
 inline bool decode_fits(int M, int N, int K, int64_t ldw) {
-    if (M < 1 || M > DECODE_MAX_M || K % 1024 != 0 || K > 8192) return false;
+    if (M < 1 || M > DECODE_MAX_M || K % 128 != 0 || K > 8192) return false;
     const int R = decode_rows(N, K);
     if (R < 4) return false;
     return (int64_t)R * ldw < ((int64_t)1 << 31);

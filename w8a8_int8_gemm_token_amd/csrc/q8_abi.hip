@@ -289,15 +289,18 @@ q8_status quant_scaled_mm_impl(const uint16_t* x, int64_t ldx, const int8_t* b, 
     if (r == Q8_OK && M > 0 && !al(xq, 16)) r = Q8_EUNSUPPORTED;
     if (r != Q8_OK || M == 0) return r;
     hipStream_t s = st(stream);
+    // one kernel for the whole layer where one applies: below K = 1024 the
+    // small-layer kernel, then the decode kernel (up to 8 tokens), then the
+    // small-layer kernel at K = 1024
+    const bool small = small_fits((int)M, (int)N, (int)K, ldb);
+    const SmallArgs sa{x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok, (int)M, (int)N, (int)K};
+    if (small && K < SMALL_MAX_K) return hip_status(launch_small<F16>(sa, s));
     if (decode_fits((int)M, (int)N, (int)K, ldb) && decode_beats_stream((int)N, (int)K)) {
         const DecodeArgs d{x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok,
                            (int)M, (int)N, (int)K, decode_rows((int)N, (int)K)};
         return hip_status(launch_decode<F16>(d, s));
     }
-    if (small_fits((int)M, (int)N, (int)K, ldb)) {
-        const SmallArgs sa{x, ldx, b, ldb, scale_ch, c, ldc, xq, scale_tok, (int)M, (int)N, (int)K};
-        return hip_status(launch_small<F16>(sa, s));
-    }
+    if (small) return hip_status(launch_small<F16>(sa, s));
     hipError_t e = run_quant<F16>(x, ldx, xq, K, scale_tok, (int)M, (int)K, s);
     if (e != hipSuccess) return Q8_EHIP;
     GemmArgs p{xq, K, b, ldb, scale_tok, scale_ch, c, ldc, (int)M, (int)N, (int)K};
