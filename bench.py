@@ -72,9 +72,9 @@ GEMM_COUNTERS = {
     "sources_sha256": {
         "gemm_big.hpp": "8fdf1c7bc31a1e14bde9abe6fe27a066c4ac91c62b301cdfb7a258b52749a483",
         "gemm_i8.hpp": "febc8517b77d8095609f9562f5666c5cbbab9ae7ee7319a48cf8b27227353afa",
-        "q8_device.hpp": "ed736ec37d5cbc69b0a47c089b8e905c0402c85d7e50b9ebeef5c8e1b0b2ec0e",
+        "q8_device.hpp": "ccd2b93eca43b76b27e87299ed951a8a59342afdb931f850f87bdacbbe91dfc2",
     },
-    "fetch_kib": 367718.6, "write_kib": 262624.1,
+    "fetch_kib": 367718.4, "write_kib": 262611.4,
     "copy_kib": 524288.0, "copy_fetch_kib": 262155.5, "copy_write_kib": 524288.0,
 }
 
