@@ -891,6 +891,48 @@ def test_group128_shapes(M, N, K):
     assert_ulp1(bits(host(y)), y_ref, f"group128 {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,pad", [
+    (1, 16, 128, 0),         # one block, one workgroup of 4 channels
+    (8, 5120, 5120, 16),     # the decode shape, strided operands
+    (16, 1040, 1152, 0),     # a partial last K segment (9 blocks), ragged workgroups
+    (17, 4112, 3072, 16),    # two token groups
+    (33, 272, 896, 0),       # four token groups, one partial segment
+    (64, 5120, 17408, 0),    # the down projection's K: 136 blocks, 17 segments
+    (5, 17408, 5120, 0),     # several workgroups per CU
+])
+def test_group128_few_tokens_streaming(M, N, K, pad):
+    """Up to 64 tokens: both group-scaled GEMMs stream the weights once,
+    each multiplying wave folding its tile's 128-wide block sums in
+    ascending order. Against the oracle with strided codes, weights and
+    output (padding untouched), a zero row, and the fp16 per-group form."""
+    say("group128 streaming", M, N, K, pad)
+    x, w = synth.custom(M, K, N, seed=23 * M + N + K, outlier_cols=max(1, K // 100))
+    x[M // 2] = 0
+    xq_ref, st_ref = oracle.quant_per_token(bits(x))
+    wq_ref, sg_ref = oracle.quant_weight(w.numpy(), group=128)
+    xg_ref, sx_ref = oracle.quant_per_group128(bits(x))
+
+    def strided(a, rows, cols):
+        full = torch.full((rows, cols + pad), 99, dtype=torch.int8, device=DEV)
+        full[:, :cols] = dev(torch.from_numpy(a))
+        return full[:, :cols]
+    wq, sg = strided(wq_ref, N, K), dev(torch.from_numpy(sg_ref))
+    yfull = torch.full((M, N + pad), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    y = q8.q8_scaled_mm_group128(strided(xq_ref, M, K), wq, dev(torch.from_numpy(st_ref)), sg, out=yfull[:, :N])
+    assert_ulp1(bits(host(y).contiguous()), oracle.scaled_mm_group128(xq_ref, wq_ref, st_ref, sg_ref),
+                f"group128 streaming {M}x{N}x{K}")
+    if pad:
+        assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
+    y = q8.q8_scaled_mm_group128_act(strided(xg_ref, M, K), wq, dev(torch.from_numpy(sx_ref)), sg)
+    assert_ulp1(bits(host(y)), oracle.scaled_mm_group128_act(xg_ref, wq_ref, sx_ref, sg_ref),
+                f"group128 act streaming {M}x{N}x{K}")
+    yh = q8.q8_scaled_mm_group128_act_f16(strided(xg_ref, M, K), wq, dev(torch.from_numpy(sx_ref)), sg)
+    assert_ulp1(host(yh).view(torch.int16).numpy().view(np.uint16),
+                oracle.scaled_mm_group128_act_f16(xg_ref, wq_ref, sx_ref, sg_ref),
+                f"group128 act f16 streaming {M}x{N}x{K}")
+    assert q8.q8_wait_timeouts(reset=True) == 0
+
+
 def test_group_scaled_large_tiles_ragged():
     """Enough tiles for the 256 x 128 group-scaled configuration, with a
     ragged last tile in M and in N: both group-scaled epilogues, sampled

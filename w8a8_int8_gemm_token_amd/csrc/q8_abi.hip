@@ -18,6 +18,7 @@
 #include "gemm_w16.hpp"
 #include "stream_gemm.hpp"
 #include "small_fused.hpp"
+#include "stream_group.hpp"
 #include "fp8.hpp"
 #include "splitk.hpp"
 
@@ -128,6 +129,13 @@ hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
 // CU.
 template <int EPI>
 hipError_t run_gemm_grouped(const GemmArgs& p, hipStream_t s) {
+    // up to 64 tokens: stream the weights once (stream_group.hpp)
+    if (sgg_fits(p.M, p.N, p.K, p.ldx, p.ldw)) {
+        const StreamGroupArgs q{p.x, p.ldx, p.w, p.ldw, p.s_tok, p.s_w, static_cast<uint16_t*>(p.c), p.ldc,
+                                p.M, p.N, p.K, 0, 0};
+        constexpr bool ACT = EPI != EPI_GROUP;
+        return launch_stream_group<ACT, EPI == EPI_GROUP_ACT_F16>(q, s);
+    }
     if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
     // The first of 32, 64 and 128 tokens per tile that gives at most 256
     // workgroups (one per CU), else 256 (measured over 65-1024 tokens at
