@@ -674,10 +674,14 @@ def test_quant_scaled_mm_9_16_tokens(M, N, K, pad):
         assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
 
 
-@pytest.mark.parametrize("M,N,K", [(97, 9216, 384), (200, 9216, 256), (450, 8192, 128)])
+@pytest.mark.parametrize("M,N,K", [(97, 9216, 384), (200, 9216, 256), (450, 8192, 128),
+                                   # over 512 tiles of 128 x 128: one round of 256 x 256
+                                   (520, 16384, 256), (601, 16400, 384)])
 def test_scaled_mm_mid_token_tiles(M, N, K):
-    """65-512 tokens where 256 x 256 tiles are too few: 32 x 128, 64 x 128
-    and 128 x 128 tiles by workgroup count (ragged M), against the oracle."""
+    """65-1024 tokens where 256 x 256 tiles are too few to fill the chip:
+    32 x 128, 64 x 128 and 128 x 128 tiles by workgroup count, and 256 x 256
+    tiles where 128 x 128 would need a second round (ragged M and N), every
+    output against the oracle."""
     say("scaled_mm mid tiles", M, N, K)
     x, w = synth.custom(M, K, N, seed=M + N + K, outlier_cols=4)
     xq_ref, st_ref = oracle.quant_per_token(bits(x))
@@ -787,7 +791,7 @@ def _at_allocation_end(t: torch.Tensor) -> torch.Tensor:
     return v
 
 
-@pytest.mark.parametrize("M,N,K", [(4100, 4000, 512),    # 256 x 384; group 256 x 128; W8A16 256 x 320
+@pytest.mark.parametrize("M,N,K", [(4100, 4000, 512),    # 256 x 384; group 128 x 128; W8A16 256 x 320
                                    (4000, 4000, 384),    # 256 x 256; W8A16 on the 256 x 128 tiles
                                    (1100, 4112, 384),    # 128 x 128 tiles
                                    (300, 1040, 256)])    # 32 x 128 tiles
@@ -838,7 +842,7 @@ def test_quant_per_group128(M, K, pad):
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (8, 256, 1024), (64, 144, 640),
                                    (65, 272, 1152), (200, 384, 2048), (257, 128, 256),
-                                   # tiles by workgroup count: 64 x 128, 128 x 128, 256 x 128
+                                   # tiles by workgroup count: 64 x 128, then 128 x 128
                                    (300, 5120, 256), (600, 5120, 256), (1100, 5120, 128)])
 def test_scaled_mm_group128_act_shapes(M, N, K):
     say("group128 act", M, N, K)
@@ -876,7 +880,7 @@ def test_group128_act_full_size_every_row():
 
 @pytest.mark.parametrize("M,N,K", [(16, 128, 256), (33, 144, 384), (130, 256, 1024),
                                    (257, 128, 128),
-                                   # tiles by workgroup count: 32, 64, 128 and 256 tokens
+                                   # tiles by workgroup count: 32, 64 and 128 tokens
                                    (100, 1040, 512), (300, 5120, 256), (600, 5120, 256),
                                    (1100, 5120, 128)])
 def test_group128_shapes(M, N, K):
@@ -934,9 +938,9 @@ def test_group128_few_tokens_streaming(M, N, K, pad):
 
 
 def test_group_scaled_large_tiles_ragged():
-    """Enough tiles for the 256 x 128 group-scaled configuration, with a
-    ragged last tile in M and in N: both group-scaled epilogues, sampled
-    rows (including the ragged ones) against the oracle."""
+    """Several 128 x 128 group-scaled tiles per CU (more than two rounds),
+    with a ragged last tile in M and in N: both group-scaled epilogues,
+    sampled rows (including the ragged ones) against the oracle."""
     M, N, K = 2100, 3728, 640
     say("group-scaled large tiles", M, N, K)
     x, w = synth.custom(M, K, N, seed=97, outlier_cols=5)

@@ -59,8 +59,10 @@ inline q8_status check_scale(const float* s) {
 }
 
 // Tile configurations of the INT8 GEMM, chosen by the problem size: 32-token
-// tiles for small batches, 256 x 256 tiles (8 waves of 128 x 64) once there
-// are enough of them to fill the 256 CUs, 128 x 128 tiles in between.
+// tiles for small batches, 256 x 384 or 256 x 256 tiles (8 waves) once there
+// are enough of them to fill the 256 CUs, smaller tiles by workgroup count in
+// between, and 256 x 256 again where 128 x 128 tiles would need a second,
+// partly filled round.
 template <int EPI>
 hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
     if constexpr (EPI == EPI_CHANNEL || EPI == EPI_CHANNEL_F16) {
@@ -113,7 +115,14 @@ hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
         const int64_t nt = (p.N + 127) / 128;
         if ((p.M + 31) / 32 * nt <= 420) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
         if ((p.M + 63) / 64 * nt <= 420) return launch_gemm_i8<64, 128, 2, 2, EPI, 8>(p, s);
-        return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
+        // 128 x 128 tiles run two to a CU: past 512 of them the second, partly
+        // filled round costs more than the one round of 256 x 256 tiles (K =
+        // 5120, rotating weight copies: N = 17408 at 448-768 tokens 93-99
+        // against 71-79 us, N = 15360 and 13824 at 576-1024 tokens 80-106
+        // against 67-81 us; at 512 tiles or fewer 128 x 128 stays 20-35%
+        // faster)
+        if ((p.M + 127) / 128 * nt <= 512) return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
+        return launch_gemm_i8<256, 256, 2, 4, EPI, 8>(p, s);
     }
     // Whole waves of 256 tiles (a partly filled last wave costs a whole
     // one); a wave of 256 x 384 tiles takes about 1.4 times as long as one
@@ -123,10 +132,9 @@ hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
     return launch_gemm_i8<256, 256, 2, 4, EPI, 8>(p, s);
 }
 
-// Group-scaled epilogues: 256 x 128 tiles of 8 waves (64 x 64 each, two
-// waves per SIMD: the per-block fold keeps a second set of fp32
-// accumulators) once smaller tiles would give more than one workgroup per
-// CU.
+// Group-scaled epilogues: 32 x 128 or 64 x 128 tiles while they give at most
+// one workgroup per CU, else 128 x 128 tiles of 4 waves (64 x 64 each, with
+// the fold's second set of fp32 accumulators), two to a CU.
 template <int EPI>
 hipError_t run_gemm_grouped(const GemmArgs& p, hipStream_t s) {
     // up to 64 tokens: stream the weights once (stream_group.hpp)
@@ -137,15 +145,17 @@ hipError_t run_gemm_grouped(const GemmArgs& p, hipStream_t s) {
         return launch_stream_group<ACT, EPI == EPI_GROUP_ACT_F16>(q, s);
     }
     if (p.M <= 64) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
-    // The first of 32, 64 and 128 tokens per tile that gives at most 256
-    // workgroups (one per CU), else 256 (measured over 65-1024 tokens at
-    // N = 5120 and 15360: within 3% of the fastest of the four, and 20-37%
-    // faster than the 128 x 128 tiles used throughout before).
+    // 32 or 64 tokens per tile while that gives at most 256 workgroups (one
+    // per CU), else 128.  Two 128 x 128 workgroups share a CU, and the last,
+    // partly filled round of such tiles costs less than one of 256 x 128
+    // tiles (one per CU): K = 5120, rotating weight copies, 128 x 128 against
+    // 256 x 128 tiles at N = 5120, 15360 and 17408 over 128-4096 tokens were
+    // 0-47% faster (4096 x 5120: 167 against 191 us; 384 x 17408: 63 against
+    // 118 us) and never more than 2% slower.
     const int64_t nt = (p.N + 127) / 128;
     if ((p.M + 31) / 32 * nt <= 256) return launch_gemm_i8<32, 128, 1, 4, EPI, 8>(p, s);
     if ((p.M + 63) / 64 * nt <= 256) return launch_gemm_i8<64, 128, 2, 2, EPI, 8>(p, s);
-    if ((p.M + 127) / 128 * nt <= 256) return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
-    return launch_gemm_i8<256, 128, 4, 2, EPI, 8>(p, s);
+    return launch_gemm_i8<128, 128, 2, 2, EPI, 8>(p, s);
 }
 
 template <int EPI>  // EPI_GROUP_ACT or EPI_GROUP_ACT_F16
