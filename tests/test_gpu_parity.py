@@ -1049,12 +1049,15 @@ def test_w8a16_few_tokens_weight_stream(M, N, K, pad):
         assert (host(yfull)[:, N:].view(torch.int16) == -1).all()
 
 
-@pytest.mark.parametrize("M,N,K,pad", [(4100, 4000, 256, 0), (8192, 5120, 1024, 0), (4100, 4000, 384, 64)])
+@pytest.mark.parametrize("M,N,K,pad", [(4100, 4000, 256, 0), (8192, 5120, 1024, 0), (4100, 4000, 384, 64),
+                                       # one round of 256 x 128 tiles (200), and 128 x 128 below 160
+                                       (1100, 5120, 512, 0), (600, 5104, 384, 32)])
 def test_w8a16_big_tiles_sampled_rows(M, N, K, pad):
     """Large problems run on 256 x 320 tiles when that needs fewer whole
-    waves (4100 x 4000: 544 tiles of 256 x 128 against 221 of 256 x 320),
-    here with ragged tiles on both edges and, with pad, strided x, w and y;
-    sampled rows, every column."""
+    waves (4100 x 4000: 544 tiles of 256 x 128 against 221 of 256 x 320);
+    below one wave, on 256 x 128 tiles while they cover at least 160 CUs,
+    else on 128 x 128 tiles.  Ragged tiles on both edges and, with pad,
+    strided x, w and y; sampled rows, every column."""
     say("w8a16 big tiles", M, N, K, pad)
     wl = synth.WORKLOADS["w8a16"]
     xf = synth.activations(wl, 2, M=M, K=K + pad)
@@ -1065,7 +1068,7 @@ def test_w8a16_big_tiles_sampled_rows(M, N, K, pad):
     wq_full[:, :K] = dev(torch.from_numpy(wq_ref))
     yfull = torch.full((M, N + pad), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
     y = q8.w8a16_mm(dev(xf)[:, :K], wq_full[:, :K], dev(torch.from_numpy(sc_ref)), out=yfull[:, :N])
-    rows = BIG_ROWS[BIG_ROWS < M]
+    rows = np.unique(np.concatenate([BIG_ROWS[BIG_ROWS < M], [M - 2, M - 1]]))
     _check_w8a16(bits(host(y).contiguous())[rows], np.ascontiguousarray(bits(x)[rows]), wq_ref, sc_ref,
                  f"w8a16 big tiles {M}x{N}x{K}")
     if pad:

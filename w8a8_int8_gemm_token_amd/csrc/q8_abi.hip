@@ -534,13 +534,19 @@ q8_status w8a16_impl(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ld
         const int64_t nt = (N + 127) / 128;
         if ((M + 31) / 32 * nt <= 256) return hip_status(launch_gemm_i8<32, 128, 1, 4, E, 8>(p, st(stream)));
         if ((M + 63) / 64 * nt <= 256) return hip_status(launch_gemm_i8<64, 128, 2, 2, E, 8>(p, st(stream)));
+        // one round of 256 x 128 tiles over at least 160 CUs beats two
+        //128 x 128 tiles per CU (5120 channels, K = 13824: 190 against
+        // 214 us at 1024 tokens; 15360 x 5120 at 512 tokens: 93 against
+        // 106 us); with fewer tiles it leaves too many CUs idle (K = 17408,
+        // 512 tokens, 80 tiles: 249 against 200 us)
+        if (t128 >= 160) return hip_status(launch_gemm_i8<256, 128, 4, 2, E, 8>(p, st(stream)));
         return hip_status(launch_gemm_i8<128, 128, 2, 2, E, 8>(p, st(stream)));
     }
-    // Whole waves of 256 tiles; a wave of 256 x 320 tiles takes about 2.2
-    // times as long as one of 256 x 128 (measured at 8192 x 5120 x 13824:
-    // 447 us against 211).
+    // Whole waves of 256 tiles; a wave of 256 x 320 tiles takes about 1.9
+    // times as long as one of 256 x 128 (1.8-2.0 measured at 5120 channels
+    // with K = 13824 and 17408 and at 15360 x 5120, 1024-8192 tokens).
     const int64_t w128 = (t128 + 255) / 256, w320 = (t320 + 255) / 256;
-    if (220 * w320 < 100 * w128 && gemm_w16_offsets_fit(p)) return hip_status(launch_gemm_w16<F16>(p, st(stream)));
+    if (190 * w320 < 100 * w128 && gemm_w16_offsets_fit(p)) return hip_status(launch_gemm_w16<F16>(p, st(stream)));
     return hip_status(launch_gemm_i8<256, 128, 4, 2, E, 8>(p, st(stream)));
 }
 
