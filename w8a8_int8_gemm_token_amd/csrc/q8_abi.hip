@@ -535,7 +535,7 @@ q8_status w8a16_impl(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ld
         if ((M + 31) / 32 * nt <= 256) return hip_status(launch_gemm_i8<32, 128, 1, 4, E, 8>(p, st(stream)));
         if ((M + 63) / 64 * nt <= 256) return hip_status(launch_gemm_i8<64, 128, 2, 2, E, 8>(p, st(stream)));
         // one round of 256 x 128 tiles over at least 160 CUs beats two
-        //128 x 128 tiles per CU (5120 channels, K = 13824: 190 against
+        // 128 x 128 tiles per CU (5120 channels, K = 13824: 190 against
         // 214 us at 1024 tokens; 15360 x 5120 at 512 tokens: 93 against
         // 106 us); with fewer tiles it leaves too many CUs idle (K = 17408,
         // 512 tokens, 80 tiles: 249 against 200 us)
