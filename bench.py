@@ -23,7 +23,10 @@ clock it holds under this load.  Prints one JSON line:
   roofline = the GEMM kernel: its mean duration over the K timed steps from
              the events around it (on the stream it is launched on), against
              the INT8 dense MFMA peak (5.0 POP/s), with the ceiling an MFMA-only
-             loop on changing operands reaches on the same board
+             loop on changing operands reaches on the same board, and the
+             same kernel at the same shape on all-zero and on small and
+             full-range uniform codes (the clock the board holds depends on
+             the operand values)
   cpu_baseline = the CPU oracle on a bounded sample of the same workload,
              and on each of the other four workloads (per_config)
   secondary    = decode (M=1, M=8) per call in a HIP graph with the weight
@@ -146,6 +149,25 @@ def call_stats(fn, iters: int, settle_ms: float = 60.0) -> dict:
     t = np.array([a.elapsed_time(b) for a, b in ev])
     return {"mean": float(t.mean()), "p10": float(np.percentile(t, 10)),
             "p50": float(np.percentile(t, 50)), "p90": float(np.percentile(t, 90))}
+
+
+def gemm_operand_values(dev, M: int, N: int, K: int, sc, st, y, iters: int) -> dict:
+    """The prefill GEMM kernel on the same shape with other operand values:
+    all-zero codes, and codes drawn uniformly from [-4, 4] and from
+    [-127, 127] (seeded).  The instructions, addresses and traffic are the
+    same in every case; what changes is the switching in the matrix cores,
+    so the board holds another clock.  Per-call times like gemm_alone."""
+    g = torch.Generator(device=dev)
+    out = {}
+    for name, lim in (("zero", 0), ("uniform_pm4", 4), ("uniform_pm127", 127)):
+        g.manual_seed(7)
+        xq = torch.randint(-lim, lim + 1, (M, K), dtype=torch.int8, device=dev, generator=g)
+        wq = torch.randint(-lim, lim + 1, (N, K), dtype=torch.int8, device=dev, generator=g)
+        st_ = call_stats(lambda: q8.q8_scaled_mm(xq, wq, st, sc, out=y), iters)
+        out[name] = dict(_us(st_), TOPS=2.0 * M * N * K / (st_["p50"] * 1e-3) / 1e12)
+        del xq, wq
+    torch.cuda.empty_cache()
+    return out
 
 
 def _us(st: dict) -> dict:
@@ -889,6 +911,8 @@ def main():
     log("ceilings")
     ceil = ceilings(dev)
     mfma_ceil = ceil["mfma_int8_random"]["TOPS"]
+    log("gemm on other operand values")
+    operand_values = gemm_operand_values(dev, M, N, K, sc, st, y, args.steps)
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_INT8_TOPS,
                 "traffic": None if traffic is None else sum(traffic),
@@ -899,7 +923,8 @@ def main():
                 "timing": "events around the GEMM inside each of the timed steps",
                 "measured_ceiling": mfma_ceil, "frac_measured_ceiling": achieved / mfma_ceil,
                 "measured_ceiling_kind": "int8 MFMA-only loop, operands changing every MFMA",
-                "frac_256cu_2p4ghz_5033": achieved / 5033.2}
+                "frac_256cu_2p4ghz_5033": achieved / 5033.2,
+                "same_kernel_other_operand_values_us": operand_values}
     quant_step_ms = float(quant_in.mean())
     secondary = {"quant_kernel": {"in_step_us": quant_step_ms * 1e3,
                                   "in_step_GB/s": quant_bytes / (quant_step_ms * 1e-3) / 1e9,
