@@ -29,6 +29,13 @@
 // its loads of the next stage and one barrier publishes that stage and
 // frees this one, and the second half of sub-step 3 runs behind the next
 // stage's first fragment reads.
+//
+// Epilogue (16-bit outputs): written straight from the MFMA layout, each
+// store instruction would put 16-byte pieces into 32 rows, and the 252 MB
+// output of the prefill shape then cost about 80 us of the launch (the same
+// kernel with the stores branched off: 472 against 551 us).  The values go
+// through LDS instead and leave in whole 128-byte lines with non-temporal
+// 16-byte stores: 558 -> 531 us, bit-identical.
 #pragma once
 
 #include "gemm_i8.hpp"
@@ -183,6 +190,73 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs p) {
     // the hand-over waited for them
 
     // ---------------------------------------------------------- epilogue --
+    if constexpr (EPI == EPI_CHANNEL) {
+        // 16-bit outputs leave through LDS, so that every store instruction
+        // writes whole 128-byte lines: a lane of the MFMA layout holds four
+        // channels of one token, and stored directly each instruction would
+        // write 16-byte pieces of 32 rows.  Two passes, each of two 32-token
+        // blocks of both wave rows (64 tokens x 384 channels, 48 KB, in the
+        // two weight stage buffers).  The values and their rounding are the
+        // direct form's; only the route to memory differs.
+        wait_vm_lgkm0<0>();
+        block_barrier();  // every wave is done with the stage buffers
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int a = 2 * pass + h;
+                int8_t* buf = h ? lw1 : lw0;
+                const int r = wm * 32 + (lane & 31);  // row of the 64-token block
+                const int j = min(m0 + wm * WTM + a * 32 + (lane & 31), M - 1);
+                const float st = p.s_tok[j];
+#pragma unroll
+                for (int b = 0; b < TN; ++b) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int c8 = wn * (WTN / 4) + b * 8 + g * 2 + hi;  // 8-byte unit in the row
+                        const int ch = min(n0 + 4 * c8, N - 4);
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float t = (float)acc[a][b][g * 4 + e] * st;
+                            v[e] = t * p.s_w[ch + e];
+                        }
+                        v2u o;
+                        o[0] = pack16x2<OUT_F16>(v[0], v[1]);
+                        o[1] = pack16x2<OUT_F16>(v[2], v[3]);
+                        // unit c8 of row r at c8 ^ (r & 31): the 32 rows a
+                        // write instruction touches fall in distinct banks
+                        *reinterpret_cast<v2u*>(buf + r * (BN * 2) + ((c8 ^ (r & 31)) << 3)) = o;
+                    }
+                }
+            }
+            wait_vm_lgkm0<63>();  // LDS writes done (stores still in flight)
+            block_barrier();
+            // 2 x 64 rows x 48 chunks of 16 bytes; lane-consecutive chunks
+            // of a row, so eight lanes write one whole line
+            constexpr int CPR = BN * 2 / 16;  // 16-byte chunks per row
+#pragma unroll
+            for (int i = 0; i < 2 * 64 * CPR / (NW * 64); ++i) {
+                const int idx = i * NW * 64 + tid;
+                const int h = idx / (64 * CPR);
+                const int rr = (idx / CPR) % 64, q = idx % CPR;
+                const int s = rr & 31;
+                const int base = (2 * q) ^ (s & ~1);
+                v4u d = *reinterpret_cast<const v4u*>((h ? lw1 : lw0) + rr * (BN * 2) + (base << 3));
+                if (s & 1) d = v4u{d[2], d[3], d[0], d[1]};
+                const int j = m0 + (rr >> 5) * WTM + (2 * pass + h) * 32 + (rr & 31);
+                const int ch = n0 + q * 8;
+                if (j < M && ch < N)
+                    __builtin_nontemporal_store(d, reinterpret_cast<v4u*>(static_cast<uint16_t*>(p.c) +
+                                                                           (int64_t)j * p.ldc + ch));
+            }
+            if (pass == 0) {
+                wait_vm_lgkm0<63>();
+                block_barrier();  // the reads are done before the next pass writes
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
         const int j = m0 + wm * WTM + a * 32 + (lane & 31);  // token
