@@ -508,6 +508,73 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
     if (kt < KT) stage(kt, lx0, lw0, ls0, lx1, lw1, ls1);
 
     // ---------------------------------------------------------- epilogue --
+    if constexpr (!RAW) {
+        // 16-bit outputs leave through LDS in whole 128-byte lines (stored
+        // straight from the MFMA layout each instruction would write 16-byte
+        // pieces of 32 rows): one 32-token block of every wave row per pass,
+        // WM*32 rows x BN channels, alternating between two stage buffers
+        // that hold it.  Same values and rounding as a direct store.
+        constexpr bool USE_W = WM * 32 * BN * 2 <= BN * BK;
+        static_assert(USE_W || WM * 32 * BN * 2 <= BM * BK, "a pass fits a stage buffer");
+        static_assert(BN % 128 == 0, "rows of whole 32-unit swizzle groups");
+        constexpr int RB = BN * 2;    // bytes per staged row
+        constexpr int CPR = RB / 16;  // 16-byte chunks per row
+        wait_vm_lgkm0<0>();
+        block_barrier();  // every wave is done with the stage buffers
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            int8_t* buf = USE_W ? ((a & 1) ? lw1 : lw0) : ((a & 1) ? lx1 : lx0);
+            const int r = wm * 32 + (lane & 31);  // staged row
+            const int j = min(m0 + wm * WTM + a * 32 + (lane & 31), M - 1);
+            const float st = (EPI == EPI_CHANNEL || EPI == EPI_GROUP) ? p.s_tok[j] : 0.0f;
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int c8 = wn * (WTN / 4) + b * 8 + g * 2 + hi;  // 8-byte unit in the row
+                    const int ch = min(n0 + 4 * c8, N - 4);
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (EPI == EPI_CHANNEL) {
+                            float t = (float)acc[a][b][g * 4 + e] * st;
+                            v[e] = t * p.s_w[ch + e];
+                        } else if constexpr (EPI == EPI_GROUP) {
+                            v[e] = facc[a][b][g * 4 + e] * st;
+                        } else if constexpr (W16) {
+                            v[e] = p.s_w[ch + e] * acc[a][b][g * 4 + e];
+                        } else {
+                            v[e] = facc[a][b][g * 4 + e];
+                        }
+                    }
+                    v2u o;
+                    o[0] = pack16x2<OUT_F16>(v[0], v[1]);
+                    o[1] = pack16x2<OUT_F16>(v[2], v[3]);
+                    // unit c8 of row r at c8 ^ (r & 31): conflict-free writes
+                    *reinterpret_cast<v2u*>(buf + r * RB + ((c8 ^ (r & 31)) << 3)) = o;
+                }
+            }
+            // LDS writes done; the previous pass's reads of the other buffer
+            // were waited for before this barrier as well
+            wait_vm_lgkm0<63>();
+            block_barrier();
+#pragma unroll
+            for (int i = 0; i < WM * 32 * CPR / (NW * 64); ++i) {
+                const int idx = i * NW * 64 + tid;
+                const int rr = idx / CPR, q = idx % CPR;
+                const int sw = rr & 31;
+                const int base = (2 * q) ^ (sw & ~1);
+                v4u d = *reinterpret_cast<const v4u*>(buf + rr * RB + (base << 3));
+                if (sw & 1) d = v4u{d[2], d[3], d[0], d[1]};
+                const int jj = m0 + (rr >> 5) * WTM + a * 32 + (rr & 31);
+                const int cc = n0 + q * 8;
+                if (jj < M && cc < N)
+                    __builtin_nontemporal_store(d, reinterpret_cast<v4u*>(static_cast<uint16_t*>(p.c) +
+                                                                           (int64_t)jj * p.ldc + cc));
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
         const int j = m0 + wm * WTM + a * 32 + (lane & 31);  // token
