@@ -200,24 +200,59 @@ __global__ __launch_bounds__(512) void gemm_w16_kernel(GemmArgs p) {
     if (kt < KT) stage(kt, lx0, lw0, lx1, lw1);
 
     // ---------------------------------------------------------- epilogue --
+    // The outputs leave through LDS in whole 128-byte lines (stored straight
+    // from the MFMA layout each instruction would write 16-byte pieces of 32
+    // rows).  One pass per 32-token block a: the rows of wave rows 0-1 in one
+    // weight stage buffer and those of wave rows 2-3 in the other (64 rows x
+    // 320 channels, 40 KB each).  Same values and rounding as a direct
+    // store.
+    constexpr int RB = BN * 2;    // 640 bytes per staged row
+    constexpr int CPR = RB / 16;  // 40 chunks of 16 bytes
+    static_assert(64 * RB <= BN * BK && (RB / 8) % 16 == 0 && WM == 4, "staging layout");
+    wait_vm_lgkm0<0>();
+    block_barrier();  // every wave is done with the stage buffers
+    int8_t* const wbuf = (wm >> 1) ? lw1 : lw0;
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
-        const int j = m0 + wm * WTM + a * 32 + (lane & 31);  // token
-        if (j >= M) continue;
+        const int r = (wm & 1) * 32 + (lane & 31);  // staged row
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int ch = n0 + wn * WTN + b * 32 + g * 8 + hi * 4;
-                if (ch >= N) continue;
+                const int c8 = wn * (WTN / 4) + b * 8 + g * 2 + hi;  // 8-byte unit in the row
+                const int ch = min(n0 + 4 * c8, N - 4);
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = p.s_w[ch + e] * acc[a][b][g * 4 + e];
                 v2u o;
                 o[0] = pack16x2<F16>(v[0], v[1]);
                 o[1] = pack16x2<F16>(v[2], v[3]);
-                *reinterpret_cast<v2u*>(static_cast<uint16_t*>(p.c) + (int64_t)j * p.ldc + ch) = o;
+                // unit c8 of row r at c8 ^ ((r >> 1) & 15) (rows of 160
+                // dwords alternate between the two bank halves): the 32 rows
+                // a write instruction touches fall in distinct banks
+                *reinterpret_cast<v2u*>(wbuf + r * RB + ((c8 ^ ((r >> 1) & 15)) << 3)) = o;
             }
+        }
+        wait_vm_lgkm0<63>();  // LDS writes done (stores still in flight)
+        block_barrier();
+#pragma unroll
+        for (int i = 0; i < 2 * 64 * CPR / (NW * 64); ++i) {
+            const int idx = i * NW * 64 + tid;
+            const int h = idx / (64 * CPR);
+            const int rr = (idx / CPR) % 64, q = idx % CPR;
+            const int sw = (rr >> 1) & 15;
+            const int base = (2 * q) ^ (sw & ~1);
+            v4u d = *reinterpret_cast<const v4u*>((h ? lw1 : lw0) + rr * RB + (base << 3));
+            if (sw & 1) d = v4u{d[2], d[3], d[0], d[1]};
+            const int jj = m0 + (2 * h + (rr >> 5)) * WTM + a * 32 + (rr & 31);
+            const int cc = n0 + q * 8;
+            if (jj < M && cc < N)
+                __builtin_nontemporal_store(d, reinterpret_cast<v4u*>(static_cast<uint16_t*>(p.c) +
+                                                                       (int64_t)jj * p.ldc + cc));
+        }
+        if (a + 1 < TM) {
+            wait_vm_lgkm0<63>();
+            block_barrier();  // the reads are done before the next pass writes
         }
     }
 }
