@@ -73,11 +73,11 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 # (null).
 GEMM_COUNTERS = {
     "sources_sha256": {
-        "gemm_big.hpp": "8fdf1c7bc31a1e14bde9abe6fe27a066c4ac91c62b301cdfb7a258b52749a483",
-        "gemm_i8.hpp": "febc8517b77d8095609f9562f5666c5cbbab9ae7ee7319a48cf8b27227353afa",
+        "gemm_big.hpp": "6e269a623d683ecb481dff57c0c49141c2e95c1db0e335c09c51e73819d8031d",
+        "gemm_i8.hpp": "9372a1092814a93701bef21ef1a57443f91720a46b43084da5e8311df2d929e4",
         "q8_device.hpp": "ccd2b93eca43b76b27e87299ed951a8a59342afdb931f850f87bdacbbe91dfc2",
     },
-    "fetch_kib": 367718.4, "write_kib": 262611.4,
+    "fetch_kib": 363688.1, "write_kib": 245861.1,
     "copy_kib": 524288.0, "copy_fetch_kib": 262155.5, "copy_write_kib": 524288.0,
 }
 
