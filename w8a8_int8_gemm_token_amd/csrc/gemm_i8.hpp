@@ -574,6 +574,57 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_kernel(GemmArgs p) {
             }
         }
         return;
+    } else if constexpr (WM <= 2) {
+        // Raw int32 (or fp32) sums, as a split-K plane or q8_mm_i32's
+        // output, through LDS as well: one 32-row block per wave row and pass,
+        // wave row i in stage buffer i (32 rows x BN x 4 bytes, BN x 128
+        // bytes of LDS), 16-byte unit u of row r at u ^ (r & 31), then whole
+        // lines out.
+        constexpr int RB = BN * 4;    // bytes per staged row
+        constexpr int CPR = RB / 16;  // 16-byte chunks per row
+        static_assert(32 * RB <= BN * BK && CPR % 32 == 0, "staging layout");
+        wait_vm_lgkm0<0>();
+        block_barrier();  // every wave is done with the stage buffers
+        int8_t* const wbuf = (wm & 1) ? lw1 : lw0;
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            const int r = lane & 31;
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int u = wn * (WTN / 4) + b * 8 + g * 2 + hi;  // 16-byte unit in the row
+                    v4i o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (EPI == EPI_I32) o[e] = acc[a][b][g * 4 + e];
+                        else o[e] = __float_as_int(acc[a][b][g * 4 + e]);
+                    }
+                    *reinterpret_cast<v4i*>(wbuf + r * RB + ((u ^ r) << 4)) = o;
+                }
+            }
+            wait_vm_lgkm0<63>();  // LDS writes done (stores still in flight)
+            block_barrier();
+#pragma unroll
+            for (int i = 0; i < WM * 32 * CPR / (NW * 64); ++i) {
+                const int idx = i * NW * 64 + tid;
+                const int h = idx / (32 * CPR);
+                const int rr = (idx / CPR) % 32, q = idx % CPR;
+                const v4i d = *reinterpret_cast<const v4i*>((h ? lw1 : lw0) + rr * RB + ((q ^ rr) << 4));
+                const int jj = m0 + h * WTM + a * 32 + rr;
+                const int cc = n0 + q * 4;
+                if (jj < M && cc < N) {
+                    v4i* dst = reinterpret_cast<v4i*>(static_cast<int32_t*>(p.c) + (int64_t)blockIdx.y * p.plane +
+                                                      (int64_t)jj * p.ldc + cc);
+                    *dst = d;  // plain store: the reduce reads the planes next
+                }
+            }
+            if (a + 1 < TM) {
+                wait_vm_lgkm0<63>();
+                block_barrier();  // the reads are done before the next pass writes
+            }
+        }
+        return;
     }
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
