@@ -289,6 +289,221 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs p) {
     }
 }
 
+// gemm_big16_kernel: the per-channel (16-bit output) launches of this tile.
+// Why a second form: under changing operands the board lowers its clock
+// with the matrix cores' power, and the 16 x 16 x 64 instruction writes half
+// the accumulators per product of the 32 x 32 x 32 one.  An MFMA-only loop
+// on random int8 operands sustains 3,568 TOP/s with it against 3,135 (zero
+// operands: 4,657 against 4,716); this kernel takes 473 us at 8192 x 15360
+// x 5120 against 525 us for gemm_big_kernel on the same board, bit-identical.
+// gemm_big_kernel keeps the raw int32 mode.
+//
+// The same tile, loads, LDS layout and epilogue on v_mfma_i32_16x16x64_i8:
+// a wave's 128 tokens x 96 channels are 8 x 6 blocks of 16 x 16 (four int32
+// sums per lane, four consecutive channels of one token), each 128-deep stage
+// two 64-deep sub-steps.  A lane's fragment is 16 bytes of K (chunk 4 kk +
+// lane / 16 of row lane % 16 of the 16-row block) for both operands, so the
+// products pair equal k.  The six channel fragments stay for a whole
+// sub-step; the token fragments are read one block ahead into two register
+// slots.  Integer sums are order-free: bit-identical to gemm_big_kernel.
+template <int EPI_>
+__global__ __launch_bounds__(512) void gemm_big16_kernel(GemmArgs p) {
+    constexpr int EPI = epi_base(EPI_);
+    constexpr bool OUT_F16 = EPI_ != EPI;
+    static_assert(EPI == EPI_CHANNEL, "per-channel epilogue");
+    constexpr int BM = BIG_BM, BN = BIG_BN, WM = 2, WN = 4, NW = WM * WN, GM = 8, BK = 128;
+    constexpr int WTM = BM / WM, WTN = BN / WN;  // 128 tokens x 96 channels per wave
+    constexpr int TT = WTM / 16, TC = WTN / 16;  // 8 token blocks, 6 channel blocks
+    constexpr int XIW = BM / 8 / NW, WIW = BN / 8 / NW;
+
+    __shared__ __attribute__((aligned(1024))) int8_t lx0[BM * BK];
+    __shared__ __attribute__((aligned(1024))) int8_t lx1[BM * BK];
+    __shared__ __attribute__((aligned(1024))) int8_t lw0[BN * BK];
+    __shared__ __attribute__((aligned(1024))) int8_t lw1[BN * BK];
+
+    const int M = p.M, N = p.N, K = p.K;
+    const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+    const int id = xcd_remap(blockIdx.x, nbm * nbn);
+    const int per_group = GM * nbn;
+    const int first_m = (id / per_group) * GM;
+    const int gsz = min(nbm - first_m, GM);
+    const int tile_m = first_m + (id % per_group) % gsz;
+    const int tile_n = (id % per_group) / gsz;
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid % WM, wn = wid / WM;
+    const int q4 = lane >> 4;
+
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, operand_extent(M, p.ldx, K));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, operand_extent(N, p.ldw, K));
+    const int lrow = lane >> 3, lslot = lane & 7;
+    const int xv[2] = {lrow * (int)p.ldx + ((lslot ^ lrow) << 4), lrow * (int)p.ldx + ((lslot ^ lrow ^ 1) << 4)};
+    const int wv[2] = {lrow * (int)p.ldw + ((lslot ^ lrow) << 4), lrow * (int)p.ldw + ((lslot ^ lrow ^ 1) << 4)};
+    const int xs0 = (m0 + wid * XIW * 8) * (int)p.ldx;
+    const int ws0 = (n0 + wid * WIW * 8) * (int)p.ldw;
+
+    // direct loads of stage kt, instructions [i0, i1) of the wave's 10
+    auto issue = [&](int kt, int8_t* bx, int8_t* bw, int i0, int i1) __attribute__((always_inline)) {
+        const int koff = kt * BK;
+#pragma unroll
+        for (int i = 0; i < XIW + WIW; ++i) {
+            if (i < i0 || i >= i1) continue;
+            if (i < XIW)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xr, (Q8_LDS void*)(bx + (wid * XIW + i) * 1024), 16,
+                    lane_offset(xv[(wid * XIW + i) & 1], xs0 + i * 8 * (int)p.ldx + koff), 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wr, (Q8_LDS void*)(bw + (wid * WIW + i - XIW) * 1024), 16,
+                    lane_offset(wv[(wid * WIW + i - XIW) & 1], ws0 + (i - XIW) * 8 * (int)p.ldw + koff), 0, 0, 0);
+        }
+    };
+
+    // fragment offsets: sub-step kk reads chunk 4 kk + lane / 16 of the
+    // lane's row (lane % 16 of a 16-row block; 16 rows further per block,
+    // same swizzle)
+    int wbase[2], xbase[2];
+    {
+        const int rw0 = wn * WTN + (lane & 15), rx0 = wm * WTM + (lane & 15);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int ch = 4 * kk + q4;
+            wbase[kk] = rw0 * BK + ((ch ^ lds_swizzle(rw0)) << 4);
+            xbase[kk] = rx0 * BK + ((ch ^ lds_swizzle(rx0)) << 4);
+        }
+    }
+
+    v4i acc[TT][TC];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int c = 0; c < TC; ++c) acc[t][c] = v4i{};
+    v4i fw[TC], fx[2];
+
+    auto rdx = [&](int kk, const int8_t* bx, int t) __attribute__((always_inline)) {
+        return *reinterpret_cast<const v4i*>(bx + xbase[kk] + t * 16 * BK);
+    };
+    auto rdw = [&](int kk, const int8_t* bw, int c) __attribute__((always_inline)) {
+        return *reinterpret_cast<const v4i*>(bw + wbase[kk] + c * 16 * BK);
+    };
+    auto block = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < TC; ++c)
+            acc[t][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fw[c], fx[t & 1], acc[t][c], 0, 0, 0);
+    };
+
+    // one 64-deep sub-step on fw / fx[0] (already read); the next sub-step's
+    // fragments come from (nkk, nbx, nbw); LAST: they belong to the next
+    // stage, so the hand-over (loads landed, one barrier) comes first.
+    // FIRST: this stage's sub-step 0, which also issues the next stage's
+    // loads, two per token block.
+    auto substep = [&](int kk, const int8_t* bx, int nkk, const int8_t* nbx, const int8_t* nbw, bool first,
+                       bool last, int kt, int8_t* lx_n, int8_t* lw_n) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            if (first && t < 5) issue(kt + 1, lx_n, lw_n, 2 * t, 2 * t + 2);
+            if (t + 1 < TT) fx[(t + 1) & 1] = rdx(kk, bx, t + 1);
+            if (t < TT - 1) {
+                block(t);
+                if (t == TT - 2) {
+                    if (last) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        wait_vm_lgkm0<0>();
+                        block_barrier();
+                    }
+                    fx[0] = rdx(nkk, nbx, 0);  // fx[0] last used by block 6
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < TC; ++c) {
+                    acc[t][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fw[c], fx[t & 1], acc[t][c], 0, 0, 0);
+                    fw[c] = rdw(nkk, nbw, c);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int KT = K / BK;
+    issue(0, lx0, lw0, 0, XIW + WIW);
+    wait_vm_lgkm0<0>();
+    block_barrier();
+#pragma unroll
+    for (int c = 0; c < TC; ++c) fw[c] = rdw(0, lw0, c);
+    fx[0] = rdx(0, lx0, 0);
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+        substep(0, lx0, 1, lx0, lw0, true, false, kt, lx1, lw1);
+        substep(1, lx0, 0, lx1, lw1, false, true, kt, lx1, lw1);
+        substep(0, lx1, 1, lx1, lw1, true, false, kt + 1, lx0, lw0);
+        substep(1, lx1, 0, lx0, lw0, false, true, kt + 1, lx0, lw0);
+    }
+    if (kt < KT) {
+        substep(0, lx0, 1, lx0, lw0, true, false, kt, lx1, lw1);
+        substep(1, lx0, 0, lx1, lw1, false, true, kt, lx1, lw1);
+    }
+
+    // ---------------------------------------------------------- epilogue --
+    // as gemm_big_kernel's: two passes of two 32-token groups of both wave
+    // rows (64 rows x 384 channels in a weight stage buffer), whole lines
+    // out.  8-byte unit u of row r at u ^ ((r & 15) << 1): a write
+    // instruction's 16 rows x 2 adjacent units, and a read's 16 chunks of
+    // one row, fall in distinct banks, and a 16-byte chunk stays in order.
+    wait_vm_lgkm0<0>();
+    block_barrier();
+    constexpr int RB = BN * 2, CPR = RB / 16;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int a32 = 2 * pass + h;
+            int8_t* buf = h ? lw1 : lw0;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int t = 2 * a32 + tt;
+                const int r = wm * 32 + tt * 16 + (lane & 15);
+                const int j = min(m0 + wm * WTM + t * 16 + (lane & 15), M - 1);
+                const float st = p.s_tok[j];
+#pragma unroll
+                for (int c = 0; c < TC; ++c) {
+                    const int c8 = wn * (WTN / 4) + c * 4 + q4;
+                    const int ch = min(n0 + 4 * c8, N - 4);
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float tv = (float)acc[t][c][e] * st;
+                        v[e] = tv * p.s_w[ch + e];
+                    }
+                    v2u o;
+                    o[0] = pack16x2<OUT_F16>(v[0], v[1]);
+                    o[1] = pack16x2<OUT_F16>(v[2], v[3]);
+                    *reinterpret_cast<v2u*>(buf + r * RB + ((c8 ^ ((r & 15) << 1)) << 3)) = o;
+                }
+            }
+        }
+        wait_vm_lgkm0<63>();
+        block_barrier();
+#pragma unroll
+        for (int i = 0; i < 2 * 64 * CPR / (NW * 64); ++i) {
+            const int idx = i * NW * 64 + tid;
+            const int h = idx / (64 * CPR);
+            const int rr = (idx / CPR) % 64, q = idx % CPR;
+            const v4u d = *reinterpret_cast<const v4u*>((h ? lw1 : lw0) + rr * RB + ((q ^ (rr & 15)) << 4));
+            const int j = m0 + (rr >> 5) * WTM + (2 * pass + h) * 32 + (rr & 31);
+            const int ch = n0 + q * 8;
+            if (j < M && ch < N)
+                __builtin_nontemporal_store(d, reinterpret_cast<v4u*>(static_cast<uint16_t*>(p.c) +
+                                                                       (int64_t)j * p.ldc + ch));
+        }
+        if (pass == 0) {
+            wait_vm_lgkm0<63>();
+            block_barrier();
+        }
+    }
+}
+
 // 32-bit buffer offsets: channel rows reach n0 + 383 < N + 383, token rows
 // m0 + 255, and the loads run one stage past K.
 inline bool gemm_big_offsets_fit(const GemmArgs& p) {
@@ -299,7 +514,10 @@ inline bool gemm_big_offsets_fit(const GemmArgs& p) {
 template <int EPI>
 inline hipError_t launch_gemm_big(const GemmArgs& p, hipStream_t stream) {
     const int nbm = (p.M + BIG_BM - 1) / BIG_BM, nbn = (p.N + BIG_BN - 1) / BIG_BN;
-    hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(nbm * nbn), dim3(512), 0, stream, p);
+    if constexpr (epi_base(EPI) == EPI_CHANNEL)  // 16-bit outputs: the 16 x 16 x 64 form
+        hipLaunchKernelGGL((gemm_big16_kernel<EPI>), dim3(nbm * nbn), dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(nbm * nbn), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
