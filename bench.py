@@ -23,7 +23,8 @@ clock it holds under this load.  Prints one JSON line:
   roofline = the GEMM kernel: its mean duration over the K timed steps from
              the events around it (on the stream it is launched on), against
              the INT8 dense MFMA peak (5.0 POP/s), with the ceiling an MFMA-only
-             loop on changing operands reaches on the same board, and the
+             loop of the GEMM's instruction on changing operands reaches on
+             the same board, and the
              same kernel at the same shape on all-zero and on small and
              full-range uniform codes (the clock the board holds depends on
              the operand values)
@@ -67,17 +68,17 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 
 # HBM bytes of the prefill GEMM from hardware counters (rocprofv3 --pmc
 # FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, mean over the dispatches of
-# gemm_big_kernel<EPI_CHANNEL> in a short bench run), scaled by what the same
+# gemm_big16_kernel<EPI_CHANNEL> in a short bench run), scaled by what the same
 # counters read for a plain 512 MiB device copy.  Valid only for the kernel
 # sources they were taken on: if those files change, the figure is withdrawn
 # (null).
 GEMM_COUNTERS = {
     "sources_sha256": {
-        "gemm_big.hpp": "6e269a623d683ecb481dff57c0c49141c2e95c1db0e335c09c51e73819d8031d",
-        "gemm_i8.hpp": "9372a1092814a93701bef21ef1a57443f91720a46b43084da5e8311df2d929e4",
+        "gemm_big.hpp": "ff5d80f8b17a0c77005282b4cc9502f4336cbef3a867286924b9743f69dc574d",
+        "gemm_i8.hpp": "cda32a4092af89f146b4cf1525ebbcdd0e8e91839f7c3688837cde37d5078a24",
         "q8_device.hpp": "ccd2b93eca43b76b27e87299ed951a8a59342afdb931f850f87bdacbbe91dfc2",
     },
-    "fetch_kib": 363688.1, "write_kib": 245861.1,
+    "fetch_kib": 363687.6, "write_kib": 245860.8,
     "copy_kib": 524288.0, "copy_fetch_kib": 262155.5, "copy_write_kib": 524288.0,
 }
 
@@ -189,6 +190,8 @@ def ceil_lib():
         P, I, C = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.q8c_mfma_i8_loop.argtypes = [C, C, C, P, P]
         lib.q8c_mfma_i8_loop.restype = C
+        lib.q8c_mfma_i8_loop16.argtypes = [C, C, C, P, P]
+        lib.q8c_mfma_i8_loop16.restype = C
         lib.q8c_stream_read.argtypes = [P, I, C, P, P]
         lib.q8c_stream_read.restype = C
         _ceil = lib
@@ -200,23 +203,26 @@ def _stream_ptr():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def mfma_ceiling(dev, random: bool, iters: int = 16384, reps: int = 10) -> dict:
-    """int8 MFMA rate of a loop of v_mfma_i32_32x32x32_i8 from registers
-    (no memory traffic): 768 workgroups of 4 waves (3 waves per SIMD, all
-    resident), each wave 4 * iters MFMAs; operands changing every MFMA
-    (random) or all zero."""
+def mfma_ceiling(dev, random: bool, iters: int = 16384, reps: int = 10, form: str = "32x32x32") -> dict:
+    """int8 MFMA rate of a loop of v_mfma_i32_32x32x32_i8 (four chains per
+    wave) or v_mfma_i32_16x16x64_i8 (eight chains) from registers (no
+    memory traffic): 768 workgroups of 4 waves (3 waves per SIMD, all
+    resident); operands changing every MFMA (random) or all zero."""
     import ctypes
     lib = ceil_lib()
     blocks = 768
     out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    fn = lib.q8c_mfma_i8_loop if form == "32x32x32" else lib.q8c_mfma_i8_loop16
 
     def f():
-        rc = lib.q8c_mfma_i8_loop(blocks, iters, int(random), ctypes.c_void_p(out.data_ptr()), _stream_ptr())
+        rc = fn(blocks, iters, int(random), ctypes.c_void_p(out.data_ptr()), _stream_ptr())
         if rc != 0:
-            raise RuntimeError(f"q8c_mfma_i8_loop failed ({rc})")
+            raise RuntimeError(f"MFMA loop failed ({rc})")
     ms = events_time(f, reps)
-    ops = blocks * 4 * 4 * iters * 65536.0
-    return {"TOPS": ops / (ms * 1e-3) / 1e12, "ms": ms, "operands": "random" if random else "zero"}
+    # per wave: 4 chains of 32x32x32 (65536 ops each) or 8 of 16x16x64 (32768)
+    ops = blocks * 4 * iters * (4 * 65536.0 if form == "32x32x32" else 8 * 32768.0)
+    return {"TOPS": ops / (ms * 1e-3) / 1e12, "ms": ms, "operands": "random" if random else "zero",
+            "form": form}
 
 
 def read_ceiling_graph(dev, nbytes: int, ncopy: int = 24, reps: int = 20) -> dict:
@@ -281,6 +287,8 @@ def ceilings(dev) -> dict:
     if not _CEILINGS:
         _CEILINGS["mfma_int8_random"] = mfma_ceiling(dev, True)
         _CEILINGS["mfma_int8_zero"] = mfma_ceiling(dev, False)
+        _CEILINGS["mfma_int8_16x16x64_random"] = mfma_ceiling(dev, True, form="16x16x64")
+        _CEILINGS["mfma_int8_16x16x64_zero"] = mfma_ceiling(dev, False, form="16x16x64")
         _CEILINGS["read_decode_bytes_graph"] = read_ceiling_graph(dev, 26_398_752)
         _CEILINGS["read_512MiB"] = read_ceiling_big(dev)
         torch.cuda.empty_cache()
@@ -910,19 +918,20 @@ def main():
     algo_bytes = M * K + N * K + 4 * M + 4 * N + 2 * M * N
     log("ceilings")
     ceil = ceilings(dev)
-    mfma_ceil = ceil["mfma_int8_random"]["TOPS"]
+    mfma_ceil = ceil["mfma_int8_16x16x64_random"]["TOPS"]
     log("gemm on other operand values")
     operand_values = gemm_operand_values(dev, M, N, K, sc, st, y, args.steps)
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_INT8_TOPS,
                 "traffic": None if traffic is None else sum(traffic),
                 "traffic_read_write": traffic, "algorithmic_bytes": algo_bytes,
-                "kernel": "gemm_big_kernel (per-channel epilogue, 256 x 384 tiles)",
+                "kernel": "gemm_big16_kernel (per-channel epilogue, 256 x 384 tiles, 16x16x64 int8 MFMA)",
                 "kernel_us": gemm_ms * 1e3,
                 "kernel_us_p10_p50_p90": [round(float(np.percentile(gemm_in, q)) * 1e3, 2) for q in (10, 50, 90)],
                 "timing": "events around the GEMM inside each of the timed steps",
                 "measured_ceiling": mfma_ceil, "frac_measured_ceiling": achieved / mfma_ceil,
-                "measured_ceiling_kind": "int8 MFMA-only loop, operands changing every MFMA",
+                "measured_ceiling_kind": "int8 MFMA-only loop of the GEMM's instruction (16x16x64), "
+                                         "operands changing every MFMA",
                 "frac_256cu_2p4ghz_5033": achieved / 5033.2,
                 "same_kernel_other_operand_values_us": operand_values}
     quant_step_ms = float(quant_in.mean())

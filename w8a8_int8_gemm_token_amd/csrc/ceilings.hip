@@ -67,6 +67,36 @@ __global__ __launch_bounds__(256) void mfma_i8_loop_kernel(int iters, int random
     out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// The same loop on v_mfma_i32_16x16x64_i8 (the prefill GEMM's form): eight
+// independent chains, each MFMA 16 x 16 x 64.
+template <int NF>
+__global__ __launch_bounds__(256) void mfma_i8_loop16_kernel(int iters, int random, int* out) {
+    v4i f[NF];
+    const uint32_t seed = (blockIdx.x * 256u + threadIdx.x) * 131u;
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[j][e] = random ? (int)mix32(seed + 4u * j + e) : 0;
+    v4i acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = v4i{};
+    for (int i = 0; i < iters; i += NF) {
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f[(j + c) % NF], f[(j + c + 1) % NF], acc[c], 0,
+                                                               0, 0);
+        }
+    }
+    int s = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s ^= acc[c][e];
+    out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 __global__ __launch_bounds__(256) void stream_read_kernel(const v4i* __restrict__ p, int64_t n16,
                                                           int* out) {
     const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -100,6 +130,14 @@ int q8c_mfma_i8_loop(int blocks, int iters, int random, int* out, void* stream) 
 
 // Streaming read of `bytes` bytes at p (16-byte aligned, bytes a multiple
 // of 16) by `blocks` workgroups of 256 threads.  out: int32 [blocks * 256].
+// iters 16x16x64 MFMAs on each of 8 chains per wave
+int q8c_mfma_i8_loop16(int blocks, int iters, int random, int* out, void* stream) {
+    if (blocks <= 0 || iters <= 0 || iters % 8 != 0 || !out) return 1;
+    hipLaunchKernelGGL((mfma_i8_loop16_kernel<8>), dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters,
+                       random, out);
+    return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
 int q8c_stream_read(const void* p, int64_t bytes, int blocks, int* out, void* stream) {
     if (!p || !out || bytes <= 0 || bytes % 16 != 0 || blocks <= 0 || ((uintptr_t)p & 15) != 0) return 1;
     hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
