@@ -125,10 +125,13 @@ hipError_t run_gemm_i8(const GemmArgs& p, hipStream_t s) {
         return launch_gemm_i8<256, 256, 2, 4, EPI, 8>(p, s);
     }
     // Whole waves of 256 tiles (a partly filled last wave costs a whole
-    // one); a wave of 256 x 384 tiles takes about 1.4 times as long as one
-    // of 256 x 256 (measured at the prefill shape: 111.5 us against 78-83).
+    // one); a wave of 256 x 384 tiles takes about 1.3 times as long as one
+    // of 256 x 256 (1.26-1.34 measured at 8192 tokens for 5120, 13824 and
+    // 15360 channels, the 256 x 384 tile on the 16 x 16 x 64 kernel; with
+    // the 32 x 32 x 32 one, which the raw int32 output keeps, it was 1.4)
     const int64_t w256 = (t256 + 255) / 256, w384 = (t384 + 255) / 256;
-    if (140 * w384 < 100 * w256 && gemm_big_offsets_fit(p)) return launch_gemm_big<EPI>(p, s);
+    const int64_t ratio = epi_base(EPI) == EPI_CHANNEL ? 130 : 140;
+    if (ratio * w384 < 100 * w256 && gemm_big_offsets_fit(p)) return launch_gemm_big<EPI>(p, s);
     return launch_gemm_i8<256, 256, 2, 4, EPI, 8>(p, s);
 }
 
