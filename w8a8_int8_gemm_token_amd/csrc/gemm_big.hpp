@@ -306,6 +306,19 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs p) {
 // products pair equal k.  The six channel fragments stay for a whole
 // sub-step; the token fragments are read one block ahead into two register
 // slots.  Integer sums are order-free: bit-identical to gemm_big_kernel.
+//
+// Persistent: one workgroup per CU (each holds the CU's whole LDS) takes
+// tiles b, b + grid, ... in turn.  Launched one tile per workgroup, a CU's
+// matrix cores idle while its tile's 196 KB of output leave and until the
+// next tile's first stage lands; here the next tile's stage 0 is issued into
+// lx0 / lw0 right after the last stage, the epilogue stages through lw1 alone
+// (four 64-row passes) with the scales in lx1, and the next tile starts as
+// soon as its own loads landed: vmcnt retires in issue order, and every wave
+// issues the same 24 output stores after them (a store outside C gets an
+// offset past its buffer resource and is dropped), so a wait for all but 24
+// operations is a wait for exactly the stage-0 loads.  The stores drain
+// behind the next tile's first stage.  Same board, bit-identical: 456 against
+// 481 us (random codes), 353 against 373 us (zero codes) at 8192 x 15360 x 5120.
 template <int EPI_>
 __global__ __launch_bounds__(512) void gemm_big16_kernel(GemmArgs p) {
     constexpr int EPI = epi_base(EPI_);
@@ -323,13 +336,18 @@ __global__ __launch_bounds__(512) void gemm_big16_kernel(GemmArgs p) {
 
     const int M = p.M, N = p.N, K = p.K;
     const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
-    const int id = xcd_remap(blockIdx.x, nbm * nbn);
+    const int ntiles = nbm * nbn;
     const int per_group = GM * nbn;
-    const int first_m = (id / per_group) * GM;
-    const int gsz = min(nbm - first_m, GM);
-    const int tile_m = first_m + (id % per_group) % gsz;
-    const int tile_n = (id % per_group) / gsz;
-    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    // tile L of the launch order (workgroup b takes b, b + grid, ...; with a
+    // grid that is a multiple of 8, tile L runs on the XCD that dispatch id
+    // L would, so xcd_remap keeps each XCD's tiles together)
+    auto tile_of = [&](int L, int& tm0, int& tn0) __attribute__((always_inline)) {
+        const int id = xcd_remap(L, ntiles);
+        const int first_m = (id / per_group) * GM;
+        const int gsz = min(nbm - first_m, GM);
+        tm0 = (first_m + (id % per_group) % gsz) * BM;
+        tn0 = ((id % per_group) / gsz) * BN;
+    };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -341,11 +359,11 @@ __global__ __launch_bounds__(512) void gemm_big16_kernel(GemmArgs p) {
     const int lrow = lane >> 3, lslot = lane & 7;
     const int xv[2] = {lrow * (int)p.ldx + ((lslot ^ lrow) << 4), lrow * (int)p.ldx + ((lslot ^ lrow ^ 1) << 4)};
     const int wv[2] = {lrow * (int)p.ldw + ((lslot ^ lrow) << 4), lrow * (int)p.ldw + ((lslot ^ lrow ^ 1) << 4)};
-    const int xs0 = (m0 + wid * XIW * 8) * (int)p.ldx;
-    const int ws0 = (n0 + wid * WIW * 8) * (int)p.ldw;
 
-    // direct loads of stage kt, instructions [i0, i1) of the wave's 10
-    auto issue = [&](int kt, int8_t* bx, int8_t* bw, int i0, int i1) __attribute__((always_inline)) {
+    // direct loads of stage kt of the tile at (xs0, ws0), instructions
+    // [i0, i1) of the wave's 10
+    auto issue = [&](int kt, int8_t* bx, int8_t* bw, int i0, int i1, int xs0, int ws0)
+        __attribute__((always_inline)) {
         const int koff = kt * BK;
 #pragma unroll
         for (int i = 0; i < XIW + WIW; ++i) {
@@ -360,6 +378,8 @@ __global__ __launch_bounds__(512) void gemm_big16_kernel(GemmArgs p) {
                     lane_offset(wv[(wid * WIW + i - XIW) & 1], ws0 + (i - XIW) * 8 * (int)p.ldw + koff), 0, 0, 0);
         }
     };
+    auto xs_of = [&](int tm0) __attribute__((always_inline)) { return (tm0 + wid * XIW * 8) * (int)p.ldx; };
+    auto ws_of = [&](int tn0) __attribute__((always_inline)) { return (tn0 + wid * WIW * 8) * (int)p.ldw; };
 
     // fragment offsets: sub-step kk reads chunk 4 kk + lane / 16 of the
     // lane's row (lane % 16 of a 16-row block; 16 rows further per block,
@@ -376,10 +396,6 @@ __global__ __launch_bounds__(512) void gemm_big16_kernel(GemmArgs p) {
     }
 
     v4i acc[TT][TC];
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-#pragma unroll
-        for (int c = 0; c < TC; ++c) acc[t][c] = v4i{};
     v4i fw[TC], fx[2];
 
     auto rdx = [&](int kk, const int8_t* bx, int t) __attribute__((always_inline)) {
@@ -394,16 +410,22 @@ __global__ __launch_bounds__(512) void gemm_big16_kernel(GemmArgs p) {
             acc[t][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fw[c], fx[t & 1], acc[t][c], 0, 0, 0);
     };
 
+    const int KT = K / BK;
+    int m0, n0;
+    tile_of(blockIdx.x, m0, n0);
+    int xs0 = xs_of(m0), ws0 = ws_of(n0);
+
     // one 64-deep sub-step on fw / fx[0] (already read); the next sub-step's
     // fragments come from (nkk, nbx, nbw); LAST: they belong to the next
     // stage, so the hand-over (loads landed, one barrier) comes first.
     // FIRST: this stage's sub-step 0, which also issues the next stage's
-    // loads, two per token block.
+    // loads (if any), two per token block.
     auto substep = [&](int kk, const int8_t* bx, int nkk, const int8_t* nbx, const int8_t* nbw, bool first,
                        bool last, int kt, int8_t* lx_n, int8_t* lw_n) __attribute__((always_inline)) {
+
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-            if (first && t < 5) issue(kt + 1, lx_n, lw_n, 2 * t, 2 * t + 2);
+            if (first && t < 5) issue(kt + 1, lx_n, lw_n, 2 * t, 2 * t + 2, xs0, ws0);
             if (t + 1 < TT) fx[(t + 1) & 1] = rdx(kk, bx, t + 1);
             if (t < TT - 1) {
                 block(t);
@@ -426,81 +448,125 @@ __global__ __launch_bounds__(512) void gemm_big16_kernel(GemmArgs p) {
         }
     };
 
-    const int KT = K / BK;
-    issue(0, lx0, lw0, 0, XIW + WIW);
-    wait_vm_lgkm0<0>();
-    block_barrier();
-#pragma unroll
-    for (int c = 0; c < TC; ++c) fw[c] = rdw(0, lw0, c);
-    fx[0] = rdx(0, lx0, 0);
-    int kt = 0;
-    for (; kt + 2 <= KT; kt += 2) {
-        substep(0, lx0, 1, lx0, lw0, true, false, kt, lx1, lw1);
-        substep(1, lx0, 0, lx1, lw1, false, true, kt, lx1, lw1);
-        substep(0, lx1, 1, lx1, lw1, true, false, kt + 1, lx0, lw0);
-        substep(1, lx1, 0, lx0, lw0, false, true, kt + 1, lx0, lw0);
-    }
-    if (kt < KT) {
-        substep(0, lx0, 1, lx0, lw0, true, false, kt, lx1, lw1);
-        substep(1, lx0, 0, lx1, lw1, false, true, kt, lx1, lw1);
-    }
-
-    // ---------------------------------------------------------- epilogue --
-    // as gemm_big_kernel's: two passes of two 32-token groups of both wave
-    // rows (64 rows x 384 channels in a weight stage buffer), whole lines
-    // out.  8-byte unit u of row r at u ^ ((r & 15) << 1): a write
-    // instruction's 16 rows x 2 adjacent units, and a read's 16 chunks of
-    // one row, fall in distinct banks, and a 16-byte chunk stays in order.
-    wait_vm_lgkm0<0>();
-    block_barrier();
+    // Tiles in turn.  Each tile's stage 0 is issued into lx0 / lw0 before
+    // the previous tile's epilogue (which stages through lw1 only), so its
+    // loads land and its first MFMAs run while that epilogue's stores drain:
+    // vmcnt counts loads and stores in issue order, so waiting for all but
+    // the EPI_STORES stores of a whole tile waits for exactly those loads.
     constexpr int RB = BN * 2, CPR = RB / 16;
+    constexpr int EPI_STORES = 4 * (64 * CPR / (NW * 64));  // per wave, whole tile
+    static_assert(EPI_STORES < 64, "vmcnt range");
+    issue(0, lx0, lw0, 0, XIW + WIW, xs0, ws0);
+    wait_vm_lgkm0<0>();
+    for (int L = blockIdx.x;;) {
+        block_barrier();
+        // the epilogue's scales, fp32 in lx1 there: thread tid holds token
+        // scale tid (tid < 256) or channel scale tid - 256, then channel
+        // scale 256 + tid (tid < 128)
+        constexpr int CH0 = NW * 64 - BM, CH1 = BN - CH0;
+        const float sv0 = tid < BM ? p.s_tok[min(m0 + tid, M - 1)] : p.s_w[min(n0 + tid - BM, N - 1)];
+        const float sv1 = p.s_w[min(n0 + CH0 + tid % CH1, N - 1)];  // used below tid = 128
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+        for (int t = 0; t < TT; ++t)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int a32 = 2 * pass + h;
-            int8_t* buf = h ? lw1 : lw0;
+            for (int c = 0; c < TC; ++c) acc[t][c] = v4i{};
+#pragma unroll
+        for (int c = 0; c < TC; ++c) fw[c] = rdw(0, lw0, c);
+        fx[0] = rdx(0, lx0, 0);
+        int kt = 0;
+        for (; kt + 2 <= KT; kt += 2) {
+            substep(0, lx0, 1, lx0, lw0, true, false, kt, lx1, lw1);
+            substep(1, lx0, 0, lx1, lw1, false, true, kt, lx1, lw1);
+            substep(0, lx1, 1, lx1, lw1, true, false, kt + 1, lx0, lw0);
+            substep(1, lx1, 0, lx0, lw0, false, true, kt + 1, lx0, lw0);
+        }
+        if (kt < KT) {
+            substep(0, lx0, 1, lx0, lw0, true, false, kt, lx1, lw1);
+            substep(1, lx0, 0, lx1, lw1, false, true, kt, lx1, lw1);
+        }
+
+        // -------------------------------------------------------- epilogue --
+        // four passes of one 32-token group of both wave rows (64 rows x 384
+        // channels in lw1), whole lines out.  8-byte unit u of row r at
+        // u ^ ((r & 15) << 1): a write instruction's 16 rows x 2 adjacent
+        // units, and a read's 16 chunks of one row, fall in distinct banks,
+        // and a 16-byte chunk stays in order.
+        wait_vm_lgkm0<0>();
+        block_barrier();  // both stage buffers are free
+        // per-lane values from here on are made inside the tile loop (an
+        // empty asm hides their loop invariance), so that none of them stays
+        // live across the main loop
+        int le = lane, te = tid;
+        asm volatile("" : "+v"(le), "+v"(te));
+        // the tile's scales (loaded at its start) go to lx1: the passes read
+        // them from LDS, and no global load of the epilogue waits behind the
+        // next tile's loads or this tile's stores
+        float* sc_s = reinterpret_cast<float*>(lx1);
+        const int Ln = L + (int)gridDim.x;
+        const bool next = Ln < ntiles;
+        int m0n = 0, n0n = 0;
+        if (next) {
+            tile_of(Ln, m0n, n0n);
+            issue(0, lx0, lw0, 0, XIW + WIW, xs_of(m0n), ws_of(n0n));
+        }
+        sc_s[te] = sv0;
+        if (te < CH1) sc_s[BM + CH0 + te] = sv1;
+        wait_vm_lgkm0<63>();
+        block_barrier();
+        // C through a buffer resource from the tile's first row: every
+        // lane issues its store (one past the resource, offset 2^31, for an
+        // element outside C, which the hardware drops), so that each wave
+        // issues exactly EPI_STORES of them
+        const __amdgpu_buffer_rsrc_t cr =
+            make_rsrc(static_cast<uint16_t*>(p.c) + (int64_t)m0 * p.ldc,
+                      (uint32_t)(((int64_t)(min(BM, M - m0) - 1) * p.ldc + N) * 2));
+#pragma unroll
+        for (int a32 = 0; a32 < 4; ++a32) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const int t = 2 * a32 + tt;
-                const int r = wm * 32 + tt * 16 + (lane & 15);
-                const int j = min(m0 + wm * WTM + t * 16 + (lane & 15), M - 1);
-                const float st = p.s_tok[j];
+                const int r = wm * 32 + tt * 16 + (le & 15);
+                const float st = sc_s[wm * WTM + t * 16 + (le & 15)];
 #pragma unroll
                 for (int c = 0; c < TC; ++c) {
-                    const int c8 = wn * (WTN / 4) + c * 4 + q4;
-                    const int ch = min(n0 + 4 * c8, N - 4);
+                    const int c8 = wn * (WTN / 4) + c * 4 + (le >> 4);
+                    const v4f sw = *reinterpret_cast<const v4f*>(sc_s + BM + 4 * c8);
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float tv = (float)acc[t][c][e] * st;
-                        v[e] = tv * p.s_w[ch + e];
+                        v[e] = tv * sw[e];
                     }
                     v2u o;
                     o[0] = pack16x2<OUT_F16>(v[0], v[1]);
                     o[1] = pack16x2<OUT_F16>(v[2], v[3]);
-                    *reinterpret_cast<v2u*>(buf + r * RB + ((c8 ^ ((r & 15) << 1)) << 3)) = o;
+                    *reinterpret_cast<v2u*>(lw1 + r * RB + ((c8 ^ ((r & 15) << 1)) << 3)) = o;
                 }
             }
-        }
-        wait_vm_lgkm0<63>();
-        block_barrier();
-#pragma unroll
-        for (int i = 0; i < 2 * 64 * CPR / (NW * 64); ++i) {
-            const int idx = i * NW * 64 + tid;
-            const int h = idx / (64 * CPR);
-            const int rr = (idx / CPR) % 64, q = idx % CPR;
-            const v4u d = *reinterpret_cast<const v4u*>((h ? lw1 : lw0) + rr * RB + ((q ^ (rr & 15)) << 4));
-            const int j = m0 + (rr >> 5) * WTM + (2 * pass + h) * 32 + (rr & 31);
-            const int ch = n0 + q * 8;
-            if (j < M && ch < N)
-                __builtin_nontemporal_store(d, reinterpret_cast<v4u*>(static_cast<uint16_t*>(p.c) +
-                                                                       (int64_t)j * p.ldc + ch));
-        }
-        if (pass == 0) {
             wait_vm_lgkm0<63>();
             block_barrier();
+#pragma unroll
+            for (int i = 0; i < 64 * CPR / (NW * 64); ++i) {
+                const int idx = i * NW * 64 + te;
+                const int rr = idx / CPR, q = idx % CPR;
+                const v4u d = *reinterpret_cast<const v4u*>(lw1 + rr * RB + ((q ^ (rr & 15)) << 4));
+                const int jr = (rr >> 5) * WTM + a32 * 32 + (rr & 31);  // row in the tile
+                const int ch = n0 + q * 8;
+                const int off = m0 + jr < M && ch < N ? (jr * (int)p.ldc + ch) * 2 : INT32_MIN;
+                __builtin_amdgcn_raw_buffer_store_b128(d, cr, off, 0, 2);  // 2: non-temporal
+            }
+            if (a32 < 3) {
+                wait_vm_lgkm0<63>();
+                block_barrier();
+            }
         }
+        if (!next) break;
+        L = Ln;
+        m0 = m0n;
+        n0 = n0n;
+        xs0 = xs_of(m0);
+        ws0 = ws_of(n0);
+        wait_vm_lgkm0<EPI_STORES>();  // the next tile's stage 0 landed
     }
 }
 
@@ -508,14 +574,29 @@ __global__ __launch_bounds__(512) void gemm_big16_kernel(GemmArgs p) {
 // m0 + 255, and the loads run one stage past K.
 inline bool gemm_big_offsets_fit(const GemmArgs& p) {
     const int64_t lim = (int64_t)1 << 31;
-    return ((int64_t)p.M + 256) * p.ldx + 256 < lim && ((int64_t)p.N + 384) * p.ldw + 256 < lim;
+    return ((int64_t)p.M + 256) * p.ldx + 256 < lim && ((int64_t)p.N + 384) * p.ldw + 256 < lim &&
+           (int64_t)257 * p.ldc * 4 < lim;  // C offsets within a tile (gemm_big16_kernel's stores)
+}
+
+// Workgroups of the 16 x 16 x 64 launch: one per CU of the current device
+// (each holds a CU's whole LDS), which then take the tiles in turn.
+inline int big16_grid() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
 }
 
 template <int EPI>
 inline hipError_t launch_gemm_big(const GemmArgs& p, hipStream_t stream) {
     const int nbm = (p.M + BIG_BM - 1) / BIG_BM, nbn = (p.N + BIG_BN - 1) / BIG_BN;
     if constexpr (epi_base(EPI) == EPI_CHANNEL)  // 16-bit outputs: the 16 x 16 x 64 form
-        hipLaunchKernelGGL((gemm_big16_kernel<EPI>), dim3(nbm * nbn), dim3(512), 0, stream, p);
+        hipLaunchKernelGGL((gemm_big16_kernel<EPI>), dim3(nbm * nbn < big16_grid() ? nbm * nbn : big16_grid()), dim3(512), 0, stream, p);
     else
         hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(nbm * nbn), dim3(512), 0, stream, p);
     return hipGetLastError();
