@@ -333,6 +333,32 @@ def test_big_tiles_scaled_mm_sampled_rows(M, N, K):
     assert_ulp1(got_h, ref_h, f"big tiles scaled_mm_f16 {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("f16", [False, True])
+def test_big_tiles_persistent_ragged_strided_output(f16):
+    """The per-channel 256 x 384 kernel runs one workgroup per CU taking the
+    tiles in turn (here 33 x 41 = 1,353 tiles, ragged in both directions):
+    every row on each side of a tile boundary and in the partial last row of
+    tiles matches the oracle, and the stores of the ragged tiles, issued by
+    every lane and dropped past C's buffer resource, leave the padding
+    columns of a strided output and the rows below it untouched."""
+    M, N, K, pad = 8200, 15376, 256, 24
+    say("big tiles persistent ragged", M, N, K, pad, f16)
+    a = synth.int8_uniform((M, K), seed=41, lo=-127)
+    b = synth.int8_uniform((N, K), seed=43, lo=-127)
+    st = synth.uniform_f32((M,), seed=47, lo=1e-4, hi=2e-2)
+    sc = synth.uniform_f32((N,), seed=53, lo=1e-4, hi=2e-2)
+    dt = torch.float16 if f16 else torch.bfloat16
+    buf = torch.full((M + 2, N + pad), -1, dtype=torch.int16, device=DEV).view(dt)
+    fn = q8.q8_scaled_mm_f16 if f16 else q8.q8_scaled_mm
+    fn(dev(a), dev(b), dev(st), dev(sc), out=buf[:M, :N])
+    rows = np.array([0, 1, 255, 256, 4095, 4096, 8191, 8192, 8198, 8199])
+    got = host(buf).contiguous().view(torch.int16).numpy().view(np.uint16)
+    ref = (oracle.scaled_mm_f16 if f16 else oracle.scaled_mm)(np.ascontiguousarray(a[rows]), b, st[rows], sc)
+    assert_ulp1(got[rows, :N], ref, f"persistent big tiles f16={f16}")
+    assert (got[:M, N:] == 0xFFFF).all(), "wrote into the padding columns"
+    assert (got[M:] == 0xFFFF).all(), "wrote below the output"
+
+
 # ------------------------------------------------------------ W8A8 layer -
 
 def _layer_inputs(name, seed, M=None):
